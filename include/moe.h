@@ -1,0 +1,221 @@
+/*
+ * moe.h: C ABI of the routed-expert FFN (qwen3_5-MoE shaped) with low-bit
+ * affine expert weights, for one AMD MI355X (gfx950).
+ *
+ * The layer computed (sources named per entry point below):
+ *   logits l[r,e] = W_router[e,:] . x[r,:]  (+ bias[e]),   fp32
+ *   gate logit c[r] = w_gate[:] . x[r,:],                    fp32
+ *   ids[r,0..k)  = top-k of l[r,:], NaN > +inf > finite, ties to the lower id
+ *   p[r,j]       = exp(l[r,ids_j] - l[r,ids_0]) / sum_j' exp(l[r,ids_j'] - l[r,ids_0])
+ *   sigma[r]     = 1 / (1 + exp(-c[r]))
+ *   per slot j (k routed experts, then the shared expert):
+ *     g = Wg x, u = Wu x, h = silu(g) * u, e_j = Wd h
+ *   y[r,:]       = sum_j p[r,j] e_j + sigma[r] e_shared      (fp32, slots in pick order)
+ * with every weight matrix stored quantised: affine w = s*q + b per group of
+ * 64 (MLX-style, 3/4/8-bit), or symmetric w = s*(u-8) per group of 128 (W4A16).
+ *
+ * Conventions for every call:
+ *   - Pointers named dev_* or documented as device memory must point to
+ *     device memory of the current HIP device; host_* pointers to host memory.
+ *   - All device memory is owned by the caller. The library allocates no
+ *     device memory and keeps no global state; calls are reentrant.
+ *   - Arguments are validated before anything is enqueued; on an error code
+ *     nothing has been enqueued. moe_last_error() (thread-local) then names
+ *     the argument, tensor class or format that was refused.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     legacy default stream). Faults inside kernels surface at the caller's
+ *     next synchronisation.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* null pointer, bad count */
+  MOE_EUNSUPPORTED = -2,  /* a format / shape the kernels do not read (refused by name) */
+  MOE_ESHAPE = -3,        /* inconsistent shapes */
+  MOE_ENOSPACE = -4,      /* destination or workspace too small */
+  MOE_EHIP = -5           /* a HIP runtime call failed; moe_last_error() has the hipError_t */
+};
+
+/* ----------------------------------------------------------------- formats */
+enum moe_mode { MOE_AFFINE = 0, MOE_SYMMETRIC = 1, MOE_DENSE = 2 };
+enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1 };
+
+/* Quantised format of one tensor class.
+ * Accepted combinations (anything else is MOE_EUNSUPPORTED):
+ *   {4, 64, MOE_AFFINE, MOE_BF16}     MLX affine 4-bit, group 64
+ *       ("Sage-A1.5 ... on the XPU backend #1329", Proposal: affine 4/64 export)
+ *   {3, 64, MOE_AFFINE, MOE_BF16}     MLX affine 3-bit, group 64 (routed/shared only)
+ *       ("qwen3_5_moe on native CUDA with 3-bit routed experts #803", What I want to run)
+ *   {8, 64, MOE_AFFINE, MOE_BF16}     MLX affine 8-bit, group 64 (router/gate row only)
+ *       (same page and section: routers and the shared-expert gate at 8 bits)
+ *   {4, 128, MOE_SYMMETRIC, MOE_FP16} int4 symmetric, group 128, fp16 scales (W4A16)
+ *       ("Sage-1.5-W4A16" model card, Model details)
+ *   {16, 0, MOE_DENSE, MOE_BF16}      bf16 values (gate row only; the W4A16 export
+ *       keeps the shared-expert gate in BF16: same card, Recipe) */
+typedef struct moe_qformat {
+  int32_t bits;
+  int32_t group;
+  int32_t mode;         /* enum moe_mode */
+  int32_t scale_dtype;  /* enum moe_dtype: dtype of scales and biases (of values for DENSE) */
+} moe_qformat;
+
+/* Shapes and formats of one MoE layer.
+ * Supported: hidden % 256 == 0 (<= 4096), n_experts % 64 == 0 (<= 256),
+ * 1 <= top_k <= 8, inter and shared_inter % 256 == 0 (<= 2048);
+ * act_dtype BF16 or FP16 (the activations x). */
+typedef struct moe_layer_desc {
+  int32_t hidden, n_experts, top_k, inter, shared_inter, act_dtype;
+  moe_qformat router, gate_row, routed, shared;
+} moe_layer_desc;
+
+/* One quantised tensor in the canonical (MLX-style) host layout:
+ *   codes : uint32 [rows, cols*bits/32]: each row an LSB-first bitstream
+ *           (element i in stream bits [bits*i, bits*i+bits), stream bit t is
+ *           bit t%32 of word t/32). SYMMETRIC stores the nibble u = q + 8.
+ *           DENSE: uint16 bf16 values [rows, cols].
+ *   scales: uint16 bit patterns [rows, cols/group] (bf16 or fp16)
+ *   biases: uint16 bit patterns [rows, cols/group] (AFFINE only, else NULL)
+ * Stacked routed experts carry a leading [n_experts] axis, experts contiguous. */
+typedef struct moe_qtensor {
+  const void* codes;
+  const uint16_t* scales;
+  const uint16_t* biases;
+} moe_qtensor;
+
+/* Host sources of one layer (canonical layout, all host memory).
+ *   router  [E, H]     gate_row [1, H]
+ *   gate, up [E, I, H] down [E, H, I]
+ *   sh_gate, sh_up [Is, H]  sh_down [H, Is] */
+typedef struct moe_layer_src {
+  moe_qtensor router, gate_row, gate, up, down, sh_gate, sh_up, sh_down;
+} moe_layer_src;
+
+/* Byte offsets of one packed matrix class inside a packed expert block. */
+typedef struct moe_mat_off {
+  uint64_t codes, scales;
+} moe_mat_off;
+
+/* A packed layer: plain data, owns nothing; valid while `dev` lives.
+ * Filled by moe_pack_layer / moe_pack_layer_host; treat as opaque. */
+typedef struct moe_layer {
+  moe_layer_desc d;
+  const void* dev;            /* device base of the packed bytes (NULL until bound) */
+  uint64_t bytes;             /* packed size */
+  uint64_t router_off, router_scale_off, gate_row_off, gate_row_scale_off;
+  uint64_t experts_off, expert_stride;     /* routed expert e at experts_off + e*stride */
+  moe_mat_off gu, dn;                      /* inside a routed expert block */
+  uint64_t shared_off;
+  moe_mat_off sh_gu, sh_dn;                /* inside the shared expert block */
+} moe_layer;
+
+/* Optional per-projection dumps (device memory, fp32), for tests and
+ * accuracy reports; any member may be NULL. Layouts use slot index
+ * j in [0, k] where j == k is the shared expert:
+ *   logits [rows, E+1]   (column E holds the shared-gate logit c)
+ *   gu     [rows, k+1, 2, Imax]  (g then u; Imax = max(inter, shared_inter))
+ *   h      [rows, k+1, Imax]
+ *   e      [rows, k+1, H]        (unweighted slot outputs) */
+typedef struct moe_taps {
+  float* logits;
+  float* gu;
+  float* h;
+  float* e;
+} moe_taps;
+
+/* ------------------------------------------------------------ pack loader */
+
+/* Packed size in bytes of a layer with descriptor *d.
+ * Errors: MOE_EINVAL (null), MOE_EUNSUPPORTED (format/shape refused by name). */
+int moe_pack_size(const moe_layer_desc* d, uint64_t* bytes);
+
+/* Repack a layer from the canonical host layout into the kernel layout, into
+ * host memory host_dst[0, dst_bytes), and fill *out (out->dev = NULL).
+ * Pure host work (no HIP call). The kernel layout: each matrix is cut into
+ * tiles of 64 output rows (gate/up tiles hold 32 gate rows then the 32 up
+ * rows of the same intermediate indices: gate and up interleaved per tile);
+ * codes of a tile are stored chunk-major (32 codes per row per chunk, rows
+ * contiguous within a chunk) with each chunk's bits rearranged into 16-bit
+ * pairs of consecutive codes; per-group scale/bias words follow per tile.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPACE (dst_bytes too small). */
+int moe_pack_layer_host(const moe_layer_desc* d, const moe_layer_src* src,
+                        void* host_dst, uint64_t dst_bytes, moe_layer* out);
+
+/* Set the device base of a layer whose packed bytes the caller has copied
+ * to device memory dev_ptr (moe_pack_size bytes, 256-byte aligned). */
+int moe_layer_bind(moe_layer* layer, const void* dev_ptr);
+
+/* moe_pack_layer_host into a temporary host buffer, then a synchronous copy
+ * to device memory dev_dst (caller-owned, >= moe_pack_size bytes, 256-byte
+ * aligned) on `stream`, then moe_layer_bind. Returns when the copy is done.
+ * Errors: as moe_pack_layer_host, plus MOE_EHIP. */
+int moe_pack_layer(const moe_layer_desc* d, const moe_layer_src* src,
+                   void* dev_dst, uint64_t dst_bytes, void* stream, moe_layer* out);
+
+/* Workspace bytes for moe_experts_decode (grouped = 0) or
+ * moe_experts_grouped (grouped = 1) at `rows` rows. */
+int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t* bytes);
+
+/* ------------------------------------------------------------- hot path */
+
+/* Router of the layer ("qwen3_5_moe on native CUDA with 3-bit routed experts
+ * #803", Activity, comment "Progress on the 4-bit gate": fp32 logits over the
+ * experts and the shared expert's gate row; top-k by logit with ties to the
+ * lower id; weights exp(l - l_top) over the k; the shared expert as a slot
+ * weighted by sigmoid of its gate). Weights are renormalised over the k picks.
+ *   x          device, [rows, H] activations (act_dtype), row-major
+ *   rows       >= 1
+ *   logit_bias device, [E] fp32 added to the logits before the pick, or NULL
+ *   ids        device, [rows, k] int32, in pick order (logit desc, id asc)
+ *   p          device, [rows, k] fp32
+ *   shared_gate device, [rows] fp32 sigma(c)
+ *   taps       NULL, or taps->logits (others ignored)
+ * A row holding NaN gets the NaN-ordered picks 0..k-1 and NaN weights. */
+int moe_route(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+              int32_t* ids, float* p, float* shared_gate, const moe_taps* taps,
+              void* stream);
+
+/* Routed + shared experts and the combine for decode rows (one row per
+ * stream; the per-row form with fp32 sums of the same comment). Expert-centric:
+ * rows that picked the same expert share its weight reads, and each row's
+ * arithmetic is fixed, so a row's y is bit-identical alone or in a batch.
+ *   x       device [rows, H]; rows in 1..16
+ *   ids, p, shared_gate  from moe_route on the same layer and x
+ *   y       device [rows, H] fp32
+ *   ws      device workspace of moe_workspace_size(grouped=0) bytes
+ * Preconditions: |x| < 65504 (activations are used as fp16; bf16 values of
+ * magnitude below 2^-17 lose bits); ids valid for the layer. */
+int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const int32_t* ids,
+                       const float* p, const float* shared_gate, float* y, void* ws,
+                       uint64_t ws_bytes, const moe_taps* taps, void* stream);
+
+/* The same layer for prompt chunks (the prefill form): rows are sorted by
+ * expert (histogram, prefix scan, stable scatter), then grouped GEMMs on
+ * 16-bit MFMA compute gate/up + SwiGLU and down, then a fixed-order combine.
+ * Equal to the decode form within rounding, not bit for bit ("Sage-A1.5 ...
+ * #1329", Limits to agree on: the grouped MoE has a different sum order).
+ *   rows >= 1 (<= 65536); other arguments as moe_experts_decode, with the
+ *   workspace from moe_workspace_size(grouped=1).
+ * Preconditions: |x| < 65504 and |h| < 65504 (fp16 MFMA operands). */
+int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const int32_t* ids,
+                        const float* p, const float* shared_gate, float* y, void* ws,
+                        uint64_t ws_bytes, const moe_taps* taps, void* stream);
+
+/* ----------------------------------------------------------- diagnostics */
+const char* moe_status_string(int status);
+const char* moe_last_error(void);   /* thread-local detail of the last failed call */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,275 @@
+// C entry points: argument validation, then the kernel launches.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "moe_host.h"
+#include "moe_launch.h"
+
+namespace moe {
+const char* last_error_cstr();
+int pack_layer_host(const moe_layer_desc* d, const moe_layer_src* src, void* host_dst,
+                    uint64_t dst_bytes, moe_layer* out);
+}  // namespace moe
+
+using namespace moe;
+
+static int hip_fail(const char* what, hipError_t e) {
+  set_error(std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")");
+  return MOE_EHIP;
+}
+
+static int check_layer(const moe_layer* L) {
+  if (!L) { set_error("layer is NULL"); return MOE_EINVAL; }
+  if (!L->dev) { set_error("layer has no device buffer (moe_layer_bind was not called)"); return MOE_EINVAL; }
+  int st = validate_desc(&L->d);
+  if (st) return st;
+  moe_layer ref;
+  compute_layout(&L->d, &ref);
+  if (ref.bytes != L->bytes || ref.experts_off != L->experts_off || ref.shared_off != L->shared_off) {
+    set_error("layer offsets do not match its descriptor (not produced by this library version)");
+    return MOE_ESHAPE;
+  }
+  return MOE_OK;
+}
+
+static ExpertClass expert_class(const moe_layer* L, bool shared) {
+  ExpertClass c;
+  if (shared) {
+    c.base_off = L->shared_off;
+    c.stride = 0;
+    c.gu_codes = L->sh_gu.codes;
+    c.gu_scales = L->sh_gu.scales;
+    c.dn_codes = L->sh_dn.codes;
+    c.dn_scales = L->sh_dn.scales;
+    c.inter = L->d.shared_inter;
+  } else {
+    c.base_off = L->experts_off;
+    c.stride = L->expert_stride;
+    c.gu_codes = L->gu.codes;
+    c.gu_scales = L->gu.scales;
+    c.dn_codes = L->dn.codes;
+    c.dn_scales = L->dn.scales;
+    c.inter = L->d.inter;
+  }
+  return c;
+}
+
+extern "C" {
+
+int moe_pack_size(const moe_layer_desc* d, uint64_t* bytes) {
+  if (!d || !bytes) { set_error("moe_pack_size: NULL argument"); return MOE_EINVAL; }
+  moe_layer L;
+  int st = compute_layout(d, &L);
+  if (st) return st;
+  *bytes = L.bytes;
+  return MOE_OK;
+}
+
+int moe_pack_layer_host(const moe_layer_desc* d, const moe_layer_src* src, void* host_dst,
+                        uint64_t dst_bytes, moe_layer* out) {
+  return pack_layer_host(d, src, host_dst, dst_bytes, out);
+}
+
+int moe_layer_bind(moe_layer* layer, const void* dev_ptr) {
+  if (!layer || !dev_ptr) { set_error("moe_layer_bind: NULL argument"); return MOE_EINVAL; }
+  if (reinterpret_cast<uintptr_t>(dev_ptr) & 255u) {
+    set_error("moe_layer_bind: device pointer is not 256-byte aligned");
+    return MOE_EINVAL;
+  }
+  layer->dev = dev_ptr;
+  return MOE_OK;
+}
+
+int moe_pack_layer(const moe_layer_desc* d, const moe_layer_src* src, void* dev_dst,
+                   uint64_t dst_bytes, void* stream, moe_layer* out) {
+  if (!dev_dst || !out) { set_error("moe_pack_layer: NULL argument"); return MOE_EINVAL; }
+  uint64_t bytes = 0;
+  int st = moe_pack_size(d, &bytes);
+  if (st) return st;
+  if (dst_bytes < bytes) {
+    set_error("moe_pack_layer: device destination smaller than moe_pack_size");
+    return MOE_ENOSPACE;
+  }
+  std::vector<uint8_t> host(bytes);
+  moe_layer L;
+  st = pack_layer_host(d, src, host.data(), bytes, &L);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dev_dst, host.data(), bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail("moe_pack_layer: hipMemcpyAsync", e);
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail("moe_pack_layer: hipStreamSynchronize", e);
+  st = moe_layer_bind(&L, dev_dst);
+  if (st) return st;
+  *out = L;
+  return MOE_OK;
+}
+
+int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t* bytes) {
+  if (!d || !bytes) { set_error("moe_workspace_size: NULL argument"); return MOE_EINVAL; }
+  int st = validate_desc(d);
+  if (st) return st;
+  if (rows < 1 || (!grouped && rows > 16) || rows > 65536) {
+    set_error(std::string("moe_workspace_size: rows=") + std::to_string(rows) +
+              (grouped ? " outside 1..65536" : " outside 1..16 (decode)"));
+    return MOE_EINVAL;
+  }
+  *bytes = grouped ? grouped_ws_layout(d, rows).total : decode_ws_layout(d, rows).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+              int32_t* ids, float* p, float* shared_gate, const moe_taps* taps, void* stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if (!x || !ids || !p || !shared_gate) { set_error("moe_route: NULL x/ids/p/shared_gate"); return MOE_EINVAL; }
+  if (rows < 1 || rows > 65536) { set_error("moe_route: rows outside 1..65536"); return MOE_EINVAL; }
+  FmtInfo fr, fg;
+  format_info(layer->d.router, TC_ROUTER, &fr);
+  format_info(layer->d.gate_row, TC_GATE_ROW, &fg);
+  RouteArgs a;
+  a.base = static_cast<const uint8_t*>(layer->dev);
+  a.r_off = layer->router_off;
+  a.r_soff = layer->router_scale_off;
+  a.g_off = layer->gate_row_off;
+  a.g_soff = layer->gate_row_scale_off;
+  a.x = static_cast<const uint16_t*>(x);
+  a.act_fp16 = layer->d.act_dtype == MOE_FP16;
+  a.H = layer->d.hidden;
+  a.E = layer->d.n_experts;
+  a.k = layer->d.top_k;
+  a.bias = logit_bias;
+  a.ids = ids;
+  a.p = p;
+  a.sg = shared_gate;
+  a.logits = taps ? taps->logits : nullptr;
+  hipError_t e = launch_route(fr.kid, fg.kid, a, rows, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("moe_route: launch", e);
+  return MOE_OK;
+}
+
+static int experts_common(const char* name, const moe_layer* layer, const void* x, int rows,
+                          const int32_t* ids, const float* p, const float* sg, float* y,
+                          void* ws, int max_rows) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if (!x || !ids || !p || !sg || !y || !ws) {
+    set_error(std::string(name) + ": NULL x/ids/p/shared_gate/y/ws");
+    return MOE_EINVAL;
+  }
+  if (rows < 1 || rows > max_rows) {
+    set_error(std::string(name) + ": rows=" + std::to_string(rows) + " outside 1.." +
+              std::to_string(max_rows));
+    return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const int32_t* ids,
+                       const float* p, const float* shared_gate, float* y, void* ws,
+                       uint64_t ws_bytes, const moe_taps* taps, void* stream) {
+  int st = experts_common("moe_experts_decode", layer, x, rows, ids, p, shared_gate, y, ws, 16);
+  if (st) return st;
+  const DecodeWs wl = decode_ws_layout(&layer->d, rows);
+  if (ws_bytes < wl.total) {
+    set_error("moe_experts_decode: workspace of " + std::to_string(ws_bytes) + " bytes, needs " +
+              std::to_string(wl.total));
+    return MOE_ENOSPACE;
+  }
+  FmtInfo fe, fs;
+  format_info(layer->d.routed, TC_ROUTED, &fe);
+  format_info(layer->d.shared, TC_SHARED, &fs);
+  DecodeArgs a;
+  a.base = static_cast<const uint8_t*>(layer->dev);
+  a.rt = expert_class(layer, false);
+  a.sh = expert_class(layer, true);
+  a.x = static_cast<const uint16_t*>(x);
+  a.act_fp16 = layer->d.act_dtype == MOE_FP16;
+  a.H = layer->d.hidden;
+  a.E = layer->d.n_experts;
+  a.k = layer->d.top_k;
+  a.R = rows;
+  a.Imax = std::max(layer->d.inter, layer->d.shared_inter);
+  a.ids = ids;
+  a.p = p;
+  a.sg = shared_gate;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  a.h_ws = reinterpret_cast<float*>(w + wl.h_off);
+  a.e_ws = reinterpret_cast<float*>(w + wl.e_off);
+  a.y = y;
+  a.tap_gu = taps ? taps->gu : nullptr;
+  a.tap_h = taps ? taps->h : nullptr;
+  a.tap_e = taps ? taps->e : nullptr;
+  hipError_t e = launch_decode(fe.kid, fs.kid, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("moe_experts_decode: launch", e);
+  return MOE_OK;
+}
+
+int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const int32_t* ids,
+                        const float* p, const float* shared_gate, float* y, void* ws,
+                        uint64_t ws_bytes, const moe_taps* taps, void* stream) {
+  int st = experts_common("moe_experts_grouped", layer, x, rows, ids, p, shared_gate, y, ws, 65536);
+  if (st) return st;
+  const GroupedWs wl = grouped_ws_layout(&layer->d, rows);
+  if (ws_bytes < wl.total) {
+    set_error("moe_experts_grouped: workspace of " + std::to_string(ws_bytes) + " bytes, needs " +
+              std::to_string(wl.total));
+    return MOE_ENOSPACE;
+  }
+  FmtInfo fe, fs;
+  format_info(layer->d.routed, TC_ROUTED, &fe);
+  format_info(layer->d.shared, TC_SHARED, &fs);
+  GroupedArgs a;
+  a.base = static_cast<const uint8_t*>(layer->dev);
+  a.rt = expert_class(layer, false);
+  a.sh = expert_class(layer, true);
+  a.x = static_cast<const uint16_t*>(x);
+  a.act_fp16 = layer->d.act_dtype == MOE_FP16;
+  a.H = layer->d.hidden;
+  a.E = layer->d.n_experts;
+  a.k = layer->d.top_k;
+  a.R = rows;
+  a.Imax = std::max(layer->d.inter, layer->d.shared_inter);
+  a.ids = ids;
+  a.p = p;
+  a.sg = shared_gate;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  a.meta = reinterpret_cast<int32_t*>(w + wl.meta_off);
+  a.perm = reinterpret_cast<int32_t*>(w + wl.perm_off);
+  a.xs = reinterpret_cast<uint16_t*>(w + wl.xs_off);
+  a.hbuf = reinterpret_cast<uint16_t*>(w + wl.h_off);
+  a.e_ws = reinterpret_cast<float*>(w + wl.e_off);
+  a.tiles = reinterpret_cast<int32_t*>(w + wl.tiles_off);
+  a.max_tiles = wl.max_tiles;
+  a.y = y;
+  a.tap_gu = taps ? taps->gu : nullptr;
+  a.tap_h = taps ? taps->h : nullptr;
+  a.tap_e = taps ? taps->e : nullptr;
+  hipError_t e = launch_grouped(fe.kid, fs.kid, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("moe_experts_grouped: launch", e);
+  return MOE_OK;
+}
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: format or shape not read by the kernels";
+    case MOE_ESHAPE: return "MOE_ESHAPE: inconsistent shapes";
+    case MOE_ENOSPACE: return "MOE_ENOSPACE: buffer too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return last_error_cstr(); }
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Host-side internals shared by the pack loader and the entry points.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// kernel-side format ids (match moe_kernels.h)
+enum { KF_Q4 = 0, KF_Q3 = 1, KF_Q8 = 2, KF_S4 = 3, KF_DENSE = 4 };
+
+struct FmtInfo {
+  int kid;      // kernel format id
+  int bits;     // code width (16 for dense)
+  int group;    // group size (0 for dense)
+  int cb;       // bytes per lane per 32-code chunk
+  int scb;      // bytes per group scale entry
+  bool affine;
+};
+
+// Tensor classes, for messages and accepted-format tables.
+enum TensorClass { TC_ROUTER = 0, TC_GATE_ROW, TC_ROUTED, TC_SHARED };
+
+// Returns false (and sets the thread-local error naming the class) when the
+// format is not read by the kernels for that tensor class.
+bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* out);
+
+// Validates a descriptor (shapes + formats). Sets the error on failure.
+int validate_desc(const moe_layer_desc* d);
+
+// Computes every offset of the packed layout into *out (out->dev untouched).
+int compute_layout(const moe_layer_desc* d, moe_layer* out);
+
+void set_error(const std::string& s);
+std::string fmt_name(const moe_qformat& f);
+
+uint64_t align256(uint64_t x);
+
+// Per-kind workspace layout of the decode path.
+struct DecodeWs {
+  uint64_t h_off, e_off, total;
+};
+DecodeWs decode_ws_layout(const moe_layer_desc* d, int rows);
+
+// Per-kind workspace layout of the grouped path.
+struct GroupedWs {
+  uint64_t meta_off;   // int32 counts[E+1], offsets[E+2], tiles...
+  uint64_t perm_off;   // int32 [R*k + R]: expert-major position -> slot index (r*(k+1)+j)
+  uint64_t xs_off;     // f16 [R, H]: x converted once
+  uint64_t h_off;      // f16 [R*(k+1), Imax] in expert-major order
+  uint64_t e_off;      // f32 [R*(k+1), H] in slot order (r*(k+1)+j)
+  uint64_t tiles_off;  // int32 tile descriptors
+  uint64_t total;
+  int max_tiles;
+};
+GroupedWs grouped_ws_layout(const moe_layer_desc* d, int rows);
+
+}  // namespace moe

@@ -1,0 +1,68 @@
+// Kernel argument blocks and launchers (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+  const uint8_t* base;
+  uint64_t r_off, r_soff, g_off, g_soff;
+  const uint16_t* x;
+  int act_fp16, H, E, k;
+  const float* bias;
+  int32_t* ids;
+  float* p;
+  float* sg;
+  float* logits;
+};
+
+// Offsets of one expert class (routed or shared) inside the packed layer.
+struct ExpertClass {
+  uint64_t base_off, stride;          // expert e at base_off + e*stride
+  uint64_t gu_codes, gu_scales, dn_codes, dn_scales;
+  int inter;
+};
+
+struct DecodeArgs {
+  const uint8_t* base;
+  ExpertClass rt, sh;
+  const uint16_t* x;
+  int act_fp16, H, E, k, R, Imax;
+  const int32_t* ids;
+  const float* p;
+  const float* sg;
+  float* h_ws;    // [R, k+1, Imax]
+  float* e_ws;    // [R, k+1, H]
+  float* y;       // [R, H]
+  float* tap_gu;  // [R, k+1, 2, Imax] or null
+  float* tap_h;   // [R, k+1, Imax] or null
+  float* tap_e;   // [R, k+1, H] or null
+};
+
+struct GroupedArgs {
+  const uint8_t* base;
+  ExpertClass rt, sh;
+  const uint16_t* x;
+  int act_fp16, H, E, k, R, Imax;
+  const int32_t* ids;
+  const float* p;
+  const float* sg;
+  int32_t* meta;     // counts/offsets/tile count
+  int32_t* perm;     // expert-major position -> slot index r*(k+1)+j
+  uint16_t* xs;      // [R, H] fp16 bits
+  uint16_t* hbuf;    // [R*(k+1), Imax] fp16 bits (expert-major order)
+  float* e_ws;       // [R*(k+1), H] slot order
+  int32_t* tiles;    // tile descriptors
+  int max_tiles;
+  float* y;
+  float* tap_gu;
+  float* tap_h;
+  float* tap_e;
+};
+
+hipError_t launch_route(int fr, int fg, const RouteArgs& a, int rows, hipStream_t s);
+hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s);
+
+}  // namespace moe
