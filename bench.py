@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert FFN (qwen3_5-MoE 35B-A3B shapes) on one MI355X.
+
+Workload (the headline): decode, 8 independent rows through 40 distinct MoE
+layer weight sets (hidden 2048, 256 experts, top-8, expert intermediate 512,
+shared expert 512), 4-bit affine g64 weights everywhere (~18 GB packed, so
+the ~4 GB of expert bytes a step touches cannot stay in cache). One step is
+one pass of the whole hot path over one batch: for each of the 40 layers,
+route (logits, top-8, weights, shared gate) then the decode experts
+(gate/up + SwiGLU, down, combine). Inputs are resident in HBM before the
+timed region; each step takes a fresh set of activations (4 sets rotate).
+
+Prints ONE JSON line. `value` is MoE-layer tokens/s: rows x layers per
+second. `roofline` is the dominant kernel (decode gate/up) timed live with
+HIP events on its stream: algorithmic bytes per launch (the packed gate/up
+bytes of the unique experts the launch reads, plus x in and h out) over its
+mean duration. `cpu_baseline` is the FP64 oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2516.6
+METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA TFLOPS as % of peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(spec, fmt, inter):
+    """Packed bytes of one expert: gate/up and down (codes + scale words)."""
+    scb = 4 if fmt.mode == 0 else 2
+    gu = 2 * inter * spec.hidden * fmt.bits // 8 + 2 * inter * (spec.hidden // fmt.group) * scb
+    dn = spec.hidden * inter * fmt.bits // 8 + spec.hidden * (inter // fmt.group) * scb
+    return gu, dn
+
+
+def router_bytes(spec):
+    f, g = spec.router, spec.gate_row
+    scb = 4 if f.mode == 0 else 2
+    r = spec.n_experts * spec.hidden * f.bits // 8 + spec.n_experts * (spec.hidden // f.group) * scb
+    if g.mode == 2:
+        gr = spec.hidden * 2
+    else:
+        gr = spec.hidden * g.bits // 8 + (spec.hidden // g.group) * (4 if g.mode == 0 else 2)
+    return r + gr
+
+
+def build_layers(spec, n_layers, B, to_abi, synth, keep_host=0):
+    desc = B.layer_desc(*to_abi.desc_args(spec))
+    layers = [None] * n_layers
+    host_keep = {}
+    t0 = time.time()
+    with ThreadPoolExecutor(max_workers=6) as ex:
+        futs = {ex.submit(synth.make_layer, spec, l): l for l in range(n_layers)}
+        done = 0
+        for fut in list(futs):
+            l = futs[fut]
+            Lh = fut.result()
+            layers[l] = B.pack_layer(desc, to_abi.tensors(Lh))
+            if l < keep_host:
+                host_keep[l] = Lh
+            del Lh
+            done += 1
+            if done % 10 == 0 or done == n_layers:
+                log(f"[bench] packed {done}/{n_layers} layers ({time.time() - t0:.1f}s)")
+    return layers, host_keep
+
+
+def cpu_baseline(spec, Lh, rows, budget_s=20.0):
+    """The FP64 oracle (as it stands) on one layer x `rows` rows, BLAS on 1 thread."""
+    import contextlib
+
+    import oracle.moe_oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        ctx = contextlib.nullcontext()
+    xb = synth.make_x(spec, 0, rows, rep=0)
+    with ctx:
+        t0 = time.perf_counter()
+        done = 0
+        dense = O.DenseExperts(Lh, cache=True)
+        for r in range(rows):
+            O.moe_forward(Lh, xb[r:r + 1], dense)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return dict(value=done / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{done} decode rows x 1 layer of the same workload (per-row fp64 form, "
+                       f"experts dequantised on first use), {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=None, help="override the 40 layers (debug)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not run "
+              "(the routed-expert FFN is benchmarked on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from synth import to_abi
+    import quantized_routed_expert_fp32_amd as qr
+    B = qr.binding
+    B.lib()
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+
+    spec = synth.CONFIGS[1]
+    L = args.layers or spec.layers
+    R, k, H = spec.rows[0], spec.top_k, spec.hidden
+    NX = 4
+    log(f"[bench] workload {spec.name}: rows={R} layers={L}")
+    layers, host = build_layers(spec, L, B, to_abi, synth, keep_host=1)
+    xs = [[torch.from_numpy(synth.make_x(spec, l, R, rep=s).view(np.int16)).to(dev)
+           for s in range(NX)] for l in range(L)]
+    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
+    p = torch.empty((R, k), dtype=torch.float32, device=dev)
+    sg = torch.empty((R,), dtype=torch.float32, device=dev)
+    y = torch.empty((R, H), dtype=torch.float32, device=dev)
+    ws = B.new_workspace(layers[0], R, False, dev)
+    stream = torch.cuda.Stream()
+
+    def step(s, events=None):
+        for l in range(L):
+            x = xs[l][s % NX]
+            rt = dict(events=events[l][:2]) if events is not None else None
+            B.route(layers[l], x, taps=rt, out=(ids, p, sg), ws=ws, stream=stream)
+            tp = dict(events=events[l][2:]) if events is not None else None
+            B.experts(layers[l], x, ids, p, sg, False, ws=ws, y=y, taps=tp, stream=stream)
+
+    # unique experts per (layer, x set): algorithmic bytes
+    uniq = np.zeros((L, NX), np.int64)
+    with torch.cuda.stream(stream):
+        for l in range(L):
+            for s in range(NX):
+                B.route(layers[l], xs[l][s], out=(ids, p, sg), ws=ws, stream=stream)
+                stream.synchronize()
+                uniq[l, s] = len(np.unique(ids.cpu().numpy()))
+    gu_b, dn_b = expert_bytes(spec, spec.routed, spec.inter)
+    sgu_b, sdn_b = expert_bytes(spec, spec.shared, spec.shared_inter)
+    x_b, y_b = R * H * 2, R * H * 4
+    h_b = R * (k + 1) * max(spec.inter, spec.shared_inter) * 4
+    gu_launch_bytes = uniq * gu_b + sgu_b + x_b + h_b            # per gate/up launch
+    step_bytes = (uniq * (gu_b + dn_b) + sgu_b + sdn_b + router_bytes(spec) + x_b + y_b).sum(0)
+
+    # ---- timed region: whole steps
+    graphs = None
+    if not args.no_graph:
+        try:
+            graphs = []
+            for s in range(NX):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(s)
+                graphs.append(g)
+        except Exception as e:  # graph capture unavailable: time eager launches
+            log(f"[bench] graph capture failed ({e}); timing eager launches")
+            graphs = None
+    run = (lambda s: graphs[s % NX].replay()) if graphs else (lambda s: step(s))
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            run(s)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for s in range(args.steps):
+            run(s)
+        t1.record(stream)
+        torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    tokens_per_s = R * L / (ms_step / 1e3)
+    mean_step_bytes = float(np.mean([step_bytes[s % NX] for s in range(args.steps)]))
+    log(f"[bench] {ms_step * 1e3:.1f} us/step, {ms_step * 1e3 / L:.2f} us/layer, "
+        f"{tokens_per_s:.0f} tokens/s, step HBM {mean_step_bytes / ms_step / 1e6:.0f} GB/s")
+
+    # ---- dominant kernel: events around each kernel of the decode call
+    nk = max(1, min(args.steps, 50))
+    # events bracket each kernel: route, gate/up, down + combine
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
+           for _ in range(nk)]
+    with torch.cuda.stream(stream):
+        for es in evs:              # torch creates the HIP event on first record
+            for el in es:
+                for e in el:
+                    e.record(stream)
+        step(0)
+        torch.cuda.synchronize()
+        for s in range(nk):
+            step(s, events=evs[s])
+        torch.cuda.synchronize()
+    dur = np.zeros((3,))  # route, gate/up, down+combine
+    gu_bytes_sum = 0.0
+    for s in range(nk):
+        for l in range(L):
+            e = evs[s][l]
+            for i in range(3):
+                dur[i] += e[2 * i].elapsed_time(e[2 * i + 1])
+            gu_bytes_sum += gu_launch_bytes[l, s % NX]
+    n_launch = nk * L
+    gu_ms = dur[1] / n_launch
+    gu_bytes = gu_bytes_sum / n_launch
+    achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+    kus = dur / n_launch * 1e3
+    log(f"[bench] route {kus[0]:.2f} us, gate/up {kus[1]:.2f} us ({achieved:.0f} GB/s), "
+        f"down+combine {kus[2]:.2f} us")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        cpu = cpu_baseline(spec, host[0], R)
+        log(f"[bench] cpu baseline {cpu['value']:.3f} tokens/s")
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "rows": R, "layers": L, "hidden": H,
+                   "experts": spec.n_experts, "top_k": k, "inter": spec.inter,
+                   "shared_inter": spec.shared_inter, "weights": "affine 4-bit g64 bf16 scale/bias",
+                   "timing": "hip graph replay" if graphs else "eager"},
+        "roofline": {"bound": "hbm", "kernel": "k_dec_gateup", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "mean_us": gu_ms * 1e3, "bytes_per_launch": gu_bytes},
+        "step_hbm": {"algorithmic_bytes": mean_step_bytes,
+                     "gbs": mean_step_bytes / ms_step / 1e6,
+                     "frac": mean_step_bytes / ms_step / 1e6 / HBM_PEAK_GBS,
+                     "us_per_layer": ms_step * 1e3 / L,
+                     "kernel_us": {"route": kus[0], "decode_gateup": kus[1],
+                                   "decode_down_combine": kus[2]},
+                     "mean_unique_experts": float(uniq.mean())},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -130,6 +130,11 @@ typedef struct moe_taps {
   float* gu;
   float* h;
   float* e;
+  /* Optional timing: kernel_events[2i] / [2i+1] (hipEvent_t, may be NULL) are
+   * recorded on the stream just before / after the i-th kernel the call
+   * enqueues (route: 1 kernel; decode: gate/up, down + combine;
+   * grouped: see moe_experts_grouped). */
+  void* kernel_events[8];
 } moe_taps;
 
 /* ------------------------------------------------------------ pack loader */
@@ -161,8 +166,13 @@ int moe_layer_bind(moe_layer* layer, const void* dev_ptr);
 int moe_pack_layer(const moe_layer_desc* d, const moe_layer_src* src,
                    void* dev_dst, uint64_t dst_bytes, void* stream, moe_layer* out);
 
-/* Workspace bytes for moe_experts_decode (grouped = 0) or
- * moe_experts_grouped (grouped = 1) at `rows` rows. */
+/* Workspace bytes for moe_route plus moe_experts_decode (grouped = 0) or
+ * plus moe_experts_grouped (grouped = 1) at `rows` rows. One buffer of this
+ * size serves both calls of a layer (calls on one stream run in order).
+ * A workspace must be zero-filled before its first use: it holds arrival
+ * counters that kernels of one call use to hand work to each other, and
+ * every call leaves them at zero again. Calls that overlap on one workspace
+ * (e.g. on two streams) race; give each stream its own workspace. */
 int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t* bytes);
 
 /* ------------------------------------------------------------- hot path */
@@ -178,11 +188,13 @@ int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t*
  *   ids        device, [rows, k] int32, in pick order (logit desc, id asc)
  *   p          device, [rows, k] fp32
  *   shared_gate device, [rows] fp32 sigma(c)
- *   taps       NULL, or taps->logits (others ignored)
+ *   ws         device workspace, >= moe_workspace_size bytes for `rows`,
+ *              zero-filled before its first use (see moe_workspace_size)
+ *   taps       NULL, or taps->logits / kernel_events (route: 1 kernel)
  * A row holding NaN gets the NaN-ordered picks 0..k-1 and NaN weights. */
 int moe_route(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
-              int32_t* ids, float* p, float* shared_gate, const moe_taps* taps,
-              void* stream);
+              int32_t* ids, float* p, float* shared_gate, void* ws, uint64_t ws_bytes,
+              const moe_taps* taps, void* stream);
 
 /* Routed + shared experts and the combine for decode rows (one row per
  * stream; the per-row form with fp32 sums of the same comment). Expert-centric:
@@ -192,8 +204,10 @@ int moe_route(const moe_layer* layer, const void* x, int rows, const float* logi
  *   ids, p, shared_gate  from moe_route on the same layer and x
  *   y       device [rows, H] fp32
  *   ws      device workspace of moe_workspace_size(grouped=0) bytes
- * Preconditions: |x| < 65504 (activations are used as fp16; bf16 values of
- * magnitude below 2^-17 lose bits); ids valid for the layer. */
+ * Preconditions: ids valid for the layer (rows picking an id outside
+ * [0, E) get no contribution for that slot); |h| < 65504 (the SwiGLU
+ * output enters the down projection as fp16 high + low parts);
+ * fp16 activations are used as they are, bf16 ones exactly. */
 int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const int32_t* ids,
                        const float* p, const float* shared_gate, float* y, void* ws,
                        uint64_t ws_bytes, const moe_taps* taps, void* stream);

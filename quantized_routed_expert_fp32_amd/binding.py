@@ -59,7 +59,8 @@ class LayerC(C.Structure):
 
 
 class TapsC(C.Structure):
-    _fields_ = [("logits", C.c_void_p), ("gu", C.c_void_p), ("h", C.c_void_p), ("e", C.c_void_p)]
+    _fields_ = [("logits", C.c_void_p), ("gu", C.c_void_p), ("h", C.c_void_p), ("e", C.c_void_p),
+                ("kernel_events", C.c_void_p * 8)]
 
 
 EXPORTS = ["moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
@@ -86,7 +87,8 @@ def lib() -> C.CDLL:
     L.moe_pack_layer.argtypes = [C.POINTER(LayerDescC), C.POINTER(LayerSrcC), vp, u64, vp,
                                  C.POINTER(LayerC)]
     L.moe_workspace_size.argtypes = [C.POINTER(LayerDescC), i32, i32, C.POINTER(u64)]
-    L.moe_route.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, C.POINTER(TapsC), vp]
+    L.moe_route.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, u64, C.POINTER(TapsC),
+                            vp]
     L.moe_experts_decode.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, u64,
                                      C.POINTER(TapsC), vp]
     L.moe_experts_grouped.argtypes = L.moe_experts_decode.argtypes
@@ -199,13 +201,23 @@ def workspace_size(desc: LayerDescC, rows: int, grouped: bool) -> int:
     return n.value
 
 
+def new_workspace(layer: "Layer", rows: int, grouped: bool, device="cuda"):
+    """A zero-filled workspace for `rows` rows (route + experts of one layer)."""
+    import torch
+    return torch.zeros(workspace_size(layer.desc, rows, grouped), dtype=torch.uint8, device=device)
+
+
 def _taps(taps: Optional[dict]):
+    """taps: dict of optional device tensors logits/gu/h/e and an optional
+    list "events" of torch.cuda.Event (or None) bracketing each kernel."""
     if not taps:
         return None
     t = TapsC()
     for k in ("logits", "gu", "h", "e"):
         v = taps.get(k)
         setattr(t, k, v.data_ptr() if v is not None else None)
+    for i, ev in enumerate(taps.get("events") or []):
+        t.kernel_events[i] = ev.cuda_event if ev is not None else None
     return C.byref(t)
 
 
@@ -213,7 +225,7 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def route(layer: Layer, x, logit_bias=None, taps=None, out=None, stream=None):
+def route(layer: Layer, x, logit_bias=None, taps=None, out=None, ws=None, stream=None):
     """moe_route: returns (ids int32 [R,k], p fp32 [R,k], shared_gate fp32 [R])."""
     import torch
     R = x.shape[0]
@@ -224,8 +236,11 @@ def route(layer: Layer, x, logit_bias=None, taps=None, out=None, stream=None):
         sg = torch.empty((R,), dtype=torch.float32, device=x.device)
     else:
         ids, p, sg = out
+    if ws is None:
+        ws = new_workspace(layer, R, R > 16, x.device)
     _check(lib().moe_route(C.byref(layer.c), _ptr(x), R, _ptr(logit_bias), _ptr(ids), _ptr(p),
-                           _ptr(sg), _taps(taps), _stream_ptr(stream)), "moe_route")
+                           _ptr(sg), _ptr(ws), ws.numel() * ws.element_size(), _taps(taps),
+                           _stream_ptr(stream)), "moe_route")
     return ids, p, sg
 
 
@@ -237,8 +252,7 @@ def experts(layer: Layer, x, ids, p, sg, grouped: bool, ws=None, taps=None, y=No
     if y is None:
         y = torch.empty((R, layer.desc.hidden), dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = torch.empty(workspace_size(layer.desc, R, grouped), dtype=torch.uint8,
-                         device=x.device)
+        ws = new_workspace(layer, R, grouped, x.device)
     fn = lib().moe_experts_grouped if grouped else lib().moe_experts_decode
     _check(fn(C.byref(layer.c), _ptr(x), R, _ptr(ids), _ptr(p), _ptr(sg), _ptr(y), _ptr(ws),
               ws.numel() * ws.element_size(), _taps(taps), _stream_ptr(stream)),

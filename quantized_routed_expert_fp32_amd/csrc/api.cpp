@@ -38,6 +38,10 @@ static int check_layer(const moe_layer* L) {
   return MOE_OK;
 }
 
+static hipEvent_t* taps_events(const moe_taps* taps) {
+  return taps ? reinterpret_cast<hipEvent_t*>(const_cast<void**>(taps->kernel_events)) : nullptr;
+}
+
 static ExpertClass expert_class(const moe_layer* L, bool shared) {
   ExpertClass c;
   if (shared) {
@@ -125,11 +129,20 @@ int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t*
 }
 
 int moe_route(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
-              int32_t* ids, float* p, float* shared_gate, const moe_taps* taps, void* stream) {
+              int32_t* ids, float* p, float* shared_gate, void* ws, uint64_t ws_bytes,
+              const moe_taps* taps, void* stream) {
   int st = check_layer(layer);
   if (st) return st;
-  if (!x || !ids || !p || !shared_gate) { set_error("moe_route: NULL x/ids/p/shared_gate"); return MOE_EINVAL; }
+  if (!x || !ids || !p || !shared_gate || !ws) {
+    set_error("moe_route: NULL x/ids/p/shared_gate/ws");
+    return MOE_EINVAL;
+  }
   if (rows < 1 || rows > 65536) { set_error("moe_route: rows outside 1..65536"); return MOE_EINVAL; }
+  if (ws_bytes < route_ws_bytes(&layer->d, rows)) {
+    set_error("moe_route: workspace of " + std::to_string(ws_bytes) + " bytes, needs " +
+              std::to_string(route_ws_bytes(&layer->d, rows)));
+    return MOE_ENOSPACE;
+  }
   FmtInfo fr, fg;
   format_info(layer->d.router, TC_ROUTER, &fr);
   format_info(layer->d.gate_row, TC_GATE_ROW, &fg);
@@ -148,8 +161,14 @@ int moe_route(const moe_layer* layer, const void* x, int rows, const float* logi
   a.ids = ids;
   a.p = p;
   a.sg = shared_gate;
+  a.R = rows;
   a.logits = taps ? taps->logits : nullptr;
-  hipError_t e = launch_route(fr.kid, fg.kid, a, rows, static_cast<hipStream_t>(stream));
+  const RouteWs rw = route_ws_layout(&layer->d, rows);
+  uint8_t* wb = static_cast<uint8_t*>(ws);
+  a.cnt = reinterpret_cast<unsigned*>(wb + rw.cnt_off);
+  a.gl_ws = reinterpret_cast<float*>(wb + rw.gl_off);
+  a.lg_ws = reinterpret_cast<float*>(wb + rw.lg_off);
+  hipError_t e = launch_route(fr.kid, fg.kid, a, static_cast<hipStream_t>(stream), taps_events(taps));
   if (e != hipSuccess) return hip_fail("moe_route: launch", e);
   return MOE_OK;
 }
@@ -200,13 +219,14 @@ int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const in
   a.p = p;
   a.sg = shared_gate;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  a.h_ws = reinterpret_cast<float*>(w + wl.h_off);
-  a.e_ws = reinterpret_cast<float*>(w + wl.e_off);
+  a.hhi = reinterpret_cast<uint16_t*>(w + wl.hhi_off);
+  a.hlo = reinterpret_cast<uint16_t*>(w + wl.hlo_off);
+  a.hc = reinterpret_cast<float*>(w + wl.hc_off);
   a.y = y;
   a.tap_gu = taps ? taps->gu : nullptr;
   a.tap_h = taps ? taps->h : nullptr;
   a.tap_e = taps ? taps->e : nullptr;
-  hipError_t e = launch_decode(fe.kid, fs.kid, a, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_decode(fe.kid, fs.kid, a, static_cast<hipStream_t>(stream), taps_events(taps));
   if (e != hipSuccess) return hip_fail("moe_experts_decode: launch", e);
   return MOE_OK;
 }
@@ -251,7 +271,7 @@ int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const i
   a.tap_gu = taps ? taps->gu : nullptr;
   a.tap_h = taps ? taps->h : nullptr;
   a.tap_e = taps ? taps->e : nullptr;
-  hipError_t e = launch_grouped(fe.kid, fs.kid, a, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_grouped(fe.kid, fs.kid, a, static_cast<hipStream_t>(stream), taps_events(taps));
   if (e != hipSuccess) return hip_fail("moe_experts_grouped: launch", e);
   return MOE_OK;
 }

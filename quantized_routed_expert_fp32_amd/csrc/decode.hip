@@ -1,365 +1,263 @@
 // Decode path: routed + shared experts for up to 16 independent rows.
 //
-// Expert-centric: one workgroup per (unique expert of the batch, 64-row tile).
-// It streams the tile's packed codes once (coalesced 128-bit loads, lane =
-// output row) and applies them to every row that picked the expert. Rows
-// sharing an expert share its reads ("Native server: --backend xpu for
-// Nemotron on Intel Arc", review comments: each extra row costs about 3.7 ms
-// because more distinct experts are read; a gain needs expert reads shared
-// across rows).
+// gate/up (k_dec_gateup): one workgroup per (unit, 64-row tile of the
+// interleaved gate/up matrix), one wave per 256-wide K slice. A unit is a
+// slot (row r, pick j) whose expert no earlier slot picked, or the shared
+// expert for one row: it streams the tile's packed codes once (coalesced 128-bit loads,
+// lane = weight row) for every row that picked the expert, so rows sharing
+// an expert share its reads ("Native server: --backend xpu for Nemotron on
+// Intel Arc", review comments: each extra row costs more because more
+// distinct experts are read; the gain needs expert reads shared across
+// rows). Each wave finds its unit from the picks with one ballot (no LDS, no
+// barrier) and reads activations with uniform loads straight into
+// v_dot2_f32_bf16 / v_dot2_f32_f16. Output: h = silu(g)*u split into fp16
+// hi + lo parts (22 significant bits) plus per-32 chunk sums, for down.
 //
-// Each row's arithmetic is fixed: K is cut into 256-wide slices owned by
-// fixed waves, chunks and groups are summed in K order, slices are reduced
-// in LDS in wave order, and the combine runs the slots in pick order with
-// the shared expert last. None of it depends on how many rows share the
-// launch, so a row's y is bit-identical alone or in a batch ("Sage-A1.5 ...
-// #1329", Limits to agree on: the per-row kernels keep one stream's sum).
+// down + combine (k_dec_down): one workgroup per (row, 64-column tile of y),
+// one wave per slot (k routed + shared). Each wave computes its slot's
+// output columns over the full intermediate axis; wave 0 then forms
+// y = sum_j p_j e_j + sigma e_shared in slot order. Blocks are mapped so
+// the rows of one tile run on one XCD and share the shared expert's tile
+// in that XCD's L2.
 //
-// Kernels per call: gate/up + SwiGLU -> h (fp32), down -> e (fp32), combine -> y.
+// Every row's arithmetic is fixed (K slices owned by fixed waves, chunks
+// and groups in K order, slices reduced in slice order, slots combined in
+// pick order, shared last) and independent of the other rows, so a row's y
+// is bit-identical alone or in a batch ("Sage-A1.5 ... #1329", Limits to
+// agree on: the per-row kernels keep one stream's sum order).
 #include "moe_kernels.h"
 #include "moe_launch.h"
 
 namespace moe {
 
-constexpr int GU_WAVES = 8;   // waves per gate/up workgroup (K slices of 256)
-constexpr int DN_WAVES = 2;   // waves per down workgroup
-constexpr int NRP = 4;        // rows per pass
-
-// Finds which expert this workgroup serves (unit u: the u-th smallest picked
-// id, then the shared expert at u == #unique) and the rows (ascending) that
-// picked it with their slot. Returns the expert id, E for the shared expert,
-// or -1 when the unit is empty.
-__device__ int resolve_unit(const int32_t* ids, int R, int k, int E, int u, int* s_rows,
-                            int* s_slots, int* s_nr, uint32_t* s_mask, int* s_expert) {
-  const int tid = threadIdx.x;
-  if (tid < 8) s_mask[tid] = 0u;
-  __syncthreads();
-  for (int i = tid; i < R * k; i += blockDim.x) {
-    const int id = ids[i];
-    if (id >= 0 && id < E) atomicOr(&s_mask[id >> 5], 1u << (id & 31));
+// Rows of one unit, one at a time: the wave's codes stay in registers (one
+// K slice per wave when H <= 2048) and each row re-runs the unpack, which is
+// free for the usual single-row unit.
+template <int F, int ACT16>
+__device__ __forceinline__ void gu_body(const DecodeArgs& a, const uint16_t* __restrict__ x,
+                                        const uint8_t* codes, const uint8_t* scales,
+                                        int t, int nrows, int shared_row, uint64_t m0, uint64_t m1,
+                                        float* red, uint32_t* lx) {
+  // wave wv owns the K slices wv, wv + nw, ...
+  const int H = a.H, k = a.k, nsl = H / KBLK, nch = H / 32;
+  const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  uint32_t w[8][Fmt<F>::WORDS];
+  if (wv < nsl) {
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) load_chunk<F>(codes + chunk_off<F>(t, wv * 8 + cc, nch), lane, w[cc]);
   }
-  __syncthreads();
-  if (tid == 0) {
-    int nu = 0;
-    for (int w = 0; w < 8; ++w) nu += __popc(s_mask[w]);
-    int e = -1;
-    if (u < nu) {
-      int left = u;
-      for (int w = 0; w < 8; ++w) {
-        const int c = __popc(s_mask[w]);
-        if (left < c) {
-          uint32_t m = s_mask[w];
-          for (int b = 0; b < left; ++b) m &= m - 1;   // drop the lowest set bits
-          e = 32 * w + __ffs(m) - 1;
-          break;
-        }
-        left -= c;
+  for (int i = 0; i < nrows; ++i) {
+    int r = shared_row, j = k;
+    if (shared_row < 0) {
+      int s;
+      if (m0) { s = __ffsll((unsigned long long)m0) - 1; m0 &= m0 - 1; }
+      else { s = 64 + __ffsll((unsigned long long)m1) - 1; m1 &= m1 - 1; }
+      r = s / k;
+      j = s % k;
+    }
+    float out = 0.f;
+    for (int sl = wv; sl < nsl; sl += nw) {
+      if (sl != wv) {
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) load_chunk<F>(codes + chunk_off<F>(t, sl * 8 + cc, nch), lane, w[cc]);
       }
-    } else if (u == nu) {
-      e = E;
+      const uint16_t* xs[1] = {x + (uint64_t)r * H + sl * KBLK};
+      float part[1];
+      slice_dot<F, 1, ACT16>(w, scales + sblk_off<F>(t, sl, nsl), lane, xs, 1, lx + wv * 128, part);
+      out += part[0];
     }
-    *s_expert = e;
-  }
-  __syncthreads();
-  const int e = *s_expert;
-  if (e < 0) return -1;
-  if (tid < 64) {
-    int slot = -1;
-    if (tid < R) {
-      if (e == E) {
-        slot = k;
-      } else {
-        for (int j = 0; j < k; ++j)
-          if (ids[tid * k + j] == e) { slot = j; break; }
-      }
-    }
-    const unsigned long long m = __ballot(slot >= 0);
-    const int pos = __popcll(m & ((1ull << tid) - 1ull));
-    if (slot >= 0) { s_rows[pos] = tid; s_slots[pos] = slot; }
-    if (tid == 0) *s_nr = __popcll(m);
-  }
-  __syncthreads();
-  return e;
-}
-
-// ------------------------------------------------------------------ gate/up
-template <int F>
-__device__ void gateup_body(const DecodeArgs& a, const uint8_t* codes, const uint8_t* scales,
-                            int t, int n_r, const int* s_rows, const int* s_slots,
-                            uint8_t* smem) {
-  const int H = a.H, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nch = H / 32, nkb = H / KBLK;
-  half2v* xh = reinterpret_cast<half2v*>(smem);           // [NRP][H/2]
-  float* xc = reinterpret_cast<float*>(xh + NRP * (H / 2)); // [NRP][H/32]
-  float* red = xc + NRP * (H / 32);                        // [GU_WAVES][NRP][64]
-  constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
-  for (int r0 = 0; r0 < n_r; r0 += NRP) {
-    const int nr = min(NRP, n_r - r0);
-    for (int i = tid; i < nr * (H / 2); i += blockDim.x) {
-      const int rr = i / (H / 2), ii = i % (H / 2);
-      const uint32_t v = reinterpret_cast<const uint32_t*>(a.x + (uint64_t)s_rows[r0 + rr] * H)[ii];
-      half2v h;
-      h.x = (f16)act_to_f((uint16_t)(v & 0xFFFFu), a.act_fp16);
-      h.y = (f16)act_to_f((uint16_t)(v >> 16), a.act_fp16);
-      xh[rr * (H / 2) + ii] = h;
-    }
+    red[wv * 64 + lane] = out;
     __syncthreads();
-    for (int i = tid; i < nr * nch; i += blockDim.x) {
-      const int rr = i / nch, c = i % nch;
-      const half2v* xr = xh + rr * (H / 2) + 16 * c;
-      float s = 0.f;
-      for (int q = 0; q < 16; ++q) {
-        s += (float)xr[q].x;
-        s += (float)xr[q].y;
+    if (tid < 64) {
+      const int c = tid & 31;
+      float g = 0.f, u = 0.f;
+      for (int q = 0; q < nw; ++q) {
+        g += red[q * 64 + c];
+        u += red[q * 64 + 32 + c];
       }
-      xc[rr * nch + c] = s;
-    }
-    __syncthreads();
-    float out[NRP];
-#pragma unroll
-    for (int rr = 0; rr < NRP; ++rr) out[rr] = 0.f;
-    for (int sl = wave; sl < nkb; sl += GU_WAVES) {
-      uint32_t w[8][Fmt<F>::WORDS];
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) load_chunk<F>(codes + chunk_off<F>(t, sl * 8 + cc, nch), lane, w[cc]);
-      const uint8_t* sblk = scales + sblk_off<F>(t, sl, nkb);
-#pragma unroll
-      for (int gi = 0; gi < GPS; ++gi) {
-        float ms, bm;
-        group_coef<F>(sblk, lane, gi, ms, bm);
-        float acc[NRP];
-#pragma unroll
-        for (int rr = 0; rr < NRP; ++rr) acc[rr] = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < CPG; ++cc) {
-          const int c = sl * 8 + gi * CPG + cc;
-          uint32_t v[16];
-          unpack_chunk<F>(w[gi * CPG + cc], v);
-#pragma unroll
-          for (int rr = 0; rr < NRP; ++rr)
-            if (rr < nr) acc[rr] = dot_chunk(v, xh + rr * (H / 2) + 16 * c, acc[rr]);
-        }
-#pragma unroll
-        for (int rr = 0; rr < NRP; ++rr) {
-          if (rr < nr) {
-            float X = 0.f;
-            for (int cc = 0; cc < CPG; ++cc) X += xc[rr * nch + sl * 8 + gi * CPG + cc];
-            out[rr] = fmaf(ms, acc[rr], out[rr]);
-            out[rr] = fmaf(bm, X, out[rr]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < NRP; ++rr) red[(wave * NRP + rr) * 64 + lane] = out[rr];
-    __syncthreads();
-    if (tid < NRP * 32) {
-      const int rr = tid / 32, j = tid % 32;
-      if (rr < nr) {
-        float g = 0.f, u = 0.f;
-        for (int w2 = 0; w2 < GU_WAVES; ++w2) {
-          g += red[(w2 * NRP + rr) * 64 + j];
-          u += red[(w2 * NRP + rr) * 64 + 32 + j];
-        }
-        const int r = s_rows[r0 + rr], slot = s_slots[r0 + rr];
-        const uint64_t rs = (uint64_t)r * (a.k + 1) + slot;
-        const int col = 32 * t + j;
-        a.h_ws[rs * a.Imax + col] = silu_mul(g, u);
+      const float hv = silu_mul(g, u);
+      const f16 hi = (f16)hv, lo = (f16)(hv - (float)hi);
+      // chunk sum of hi + lo over the 32 columns: 16-lane rows by DPP, then
+      // the two rows in order (lanes 0..31 and 32..63 hold the same values)
+      const float s16 = sum16((float)hi + (float)lo);
+      const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 0)) +
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 16));
+      if (tid < 32) {
+        const uint64_t rs = (uint64_t)r * (k + 1) + j;
+        const int col = 32 * t + c;
+        a.hhi[rs * a.Imax + col] = __builtin_bit_cast(uint16_t, hi);
+        a.hlo[rs * a.Imax + col] = __builtin_bit_cast(uint16_t, lo);
+        if (c == 0) a.hc[rs * (a.Imax / 32) + t] = sv;
         if (a.tap_gu) {
           a.tap_gu[(rs * 2 + 0) * a.Imax + col] = g;
           a.tap_gu[(rs * 2 + 1) * a.Imax + col] = u;
         }
-        if (a.tap_h) a.tap_h[rs * a.Imax + col] = silu_mul(g, u);
+        if (a.tap_h) a.tap_h[rs * a.Imax + col] = hv;
       }
     }
     __syncthreads();
   }
 }
 
-template <int FR, int FS>
-__global__ __launch_bounds__(64 * GU_WAVES) void k_decode_gateup(DecodeArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int s_rows[16], s_slots[16], s_nr, s_expert;
-  __shared__ uint32_t s_mask[8];
-  const int e = resolve_unit(a.ids, a.R, a.k, a.E, blockIdx.y, s_rows, s_slots, &s_nr, s_mask,
-                             &s_expert);
-  if (e < 0) return;
-  const int t = blockIdx.x;
-  if (e == a.E) {
+// grid (gate/up tiles, R*k + R units): unit u < R*k is slot u when no earlier
+// slot picked its expert; unit R*k + r is the shared expert for row r. With
+// the linear block index t + 16u, every unit of tile t runs on XCD t % 8, so
+// the shared expert's rows re-read its tile from that XCD's L2.
+template <int FR, int FS, int ACT16>
+__global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a, const uint16_t* __restrict__ x) {
+  extern __shared__ __align__(16) float red[];   // [waves][64], then per-wave x slices
+  uint32_t* lx = reinterpret_cast<uint32_t*>(red + (blockDim.x >> 6) * 64);
+  const int t = blockIdx.x, u = blockIdx.y, lane = threadIdx.x & 63;
+  const int nslot = a.R * a.k;
+  if (u < nslot) {
+    const int e = a.ids[u];
+    if (e < 0 || e >= a.E) return;
+    if (t >= 2 * a.rt.inter / 64) return;
+    const int id0 = lane < nslot ? a.ids[lane] : -1;
+    const int id1 = lane + 64 < nslot ? a.ids[lane + 64] : -1;
+    const uint64_t m0 = __ballot(id0 == e), m1 = __ballot(id1 == e);
+    const int first = m0 ? __ffsll((unsigned long long)m0) - 1 : 64 + __ffsll((unsigned long long)m1) - 1;
+    if (first != u) return;        // an earlier slot's unit serves this expert
+    const uint8_t* blk = a.base + a.rt.base_off + (uint64_t)e * a.rt.stride;
+    gu_body<FR, ACT16>(a, x, blk + a.rt.gu_codes, blk + a.rt.gu_scales, t, __popcll(m0) + __popcll(m1),
+                       -1, m0, m1, red, lx);
+  } else {
     if (t >= 2 * a.sh.inter / 64) return;
     const uint8_t* blk = a.base + a.sh.base_off;
-    gateup_body<FS>(a, blk + a.sh.gu_codes, blk + a.sh.gu_scales, t, s_nr, s_rows, s_slots, smem);
-  } else {
-    if (t >= 2 * a.rt.inter / 64) return;
-    const uint8_t* blk = a.base + a.rt.base_off + (uint64_t)e * a.rt.stride;
-    gateup_body<FR>(a, blk + a.rt.gu_codes, blk + a.rt.gu_scales, t, s_nr, s_rows, s_slots, smem);
+    gu_body<FS, ACT16>(a, x, blk + a.sh.gu_codes, blk + a.sh.gu_scales, t, 1, u - nslot, 0, 0, red, lx);
   }
 }
 
-// --------------------------------------------------------------------- down
+// one slot's 64 output columns of tile t over the full intermediate axis
 template <int F>
-__device__ void down_body(const DecodeArgs& a, const uint8_t* codes, const uint8_t* scales, int I,
-                          int t, int n_r, const int* s_rows, const int* s_slots, uint8_t* smem) {
-  const int H = a.H, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nch = I / 32, nkb = I / KBLK;
-  half2v* hhi = reinterpret_cast<half2v*>(smem);            // [NRP][Imax/2]
-  half2v* hlo = hhi + NRP * (a.Imax / 2);                    // [NRP][Imax/2]
-  float* hc = reinterpret_cast<float*>(hlo + NRP * (a.Imax / 2));  // [NRP][Imax/32]
-  float* red = hc + NRP * (a.Imax / 32);                     // [DN_WAVES][NRP][64]
-  const int hs = a.Imax / 2, cs = a.Imax / 32;
+__device__ __forceinline__ float dn_slot(const DecodeArgs& a, const uint32_t* __restrict__ hh,
+                                         const uint32_t* __restrict__ hl, const float* __restrict__ hc,
+                                         const uint8_t* codes, const uint8_t* scales,
+                                         int I, int t, int lane) {
   constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
-  for (int r0 = 0; r0 < n_r; r0 += NRP) {
-    const int nr = min(NRP, n_r - r0);
-    for (int i = tid; i < nr * (I / 2); i += blockDim.x) {
-      const int rr = i / (I / 2), ii = i % (I / 2);
-      const uint64_t rs = (uint64_t)s_rows[r0 + rr] * (a.k + 1) + s_slots[r0 + rr];
-      const float2 hv = reinterpret_cast<const float2*>(a.h_ws + rs * a.Imax)[ii];
-      half2v hi, lo;
-      hi.x = (f16)hv.x;
-      hi.y = (f16)hv.y;
-      lo.x = (f16)(hv.x - (float)hi.x);
-      lo.y = (f16)(hv.y - (float)hi.y);
-      hhi[rr * hs + ii] = hi;
-      hlo[rr * hs + ii] = lo;
-    }
-    __syncthreads();
-    for (int i = tid; i < nr * nch; i += blockDim.x) {
-      const int rr = i / nch, c = i % nch;
-      float s = 0.f;
-      for (int q = 0; q < 16; ++q) {
-        const half2v hi = hhi[rr * hs + 16 * c + q], lo = hlo[rr * hs + 16 * c + q];
-        s += (float)hi.x + (float)lo.x;
-        s += (float)hi.y + (float)lo.y;
-      }
-      hc[rr * cs + c] = s;
-    }
-    __syncthreads();
-    float out[NRP];
+  const int nch = I / 32, nkb = I / KBLK;
+  float out = 0.f;
+  for (int s0 = 0; s0 < nkb; s0 += 2) {
+    const int ns = min(2, nkb - s0);
+    uint32_t w[2][8][Fmt<F>::WORDS];
 #pragma unroll
-    for (int rr = 0; rr < NRP; ++rr) out[rr] = 0.f;
-    for (int sl = wave; sl < nkb; sl += DN_WAVES) {
-      uint32_t w[8][Fmt<F>::WORDS];
+    for (int q = 0; q < 2; ++q)
+      if (q < ns)
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) load_chunk<F>(codes + chunk_off<F>(t, sl * 8 + cc, nch), lane, w[cc]);
-      const uint8_t* sblk = scales + sblk_off<F>(t, sl, nkb);
+        for (int cc = 0; cc < 8; ++cc)
+          load_chunk<F>(codes + chunk_off<F>(t, (s0 + q) * 8 + cc, nch), lane, w[q][cc]);
 #pragma unroll
-      for (int gi = 0; gi < GPS; ++gi) {
-        float ms, bm;
-        group_coef<F>(sblk, lane, gi, ms, bm);
-        float acc[NRP];
+    for (int q = 0; q < 2; ++q) {
+      if (q < ns) {
+        const int sl = s0 + q;
+        const uint8_t* sblk = scales + sblk_off<F>(t, sl, nkb);
 #pragma unroll
-        for (int rr = 0; rr < NRP; ++rr) acc[rr] = 0.f;
+        for (int gi = 0; gi < GPS; ++gi) {
+          float ms, bm;
+          group_coef<F>(sblk, lane, gi, ms, bm);
+          float acc = 0.f, X = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < CPG; ++cc) {
-          const int c = sl * 8 + gi * CPG + cc;
-          uint32_t v[16];
-          unpack_chunk<F>(w[gi * CPG + cc], v);
+          for (int cc = 0; cc < CPG; ++cc) {
+            const int c = sl * 8 + gi * CPG + cc;
+            uint32_t v[16], ph[16], pl[16];
+            unpack_chunk<F>(w[q][gi * CPG + cc], v);
 #pragma unroll
-          for (int rr = 0; rr < NRP; ++rr) {
-            if (rr < nr) {
-              acc[rr] = dot_chunk(v, hhi + rr * hs + 16 * c, acc[rr]);
-              acc[rr] = dot_chunk(v, hlo + rr * hs + 16 * c, acc[rr]);
-            }
+            for (int p = 0; p < 16; ++p) { ph[p] = hh[16 * c + p]; pl[p] = hl[16 * c + p]; }
+            acc = dot_chunk_h(v, ph, acc);
+            acc = dot_chunk_h(v, pl, acc);
+            X += hc[c];
           }
-        }
-#pragma unroll
-        for (int rr = 0; rr < NRP; ++rr) {
-          if (rr < nr) {
-            float X = 0.f;
-            for (int cc = 0; cc < CPG; ++cc) X += hc[rr * cs + sl * 8 + gi * CPG + cc];
-            out[rr] = fmaf(ms, acc[rr], out[rr]);
-            out[rr] = fmaf(bm, X, out[rr]);
-          }
+          out = fmaf(ms, acc, out);
+          out = fmaf(bm, X, out);
         }
       }
     }
-#pragma unroll
-    for (int rr = 0; rr < NRP; ++rr) red[(wave * NRP + rr) * 64 + lane] = out[rr];
-    __syncthreads();
-    for (int i = tid; i < nr * 64; i += blockDim.x) {
-      const int rr = i / 64, l = i % 64;
-      float s = 0.f;
-      for (int w2 = 0; w2 < DN_WAVES; ++w2) s += red[(w2 * NRP + rr) * 64 + l];
-      const uint64_t rs = (uint64_t)s_rows[r0 + rr] * (a.k + 1) + s_slots[r0 + rr];
-      a.e_ws[rs * H + 64 * t + l] = s;
-      if (a.tap_e) a.tap_e[rs * H + 64 * t + l] = s;
-    }
-    __syncthreads();
   }
+  return out;
 }
 
 template <int FR, int FS>
-__global__ __launch_bounds__(64 * DN_WAVES) void k_decode_down(DecodeArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int s_rows[16], s_slots[16], s_nr, s_expert;
-  __shared__ uint32_t s_mask[8];
-  const int e = resolve_unit(a.ids, a.R, a.k, a.E, blockIdx.y, s_rows, s_slots, &s_nr, s_mask,
-                             &s_expert);
-  if (e < 0) return;
-  const int t = blockIdx.x;
-  if (e == a.E) {
-    const uint8_t* blk = a.base + a.sh.base_off;
-    down_body<FS>(a, blk + a.sh.dn_codes, blk + a.sh.dn_scales, a.sh.inter, t, s_nr, s_rows,
-                  s_slots, smem);
+__global__ __launch_bounds__(576) void k_dec_down(DecodeArgs a, const uint16_t* __restrict__ hhi,
+                                                  const uint16_t* __restrict__ hlo,
+                                                  const float* __restrict__ hcs) {
+  __shared__ float es[9][64];
+  const int T = a.H / 64, R = a.R, k = a.k;
+  const int wg = blockIdx.x;
+  int t, r;
+  if (T % 8 == 0) {          // rows of one tile on one XCD (round-robin dispatch over 8 XCDs)
+    const int xcd = wg % 8, loc = wg / 8;
+    t = xcd + 8 * (loc / R);
+    r = loc % R;
   } else {
-    const uint8_t* blk = a.base + a.rt.base_off + (uint64_t)e * a.rt.stride;
-    down_body<FR>(a, blk + a.rt.dn_codes, blk + a.rt.dn_scales, a.rt.inter, t, s_nr, s_rows,
-                  s_slots, smem);
+    t = wg / R;
+    r = wg % R;
   }
-}
-
-// ------------------------------------------------------------------ combine
-__global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a) {
-  const int n = blockIdx.x * 256 + threadIdx.x, r = blockIdx.y;
-  if (n >= a.H) return;
-  const int k = a.k;
-  const float* e = a.e_ws + (uint64_t)r * (k + 1) * a.H + n;
-  float acc = 0.f;
-  for (int j = 0; j < k; ++j) acc = fmaf(a.p[r * k + j], e[(uint64_t)j * a.H], acc);
-  acc = fmaf(a.sg[r], e[(uint64_t)k * a.H], acc);
-  a.y[(uint64_t)r * a.H + n] = acc;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int j = __builtin_amdgcn_readfirstlane(tid >> 6);   // slot of this wave, uniform
+  const uint64_t rs = (uint64_t)r * (k + 1) + j;
+  const uint32_t* hh = reinterpret_cast<const uint32_t*>(hhi + rs * a.Imax);
+  const uint32_t* hl = reinterpret_cast<const uint32_t*>(hlo + rs * a.Imax);
+  const float* hc = hcs + rs * (a.Imax / 32);
+  float e_out = 0.f;
+  if (j < k) {
+    const int e = a.ids[r * k + j];
+    if (e >= 0 && e < a.E) {
+      const uint8_t* blk = a.base + a.rt.base_off + (uint64_t)e * a.rt.stride;
+      e_out = dn_slot<FR>(a, hh, hl, hc, blk + a.rt.dn_codes, blk + a.rt.dn_scales, a.rt.inter, t, lane);
+    }
+  } else {
+    const uint8_t* blk = a.base + a.sh.base_off;
+    e_out = dn_slot<FS>(a, hh, hl, hc, blk + a.sh.dn_codes, blk + a.sh.dn_scales, a.sh.inter, t, lane);
+  }
+  es[j][lane] = e_out;
+  if (a.tap_e) a.tap_e[rs * a.H + 64 * t + lane] = e_out;
+  __syncthreads();
+  if (j == 0) {
+    float y = 0.f;
+    for (int q = 0; q < k; ++q) y = fmaf(a.p[r * k + q], es[q][lane], y);
+    y = fmaf(a.sg[r], es[k][lane], y);
+    a.y[(uint64_t)r * a.H + 64 * t + lane] = y;
+  }
 }
 
 // ------------------------------------------------------------------ launch
-static size_t gu_smem(int H) {
-  return (size_t)NRP * (H / 2) * 4 + (size_t)NRP * (H / 32) * 4 + (size_t)GU_WAVES * NRP * 64 * 4;
-}
-static size_t dn_smem(int Imax) {
-  return (size_t)2 * NRP * (Imax / 2) * 4 + (size_t)NRP * (Imax / 32) * 4 +
-         (size_t)DN_WAVES * NRP * 64 * 4;
-}
-
 template <int FR, int FS>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-  const int units = min(a.E, a.R * a.k) + 1;
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
+  const int nw = min(8, a.H / KBLK);
+  const int units = a.R * a.k + a.R;
   const int gu_tiles = 2 * a.Imax / 64;
-  hipLaunchKernelGGL((k_decode_gateup<FR, FS>), dim3(gu_tiles, units), dim3(64 * GU_WAVES),
-                     gu_smem(a.H), s, a);
+  const size_t smem = (size_t)nw * 64 * 4 + (size_t)nw * 512;
+  mark(ev, 0, s);
+  if (a.act_fp16)
+    hipLaunchKernelGGL((k_dec_gateup<FR, FS, 1>), dim3(gu_tiles, units), dim3(64 * nw), smem, s, a, a.x);
+  else
+    hipLaunchKernelGGL((k_dec_gateup<FR, FS, 0>), dim3(gu_tiles, units), dim3(64 * nw), smem, s, a, a.x);
+  mark(ev, 1, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((k_decode_down<FR, FS>), dim3(a.H / 64, units), dim3(64 * DN_WAVES),
-                     dn_smem(a.Imax), s, a);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_decode_combine, dim3((a.H + 255) / 256, a.R), dim3(256), 0, s, a);
+  mark(ev, 2, s);
+  hipLaunchKernelGGL((k_dec_down<FR, FS>), dim3((a.H / 64) * a.R), dim3(64 * (a.k + 1)), 0, s, a,
+                     a.hhi, a.hlo, a.hc);
+  mark(ev, 3, s);
   return hipGetLastError();
 }
 
 template <int FR>
-static hipError_t launch_decode_s(int fs, const DecodeArgs& a, hipStream_t s) {
+static hipError_t launch_decode_s(int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   switch (fs) {
-    case F_Q4: return launch_decode_t<FR, F_Q4>(a, s);
-    case F_Q3: return launch_decode_t<FR, F_Q3>(a, s);
-    case F_S4: return launch_decode_t<FR, F_S4>(a, s);
+    case F_Q4: return launch_decode_t<FR, F_Q4>(a, s, ev);
+    case F_Q3: return launch_decode_t<FR, F_Q3>(a, s, ev);
+    case F_S4: return launch_decode_t<FR, F_S4>(a, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   switch (fr) {
-    case F_Q4: return launch_decode_s<F_Q4>(fs, a, s);
-    case F_Q3: return launch_decode_s<F_Q3>(fs, a, s);
-    case F_S4: return launch_decode_s<F_S4>(fs, a, s);
+    case F_Q4: return launch_decode_s<F_Q4>(fs, a, s, ev);
+    case F_Q3: return launch_decode_s<F_Q3>(fs, a, s, ev);
+    case F_S4: return launch_decode_s<F_S4>(fs, a, s, ev);
   }
   return hipErrorInvalidValue;
 }

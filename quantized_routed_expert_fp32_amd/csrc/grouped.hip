@@ -3,5 +3,5 @@
 #include "moe_launch.h"
 
 namespace moe {
-hipError_t launch_grouped(int, int, const GroupedArgs&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_grouped(int, int, const GroupedArgs&, hipStream_t, hipEvent_t*) { return hipErrorNotSupported; }
 }  // namespace moe

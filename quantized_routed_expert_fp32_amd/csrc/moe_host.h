@@ -38,15 +38,23 @@ std::string fmt_name(const moe_qformat& f);
 
 uint64_t align256(uint64_t x);
 
-// Per-kind workspace layout of the decode path.
+// Route scratch at the start of every workspace: per-row arrival counters
+// (zero between calls), gate-row logits, then [rows, E] fp32 logits.
+struct RouteWs {
+  uint64_t cnt_off, gl_off, lg_off, total;
+};
+RouteWs route_ws_layout(const moe_layer_desc* d, int rows);
+uint64_t route_ws_bytes(const moe_layer_desc* d, int rows);
+
+// Workspace layout of the decode path (after the route scratch).
 struct DecodeWs {
-  uint64_t h_off, e_off, total;
+  uint64_t hhi_off, hlo_off, hc_off, total;
 };
 DecodeWs decode_ws_layout(const moe_layer_desc* d, int rows);
 
 // Per-kind workspace layout of the grouped path.
 struct GroupedWs {
-  uint64_t meta_off;   // int32 counts[E+1], offsets[E+2], tiles...
+  uint64_t meta_off;   // after the route scratch   // int32 counts[E+1], offsets[E+2], tiles...
   uint64_t perm_off;   // int32 [R*k + R]: expert-major position -> slot index (r*(k+1)+j)
   uint64_t xs_off;     // f16 [R, H]: x converted once
   uint64_t h_off;      // f16 [R*(k+1), Imax] in expert-major order

@@ -71,6 +71,22 @@ __device__ __forceinline__ float act_to_f(uint16_t b, int act_fp16) {
   return act_fp16 ? f16_bits_to_f(b) : bf16_to_f(b);
 }
 
+// comparator of the pick: NaN first, then larger value, then lower id.
+// Branch-free (bitwise on the predicates) so it compiles to selects.
+__device__ __forceinline__ bool pick_better(float a, int ia, float b, int ib) {
+  const bool an = a != a, bn = b != b;
+  const bool tie = (a == b) | (an & bn);
+  return (an & !bn) | ((!an & !bn) & (a > b)) | (tie & (ia < ib));
+}
+
+// (x & m) | c in one v_and_or_b32. gfx9 VOP3 takes no literal constant, so
+// the mask goes in an SGPR and the constant in a VGPR (hoisted once).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
+
 // ------------------------------------------------------------------ unpack
 // 16 packed fp16 pairs (1 + q/M) of one lane's chunk.
 template <int F> __device__ __forceinline__ void unpack_chunk(const uint32_t* w, uint32_t* o);
@@ -79,10 +95,10 @@ template <> __device__ __forceinline__ void unpack_chunk<F_Q4>(const uint32_t* w
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t v = w[i];
-    o[4 * i + 0] = ((v << 6) & 0x03C003C0u) | 0x3C003C00u;
-    o[4 * i + 1] = ((v << 2) & 0x03C003C0u) | 0x3C003C00u;
-    o[4 * i + 2] = ((v >> 2) & 0x03C003C0u) | 0x3C003C00u;
-    o[4 * i + 3] = ((v >> 6) & 0x03C003C0u) | 0x3C003C00u;
+    o[4 * i + 0] = and_or(v << 6, 0x03C003C0u, 0x3C003C00u);
+    o[4 * i + 1] = and_or(v << 2, 0x03C003C0u, 0x3C003C00u);
+    o[4 * i + 2] = and_or(v >> 2, 0x03C003C0u, 0x3C003C00u);
+    o[4 * i + 3] = and_or(v >> 6, 0x03C003C0u, 0x3C003C00u);
   }
 }
 template <> __device__ __forceinline__ void unpack_chunk<F_S4>(const uint32_t* w, uint32_t* o) {
@@ -92,8 +108,8 @@ template <> __device__ __forceinline__ void unpack_chunk<F_Q8>(const uint32_t* w
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t v = w[i];
-    o[2 * i + 0] = ((v << 2) & 0x03FC03FCu) | 0x3C003C00u;
-    o[2 * i + 1] = ((v >> 6) & 0x03FC03FCu) | 0x3C003C00u;
+    o[2 * i + 0] = and_or(v << 2, 0x03FC03FCu, 0x3C003C00u);
+    o[2 * i + 1] = and_or(v >> 6, 0x03FC03FCu, 0x3C003C00u);
   }
 }
 template <> __device__ __forceinline__ void unpack_chunk<F_Q3>(const uint32_t* w, uint32_t* o) {
@@ -101,14 +117,14 @@ template <> __device__ __forceinline__ void unpack_chunk<F_Q3>(const uint32_t* w
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const uint32_t v = w[i];
-    o[5 * i + 0] = ((v << 6) & 0x01C001C0u) | 0x3C003C00u;
-    o[5 * i + 1] = ((v << 3) & 0x01C001C0u) | 0x3C003C00u;
-    o[5 * i + 2] = (v & 0x01C001C0u) | 0x3C003C00u;
-    o[5 * i + 3] = ((v >> 3) & 0x01C001C0u) | 0x3C003C00u;
-    o[5 * i + 4] = ((v >> 6) & 0x01C001C0u) | 0x3C003C00u;
+    o[5 * i + 0] = and_or(v << 6, 0x01C001C0u, 0x3C003C00u);
+    o[5 * i + 1] = and_or(v << 3, 0x01C001C0u, 0x3C003C00u);
+    o[5 * i + 2] = and_or(v, 0x01C001C0u, 0x3C003C00u);
+    o[5 * i + 3] = and_or(v >> 3, 0x01C001C0u, 0x3C003C00u);
+    o[5 * i + 4] = and_or(v >> 6, 0x01C001C0u, 0x3C003C00u);
   }
-  o[15] = ((w[0] >> 9) & 0x00400040u) | ((w[1] >> 8) & 0x00800080u) |
-          ((w[2] >> 7) & 0x01000100u) | 0x3C003C00u;
+  o[15] = and_or(w[2] >> 7, 0x01000100u,
+                 and_or(w[1] >> 8, 0x00800080u, and_or(w[0] >> 9, 0x00400040u, 0x3C003C00u)));
 }
 
 // load one lane's chunk words (CB bytes) from a chunk block base
@@ -163,17 +179,235 @@ __device__ __forceinline__ float dot_chunk(const uint32_t* v, const half2v* a, f
   return acc;
 }
 
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf2v as_b2(uint32_t u) { return __builtin_bit_cast(bf2v, u); }
+
+// 16 packed bf16 pairs (1 + q/16) of one lane's chunk: the code sits in
+// mantissa bits 3..6 of a bf16 1.0 (0x3F80). For 8-bit codes the low and high
+// nibbles give two such sets (lo: o[0..15], hi: o[16..31]).
+template <int F> __device__ __forceinline__ void unpack_chunk_bf(const uint32_t* w, uint32_t* o);
+template <> __device__ __forceinline__ void unpack_chunk_bf<F_Q4>(const uint32_t* w, uint32_t* o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t v = w[i];
+    o[4 * i + 0] = and_or(v << 3, 0x00780078u, 0x3F803F80u);
+    o[4 * i + 1] = and_or(v >> 1, 0x00780078u, 0x3F803F80u);
+    o[4 * i + 2] = and_or(v >> 5, 0x00780078u, 0x3F803F80u);
+    o[4 * i + 3] = and_or(v >> 9, 0x00780078u, 0x3F803F80u);
+  }
+}
+template <> __device__ __forceinline__ void unpack_chunk_bf<F_S4>(const uint32_t* w, uint32_t* o) {
+  unpack_chunk_bf<F_Q4>(w, o);
+}
+template <> __device__ __forceinline__ void unpack_chunk_bf<F_Q3>(const uint32_t* w, uint32_t* o) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const uint32_t v = w[i];
+    o[5 * i + 0] = and_or(v << 3, 0x00380038u, 0x3F803F80u);
+    o[5 * i + 1] = and_or(v, 0x00380038u, 0x3F803F80u);
+    o[5 * i + 2] = and_or(v >> 3, 0x00380038u, 0x3F803F80u);
+    o[5 * i + 3] = and_or(v >> 6, 0x00380038u, 0x3F803F80u);
+    o[5 * i + 4] = and_or(v >> 9, 0x00380038u, 0x3F803F80u);
+  }
+  o[15] = and_or(w[2] >> 10, 0x00200020u,
+                 and_or(w[1] >> 11, 0x00100010u, and_or(w[0] >> 12, 0x00080008u, 0x3F803F80u)));
+}
+template <> __device__ __forceinline__ void unpack_chunk_bf<F_Q8>(const uint32_t* w, uint32_t* o) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t v = w[i];
+    o[2 * i + 0] = and_or(v << 3, 0x00780078u, 0x3F803F80u);        // low nibbles
+    o[2 * i + 1] = and_or(v >> 5, 0x00780078u, 0x3F803F80u);
+    o[16 + 2 * i + 0] = and_or(v >> 1, 0x00780078u, 0x3F803F80u);   // high nibbles
+    o[16 + 2 * i + 1] = and_or(v >> 9, 0x00780078u, 0x3F803F80u);
+  }
+}
+
+// acc += sum_p v_p . a_p over 16 bf16 pairs (fixed order)
+__device__ __forceinline__ float dot_chunk_bf(const uint32_t* v, const uint32_t* a, float acc) {
+#pragma unroll
+  for (int p = 0; p < 16; ++p) acc = __builtin_amdgcn_fdot2_f32_bf16(as_b2(v[p]), as_b2(a[p]), acc, false);
+  return acc;
+}
+// same with fp16 pairs held as uint32
+__device__ __forceinline__ float dot_chunk_h(const uint32_t* v, const uint32_t* a, float acc) {
+#pragma unroll
+  for (int p = 0; p < 16; ++p) acc = __builtin_amdgcn_fdot2(as_h2(v[p]), as_h2(a[p]), acc, false);
+  return acc;
+}
+
+// Activations and h do not change while a kernel reads them: reading them
+// through the constant address space lets uniform addresses become scalar
+// loads into SGPRs.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) u32x4* cu32x4_p;
+typedef const __attribute__((address_space(4))) float* cfloat_p;
+
+// 16 uint32 activation pairs of one chunk; every lane reads the same address
+__device__ __forceinline__ void load_pairs(const uint16_t* p, uint32_t* o) {
+  const cu32x4_p q = (cu32x4_p)(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = q[i];
+    o[4 * i] = v.x; o[4 * i + 1] = v.y; o[4 * i + 2] = v.z; o[4 * i + 3] = v.w;
+  }
+}
+
+// ------------------------------------------------------------- DPP moves
+// VALU-only lane moves (no LDS round trip). dpp_ctrl codes of the GCN/CDNA
+// DPP encoding: quad_perm(1,0,3,2) = 0xB1, quad_perm(2,3,0,1) = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+// Sum over each aligned group of 8 lanes; every lane of a group gets the
+// same bits (the pairings are symmetric and addition commutes).
+__device__ __forceinline__ float sum8(float s) {
+  s += dpp_f<0xB1>(s);
+  s += dpp_f<0x4E>(s);
+  s += dpp_f<0x141>(s);
+  return s;
+}
+// Sum over each row of 16 lanes, same bits in every lane of the row.
+__device__ __forceinline__ float sum16(float s) {
+  s = sum8(s);
+  s += dpp_f<0x140>(s);
+  return s;
+}
+
+// Sum of 4 consecutive activations per lane, then over aligned groups of 8
+// lanes: lane 8c then holds the sum of chunk c of a 256-wide slice (all 8
+// lanes of a group hold the same bits). Fixed order.
+template <int ACT16>
+__device__ __forceinline__ float slice_chunk_sums(const uint16_t* xs, int lane) {
+  const uint2 v = *reinterpret_cast<const uint2*>(xs + 4 * lane);
+  float s = act_to_f((uint16_t)(v.x & 0xFFFFu), ACT16);
+  s += act_to_f((uint16_t)(v.x >> 16), ACT16);
+  s += act_to_f((uint16_t)(v.y & 0xFFFFu), ACT16);
+  s += act_to_f((uint16_t)(v.y >> 16), ACT16);
+  return sum8(s);
+}
+
+// Wave-wide best (value, id) under pick_better; every lane gets the result.
+// Within 16-lane rows by DPP, then across the 4 rows through readlane.
+__device__ __forceinline__ void wave_best(float& v, int& id) {
+  {
+    const float ov = dpp_f<0xB1>(v); const int oi = dpp_i<0xB1>(id);
+    if (pick_better(ov, oi, v, id)) { v = ov; id = oi; }
+  }
+  {
+    const float ov = dpp_f<0x4E>(v); const int oi = dpp_i<0x4E>(id);
+    if (pick_better(ov, oi, v, id)) { v = ov; id = oi; }
+  }
+  {
+    const float ov = dpp_f<0x141>(v); const int oi = dpp_i<0x141>(id);
+    if (pick_better(ov, oi, v, id)) { v = ov; id = oi; }
+  }
+  {
+    const float ov = dpp_f<0x140>(v); const int oi = dpp_i<0x140>(id);
+    if (pick_better(ov, oi, v, id)) { v = ov; id = oi; }
+  }
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(id, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    const int oi = __builtin_amdgcn_readlane(id, 16 * r);
+    if (pick_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  v = bv;
+  id = bi;
+}
+
+// One wave, one 256-wide K slice: for up to NR activation rows, the dot of
+// each lane's weight row with the row's slice. w: the lane's 8 chunks of
+// codes; sblk: the slice's scale block; xs[i]: global slice base of row i;
+// lx: this wave's LDS staging area (NR x 512 bytes). Each lane loads 4
+// activations of a row (coalesced), writes them to LDS and sums them; the
+// dot then reads each chunk's 16 pairs back as a broadcast. Only this wave
+// touches lx, and LDS serves one wave's operations in order, so no barrier.
+// Per group: (M s) * sum(v a) + (b - M s) * X (8-bit: two nibble sets).
+template <int F, int NR, int ACT16>
+__device__ __forceinline__ void slice_dot(const uint32_t (&w)[8][Fmt<F>::WORDS], const uint8_t* sblk,
+                                          int lane, const uint16_t* const* xs, int nr, uint32_t* lx,
+                                          float* out) {
+  constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
+  float csum[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    out[i] = 0.f;
+    csum[i] = 0.f;
+    if (i < nr) {
+      const uint2 v = *reinterpret_cast<const uint2*>(xs[i] + 4 * lane);
+      reinterpret_cast<uint2*>(lx + i * 128)[lane] = v;
+      float sm = act_to_f((uint16_t)(v.x & 0xFFFFu), ACT16);
+      sm += act_to_f((uint16_t)(v.x >> 16), ACT16);
+      sm += act_to_f((uint16_t)(v.y & 0xFFFFu), ACT16);
+      sm += act_to_f((uint16_t)(v.y >> 16), ACT16);
+      csum[i] = sum8(sm);
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < GPS; ++gi) {
+    float ms, bm;
+    group_coef<F>(sblk, lane, gi, ms, bm);
+    float acc[NR], acc2[NR], X[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) acc[i] = acc2[i] = X[i] = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < CPG; ++cc) {
+      const int c = gi * CPG + cc;
+      uint32_t v[F == F_Q8 ? 32 : 16];
+      if constexpr (ACT16) unpack_chunk<F>(w[c], v); else unpack_chunk_bf<F>(w[c], v);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (i < nr) {
+          uint32_t a[16];
+          const uint4* q = reinterpret_cast<const uint4*>(lx + i * 128 + 16 * c);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint4 t = q[u];
+            a[4 * u] = t.x; a[4 * u + 1] = t.y; a[4 * u + 2] = t.z; a[4 * u + 3] = t.w;
+          }
+          if constexpr (ACT16) {
+            acc[i] = dot_chunk_h(v, a, acc[i]);
+          } else {
+            acc[i] = dot_chunk_bf(v, a, acc[i]);
+            if constexpr (F == F_Q8) acc2[i] = dot_chunk_bf(v + 16, a, acc2[i]);
+          }
+          X[i] += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(csum[i]), 8 * c));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (i < nr) {
+        if constexpr (F == F_Q8) {
+          if constexpr (!ACT16) {
+            // q = lo + 16 hi: s*sum(q a) + b*X = 16s*A_lo + 256s*A_hi + (b - 272 s)*X
+            const float s = ms * (1.0f / 256.0f), b = bm + ms;
+            out[i] = fmaf(16.0f * s, acc[i], out[i]);
+            out[i] = fmaf(256.0f * s, acc2[i], out[i]);
+            out[i] = fmaf(b - 272.0f * s, X[i], out[i]);
+            continue;
+          }
+        }
+        out[i] = fmaf(ms, acc[i], out[i]);
+        out[i] = fmaf(bm, X[i], out[i]);
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
   // silu(g) * u with silu(z) = z / (1 + exp(-z))
   return (g / (1.0f + expf(-g))) * u;
 }
 
-// comparator of the pick: NaN first, then larger value, then lower id
-__device__ __forceinline__ bool pick_better(float a, int ia, float b, int ib) {
-  const bool an = a != a, bn = b != b;
-  if (an != bn) return an;
-  if (!an && a != b) return a > b;
-  return ia < ib;
-}
 
 }  // namespace moe

@@ -9,12 +9,15 @@ struct RouteArgs {
   const uint8_t* base;
   uint64_t r_off, r_soff, g_off, g_soff;
   const uint16_t* x;
-  int act_fp16, H, E, k;
+  int act_fp16, H, E, k, R;
   const float* bias;
   int32_t* ids;
   float* p;
   float* sg;
-  float* logits;
+  float* logits;   // tap [R, E+1] or null
+  float* lg_ws;    // [R, E] scratch: logits before the bias
+  float* gl_ws;    // [R] scratch: gate-row logits
+  unsigned* cnt;   // [R] per-row arrival counters; zero between calls
 };
 
 // Offsets of one expert class (routed or shared) inside the packed layer.
@@ -32,8 +35,9 @@ struct DecodeArgs {
   const int32_t* ids;
   const float* p;
   const float* sg;
-  float* h_ws;    // [R, k+1, Imax]
-  float* e_ws;    // [R, k+1, H]
+  uint16_t* hhi;  // [R, k+1, Imax] fp16 high part of h
+  uint16_t* hlo;  // [R, k+1, Imax] fp16 low part of h (h - hi)
+  float* hc;      // [R, k+1, Imax/32] chunk sums of hi + lo
   float* y;       // [R, H]
   float* tap_gu;  // [R, k+1, 2, Imax] or null
   float* tap_h;   // [R, k+1, Imax] or null
@@ -61,8 +65,13 @@ struct GroupedArgs {
   float* tap_e;
 };
 
-hipError_t launch_route(int fr, int fg, const RouteArgs& a, int rows, hipStream_t s);
-hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s);
-hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s);
+// ev: NULL or 8 events; ev[2i] / ev[2i+1] (each may be NULL) bracket kernel i
+hipError_t launch_route(int fr, int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev);
+
+inline void mark(hipEvent_t* ev, int i, hipStream_t s) {
+  if (ev && ev[i]) hipEventRecord(ev[i], s);
+}
 
 }  // namespace moe

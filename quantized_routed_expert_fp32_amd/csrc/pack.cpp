@@ -340,13 +340,27 @@ int pack_layer_host(const moe_layer_desc* d, const moe_layer_src* src, void* hos
   return MOE_OK;
 }
 
+RouteWs route_ws_layout(const moe_layer_desc* d, int rows) {
+  RouteWs w;
+  uint64_t o = 0;
+  w.cnt_off = o; o = align256(o + (uint64_t)rows * 4);
+  w.gl_off = o; o = align256(o + (uint64_t)rows * 4);
+  w.lg_off = o; o = align256(o + (uint64_t)rows * d->n_experts * 4);
+  w.total = o;
+  return w;
+}
+
+uint64_t route_ws_bytes(const moe_layer_desc* d, int rows) { return route_ws_layout(d, rows).total; }
+
 DecodeWs decode_ws_layout(const moe_layer_desc* d, int rows) {
   const uint64_t Imax = std::max(d->inter, d->shared_inter);
   const uint64_t slots = (uint64_t)rows * (d->top_k + 1);
   DecodeWs w;
-  w.h_off = 0;
-  w.e_off = align256(slots * Imax * 4);
-  w.total = align256(w.e_off + slots * (uint64_t)d->hidden * 4);
+  uint64_t o = route_ws_bytes(d, rows);
+  w.hhi_off = o; o = align256(o + slots * Imax * 2);
+  w.hlo_off = o; o = align256(o + slots * Imax * 2);
+  w.hc_off = o; o = align256(o + slots * (Imax / 32) * 4);
+  w.total = o;
   return w;
 }
 
@@ -355,7 +369,7 @@ GroupedWs grouped_ws_layout(const moe_layer_desc* d, int rows) {
   const uint64_t Imax = std::max(d->inter, d->shared_inter);
   const uint64_t slots = (uint64_t)rows * (k + 1);
   GroupedWs w;
-  uint64_t o = 0;
+  uint64_t o = route_ws_bytes(d, rows);
   w.meta_off = o; o = align256(o + (3 * (E + 2) + 64) * 4);
   w.perm_off = o; o = align256(o + slots * 4);
   w.xs_off = o; o = align256(o + (uint64_t)rows * H * 2);
