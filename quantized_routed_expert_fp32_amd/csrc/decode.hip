@@ -14,11 +14,11 @@
 // hi + lo parts (22 significant bits) plus per-32 chunk sums, for down.
 //
 // down + combine (k_dec_down): one workgroup per (row, 64-column tile of y),
-// one wave per slot (k routed + shared). Each wave computes its slot's
-// output columns over the full intermediate axis; wave 0 then forms
-// y = sum_j p_j e_j + sigma e_shared in slot order. Blocks are mapped so
-// the rows of one tile run on one XCD and share the shared expert's tile
-// in that XCD's L2.
+// k waves. Wave j computes routed slot j's output columns over the full
+// intermediate axis plus 1/k of the shared expert's (added in wave order);
+// wave 0 then forms y = sum_j p_j e_j + sigma e_shared in slot order. Blocks
+// are mapped so the rows of one tile run on one XCD and share the shared
+// expert's tile in that XCD's L2.
 //
 // Every row's arithmetic is fixed (K slices owned by fixed waves, chunks
 // and groups in K order, slices reduced in slice order, slots combined in
@@ -129,59 +129,60 @@ __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a, const uint16_t
   }
 }
 
-// one slot's 64 output columns of tile t over the full intermediate axis
-template <int F>
-__device__ __forceinline__ float dn_slot(const DecodeArgs& a, const uint32_t* __restrict__ hh,
-                                         const uint32_t* __restrict__ hl, const float* __restrict__ hc,
-                                         const uint8_t* codes, const uint8_t* scales,
-                                         int I, int t, int lane) {
-  constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
-  const int nch = I / 32, nkb = I / KBLK;
+// Part of one slot's 64 output columns of tile t over chunks c0 .. c0+n-1 of
+// the intermediate axis (chunk c covers 32 intermediate indices): load the
+// codes (dn_load), then the dot in chunk order (dn_dot). n <= MAXC.
+template <int F, int MAXC>
+__device__ __forceinline__ void dn_load(const uint8_t* codes, int I, int t, int lane, int c0, int n,
+                                        uint32_t (&w)[MAXC][Fmt<F>::WORDS]) {
+  const int nch = I / 32;
+#pragma unroll
+  for (int q = 0; q < MAXC; ++q)
+    if (q < n) load_chunk<F>(codes + chunk_off<F>(t, c0 + q, nch), lane, w[q]);
+}
+template <int F, int MAXC>
+__device__ __forceinline__ float dn_dot(const uint32_t (&w)[MAXC][Fmt<F>::WORDS],
+                                        const uint32_t* __restrict__ hh, const uint32_t* __restrict__ hl,
+                                        const float* __restrict__ hc, const uint8_t* scales, int I,
+                                        int t, int lane, int c0, int n) {
+  constexpr int CPG = Fmt<F>::G / 32;
+  const int nkb = I / KBLK;
   float out = 0.f;
-  for (int s0 = 0; s0 < nkb; s0 += 2) {
-    const int ns = min(2, nkb - s0);
-    uint32_t w[2][8][Fmt<F>::WORDS];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (q < ns)
+  for (int q0 = 0; q0 < MAXC; q0 += CPG) {
+    if (q0 < n) {
+      // one group: CPG chunks from chunk c0 + q0 (c0 is a multiple of CPG)
+      const int c = c0 + q0, sl = c / 8, gi = (c % 8) / CPG;
+      float ms, bm;
+      group_coef<F>(scales + sblk_off<F>(t, sl, nkb), lane, gi, ms, bm);
+      float acc = 0.f, X = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc)
-          load_chunk<F>(codes + chunk_off<F>(t, (s0 + q) * 8 + cc, nch), lane, w[q][cc]);
+      for (int cc = 0; cc < CPG; ++cc) {
+        uint32_t v[16], ph[16], pl[16];
+        unpack_chunk<F>(w[q0 + cc], v);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (q < ns) {
-        const int sl = s0 + q;
-        const uint8_t* sblk = scales + sblk_off<F>(t, sl, nkb);
-#pragma unroll
-        for (int gi = 0; gi < GPS; ++gi) {
-          float ms, bm;
-          group_coef<F>(sblk, lane, gi, ms, bm);
-          float acc = 0.f, X = 0.f;
-#pragma unroll
-          for (int cc = 0; cc < CPG; ++cc) {
-            const int c = sl * 8 + gi * CPG + cc;
-            uint32_t v[16], ph[16], pl[16];
-            unpack_chunk<F>(w[q][gi * CPG + cc], v);
-#pragma unroll
-            for (int p = 0; p < 16; ++p) { ph[p] = hh[16 * c + p]; pl[p] = hl[16 * c + p]; }
-            acc = dot_chunk_h(v, ph, acc);
-            acc = dot_chunk_h(v, pl, acc);
-            X += hc[c];
-          }
-          out = fmaf(ms, acc, out);
-          out = fmaf(bm, X, out);
-        }
+        for (int p = 0; p < 16; ++p) { ph[p] = hh[16 * (c + cc) + p]; pl[p] = hl[16 * (c + cc) + p]; }
+        acc = dot_chunk_h(v, ph, acc);
+        acc = dot_chunk_h(v, pl, acc);
+        X += hc[c + cc];
       }
+      out = fmaf(ms, acc, out);
+      out = fmaf(bm, X, out);
     }
   }
   return out;
 }
 
+// down + combine: one workgroup per (row, 64-column tile of y) with k waves.
+// Wave j computes routed slot j over the full intermediate axis and 1/k of
+// the shared expert's chunks; the k shared parts are added in wave order.
+// Wave 0 then forms y = sum_j p_j e_j + sigma e_shared in slot order.
 template <int FR, int FS>
-__global__ __launch_bounds__(576) void k_dec_down(DecodeArgs a, const uint16_t* __restrict__ hhi,
+__global__ __launch_bounds__(512) void k_dec_down(DecodeArgs a, const uint16_t* __restrict__ hhi,
                                                   const uint16_t* __restrict__ hlo,
                                                   const float* __restrict__ hcs) {
-  __shared__ float es[9][64];
+  __shared__ float es[8][64];
+  __shared__ float ps[8][64];
   const int T = a.H / 64, R = a.R, k = a.k;
   const int wg = blockIdx.x;
   int t, r;
@@ -195,28 +196,55 @@ __global__ __launch_bounds__(576) void k_dec_down(DecodeArgs a, const uint16_t* 
   }
   const int tid = threadIdx.x, lane = tid & 63;
   const int j = __builtin_amdgcn_readfirstlane(tid >> 6);   // slot of this wave, uniform
-  const uint64_t rs = (uint64_t)r * (k + 1) + j;
-  const uint32_t* hh = reinterpret_cast<const uint32_t*>(hhi + rs * a.Imax);
-  const uint32_t* hl = reinterpret_cast<const uint32_t*>(hlo + rs * a.Imax);
-  const float* hc = hcs + rs * (a.Imax / 32);
-  float e_out = 0.f;
-  if (j < k) {
-    const int e = a.ids[r * k + j];
-    if (e >= 0 && e < a.E) {
-      const uint8_t* blk = a.base + a.rt.base_off + (uint64_t)e * a.rt.stride;
-      e_out = dn_slot<FR>(a, hh, hl, hc, blk + a.rt.dn_codes, blk + a.rt.dn_scales, a.rt.inter, t, lane);
+  // routed slot j: all its chunks (blocks of 16 when inter > 512); the
+  // wave's share of the shared expert (whole groups, split over k waves) is
+  // loaded together with the first block
+  const uint64_t rsj = (uint64_t)r * (k + 1) + j, rsk = (uint64_t)r * (k + 1) + k;
+  const int e = a.ids[r * k + j];
+  const bool valid = e >= 0 && e < a.E;
+  const uint8_t* rblk = a.base + a.rt.base_off + (uint64_t)(valid ? e : 0) * a.rt.stride;
+  const uint8_t* sblk = a.base + a.sh.base_off;
+  const int gch = Fmt<FS>::G / 32, ngr = (a.sh.inter / 32) / gch, per = (ngr + k - 1) / k;
+  const int g0 = min(ngr, j * per), g1 = min(ngr, g0 + per);
+  const int sc0 = g0 * gch, sn = min(8, (g1 - g0) * gch);
+  const int rn = a.rt.inter / 32;
+  uint32_t wr[16][Fmt<FR>::WORDS], wsh[8][Fmt<FS>::WORDS];
+  dn_load<FR, 16>(rblk + a.rt.dn_codes, a.rt.inter, t, lane, 0, min(16, rn), wr);
+  dn_load<FS, 8>(sblk + a.sh.dn_codes, a.sh.inter, t, lane, sc0, sn, wsh);
+  const uint32_t* hhj = reinterpret_cast<const uint32_t*>(hhi + rsj * a.Imax);
+  const uint32_t* hlj = reinterpret_cast<const uint32_t*>(hlo + rsj * a.Imax);
+  float e_out = dn_dot<FR, 16>(wr, hhj, hlj, hcs + rsj * (a.Imax / 32), rblk + a.rt.dn_scales,
+                               a.rt.inter, t, lane, 0, min(16, rn));
+  for (int cb = 16; cb < rn; cb += 16) {
+    dn_load<FR, 16>(rblk + a.rt.dn_codes, a.rt.inter, t, lane, cb, min(16, rn - cb), wr);
+    e_out += dn_dot<FR, 16>(wr, hhj, hlj, hcs + rsj * (a.Imax / 32), rblk + a.rt.dn_scales,
+                            a.rt.inter, t, lane, cb, min(16, rn - cb));
+  }
+  if (!valid) e_out = 0.f;
+  float s_out = 0.f;
+  if (sn > 0) {
+    const uint32_t* hhk = reinterpret_cast<const uint32_t*>(hhi + rsk * a.Imax);
+    const uint32_t* hlk = reinterpret_cast<const uint32_t*>(hlo + rsk * a.Imax);
+    s_out = dn_dot<FS, 8>(wsh, hhk, hlk, hcs + rsk * (a.Imax / 32), sblk + a.sh.dn_scales, a.sh.inter,
+                          t, lane, sc0, sn);
+    for (int cb = sc0 + sn; cb < g1 * gch; cb += 8) {
+      const int m = min(8, g1 * gch - cb);
+      dn_load<FS, 8>(sblk + a.sh.dn_codes, a.sh.inter, t, lane, cb, m, wsh);
+      s_out += dn_dot<FS, 8>(wsh, hhk, hlk, hcs + rsk * (a.Imax / 32), sblk + a.sh.dn_scales,
+                             a.sh.inter, t, lane, cb, m);
     }
-  } else {
-    const uint8_t* blk = a.base + a.sh.base_off;
-    e_out = dn_slot<FS>(a, hh, hl, hc, blk + a.sh.dn_codes, blk + a.sh.dn_scales, a.sh.inter, t, lane);
   }
   es[j][lane] = e_out;
-  if (a.tap_e) a.tap_e[rs * a.H + 64 * t + lane] = e_out;
+  ps[j][lane] = s_out;
+  if (a.tap_e) a.tap_e[((uint64_t)r * (k + 1) + j) * a.H + 64 * t + lane] = e_out;
   __syncthreads();
   if (j == 0) {
+    float sh = 0.f;
+    for (int q = 0; q < k; ++q) sh += ps[q][lane];
+    if (a.tap_e) a.tap_e[((uint64_t)r * (k + 1) + k) * a.H + 64 * t + lane] = sh;
     float y = 0.f;
     for (int q = 0; q < k; ++q) y = fmaf(a.p[r * k + q], es[q][lane], y);
-    y = fmaf(a.sg[r], es[k][lane], y);
+    y = fmaf(a.sg[r], sh, y);
     a.y[(uint64_t)r * a.H + 64 * t + lane] = y;
   }
 }
@@ -237,7 +265,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   mark(ev, 2, s);
-  hipLaunchKernelGGL((k_dec_down<FR, FS>), dim3((a.H / 64) * a.R), dim3(64 * (a.k + 1)), 0, s, a,
+  hipLaunchKernelGGL((k_dec_down<FR, FS>), dim3((a.H / 64) * a.R), dim3(64 * a.k), 0, s, a,
                      a.hhi, a.hlo, a.hc);
   mark(ev, 3, s);
   return hipGetLastError();

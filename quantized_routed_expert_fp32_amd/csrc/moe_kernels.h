@@ -293,6 +293,38 @@ __device__ __forceinline__ float slice_chunk_sums(const uint16_t* xs, int lane) 
   return sum8(s);
 }
 
+// Order-preserving key of a logit for the pick: NaN above +inf above every
+// finite value, -0.0 equal to +0.0; larger key = better.
+__device__ __forceinline__ uint32_t pick_key(float v) {
+  const float z = v + 0.0f;
+  const uint32_t b = __float_as_uint(z);
+  if (z != z) return 0xFFFFFFFFu;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+// wave-wide max / min of a uint32: 16-lane rows by DPP, then the 4 rows
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<0xB1>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x4E>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x141>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x140>((int)v));
+  uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  m = max(m, (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  m = max(m, (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+  m = max(m, (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return m;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)dpp_i<0xB1>((int)v));
+  v = min(v, (uint32_t)dpp_i<0x4E>((int)v));
+  v = min(v, (uint32_t)dpp_i<0x141>((int)v));
+  v = min(v, (uint32_t)dpp_i<0x140>((int)v));
+  uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  m = min(m, (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  m = min(m, (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+  m = min(m, (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return m;
+}
+
 // Wave-wide best (value, id) under pick_better; every lane gets the result.
 // Within 16-lane rows by DPP, then across the 4 rows through readlane.
 __device__ __forceinline__ void wave_best(float& v, int& id) {

@@ -155,12 +155,13 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
     bias[i] = a.bias ? a.bias[e] : 0.f;
   }
   const float c = __hip_atomic_load(&a.gl_ws[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  bool taken[4];
+  // candidates of this lane: experts lane + 64 i; key 0 marks taken/absent
+  uint32_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     v[i] = a.bias ? lv[i] + bias[i] : lv[i];
-    taken[i] = e >= E;
+    key[i] = e < E ? pick_key(v[i]) : 0u;
   }
   if (a.logits) {
 #pragma unroll
@@ -168,23 +169,26 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
       if (lane + 64 * i < E) a.logits[(uint64_t)row * (E + 1) + lane + 64 * i] = v[i];
     if (lane == 0) a.logits[(uint64_t)row * (E + 1) + E] = c;
   }
-  // k rounds (fully unrolled, k <= 8): lane j keeps the j-th pick
+  // k rounds (fully unrolled, k <= 8): the wave-wide largest key, ties to the
+  // lowest id; lane j keeps the j-th pick
   float my_v = 0.f, top = 0.f;
   int my_i = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j < k) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+      const uint32_t bk = max(max(key[0], key[1]), max(key[2], key[3]));
+      const uint32_t m = wave_max_u32(bk);
+      // lowest id holding the best key (ids lane + 64 i grow with i)
+      uint32_t cid = 0xFFFFFFFFu;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool b = !taken[i] & pick_better(v[i], lane + 64 * i, bv, bi);
-        bv = b ? v[i] : bv;
-        bi = b ? lane + 64 * i : bi;
-      }
-      wave_best(bv, bi);
+      for (int i = 3; i >= 0; --i) cid = key[i] == m ? (uint32_t)(lane + 64 * i) : cid;
+      const int bi = (int)wave_min_u32(cid);
+      float bv = v[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) taken[i] = taken[i] | (bi == lane + 64 * i);
+      for (int i = 1; i < 4; ++i) bv = (bi == lane + 64 * i) ? v[i] : bv;
+      bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), bi & 63));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[i] = (bi == lane + 64 * i) ? 0u : key[i];
       if (j == 0) top = bv;
       my_v = lane == j ? bv : my_v;
       my_i = lane == j ? bi : my_i;
