@@ -262,11 +262,11 @@ int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const i
   uint8_t* w = static_cast<uint8_t*>(ws);
   a.meta = reinterpret_cast<int32_t*>(w + wl.meta_off);
   a.perm = reinterpret_cast<int32_t*>(w + wl.perm_off);
-  a.xs = reinterpret_cast<uint16_t*>(w + wl.xs_off);
   a.hbuf = reinterpret_cast<uint16_t*>(w + wl.h_off);
   a.e_ws = reinterpret_cast<float*>(w + wl.e_off);
   a.tiles = reinterpret_cast<int32_t*>(w + wl.tiles_off);
   a.max_tiles = wl.max_tiles;
+  a.gemm_nblk = 1;
   a.y = y;
   a.tap_gu = taps ? taps->gu : nullptr;
   a.tap_h = taps ? taps->h : nullptr;

@@ -1,7 +1,437 @@
-// Grouped (prompt-chunk) path: placeholder until the MFMA kernels land.
+// Grouped (prompt-chunk) path: the prefill form for chunks of many rows.
+//
+//  1. k_grp_sort (one workgroup): expert histogram of the picks, exclusive
+//     prefix scan, stable scatter of the slots (row r, pick j) into
+//     expert-major order; the shared expert follows as expert E with every
+//     row. Then the tile lists: experts with many rows get 128-row M-tiles,
+//     the rest 32-row M-tiles (the Zipf-skewed chunk has one hot expert
+//     with most rows and a long tail of small ones).
+//  2. k_grp_gemm<GU>: per (M-tile, 256-column block) a workgroup of 4 waves;
+//     wave w owns one 64-row layout tile of the gate/up matrix (32 gate rows
+//     + the 32 up rows of the same intermediate indices), so gate and up of
+//     an output land in the same lane and SwiGLU runs in registers. A (the
+//     activations of the tile's slots, gathered by the sort's permutation)
+//     is staged through LDS as fp16; B (the packed codes) goes from memory
+//     straight to registers and is dequantised there to fp16
+//     (affine: s*q + b; symmetric: s*(u - 8)); v_mfma_f32_32x32x16_f16
+//     accumulates in fp32. Output h in fp16, expert-major.
+//  3. k_grp_gemm<DN>: the same on h and the down matrices; output e in fp32
+//     in slot order.
+//  4. k_grp_combine: y = sum_j p_j e_j + sigma e_shared, slots in pick order.
+// ("Sage-A1.5 ... #1329", Proposal: grouped MoE and XMX prompt chunks;
+//  Limits to agree on: the grouped form has a different sum order than the
+//  per-row form, so it is judged by tolerance, not bits.)
 #include "moe_kernels.h"
 #include "moe_launch.h"
 
 namespace moe {
-hipError_t launch_grouped(int, int, const GroupedArgs&, hipStream_t, hipEvent_t*) { return hipErrorNotSupported; }
+
+typedef f16 half8v_t __attribute__((ext_vector_type(8)));
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+
+constexpr int BIG_MIN_ROWS = 96;   // experts with at least this many rows take 128-row tiles
+
+// meta layout (int32): [0] n_big, [1] n_small, [2 .. E+3) offsets (E+2 entries)
+constexpr int META_OFF = 8;
+
+// ------------------------------------------------------------------ sort
+__global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
+  __shared__ int cnt[260];
+  __shared__ int run[260];
+  __shared__ int off[260];
+  __shared__ int wc[16][258];
+  __shared__ int s_nt[2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E = a.E, k = a.k, R = a.R, nslot = R * k;
+  for (int e = tid; e < 260; e += 1024) { cnt[e] = 0; run[e] = 0; }
+  __syncthreads();
+  for (int i = tid; i < nslot; i += 1024) {
+    const int e = a.ids[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    cnt[E] = R;
+    int s = 0;
+    for (int e = 0; e <= E; ++e) { off[e] = s; s += cnt[e]; }
+    off[E + 1] = s;
+    for (int e = 0; e <= E + 1; ++e) a.meta[META_OFF + e] = off[e];
+  }
+  __syncthreads();
+  // stable scatter, 1024 slots at a time
+  for (int base = 0; base < nslot; base += 1024) {
+    for (int q = tid; q < 16 * 258; q += 1024) (&wc[0][0])[q] = 0;
+    __syncthreads();
+    const int i = base + tid;
+    const int e = i < nslot ? a.ids[i] : -1;
+    const bool ok = e >= 0 && e < E;
+    // lanes of this wave holding the same expert
+    unsigned long long m = __ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const unsigned long long bal = __ballot(ok && ((e >> b) & 1));
+      m &= ((e >> b) & 1) ? bal : ~bal;
+    }
+    const int rank = __popcll(m & ((1ull << lane) - 1ull));
+    if (ok && rank == 0) wc[w][e] = __popcll(m);
+    __syncthreads();
+    if (ok) {
+      int before = run[e];
+      for (int q = 0; q < w; ++q) before += wc[q][e];
+      const int pos = off[e] + before + rank;
+      const int r = i / k, j = i % k;
+      a.perm[pos] = r * (k + 1) + j;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += 1024) {
+      int s = 0;
+      for (int q = 0; q < 16; ++q) s += wc[q][ee];
+      run[ee] += s;
+    }
+    __syncthreads();
+  }
+  for (int r = tid; r < R; r += 1024) a.perm[off[E] + r] = r * (k + 1) + k;
+  // tile lists: entry = (expert, first position, rows)
+  if (tid == 0) {
+    int nb = 0, ns = 0;
+    for (int e = 0; e <= E; ++e) {
+      const int c = cnt[e];
+      if (c == 0) continue;
+      const bool big = c >= BIG_MIN_ROWS;
+      const int bm = big ? 128 : 32;
+      for (int m0 = 0; m0 < c; m0 += bm) {
+        const int rows = min(bm, c - m0);
+        int* t = big ? a.tiles + 3 * nb++ : a.tiles + 3 * (a.max_tiles + ns++);
+        t[0] = e;
+        t[1] = off[e] + m0;
+        t[2] = rows;
+      }
+    }
+    a.meta[0] = nb;
+    a.meta[1] = ns;
+  }
+}
+
+// ------------------------------------------------------------------ GEMM
+// fp16 pair dequantisation of one code word (8 codes of one weight row):
+// 4 packed fp16 pairs w = s*q + b (affine) or s*(u - 8) (symmetric), for
+// the pair layout of the packed codes (pairs of consecutive k).
+template <int F>
+__device__ __forceinline__ void deq_word(const uint32_t* wv, half2v s2, half2v b2, uint32_t* o);
+
+template <>
+__device__ __forceinline__ void deq_word<F_Q4>(const uint32_t* wv, half2v s16, half2v b2, uint32_t* o) {
+  // 1 + q/16 -> q/16 (exact) -> fma with (16 s, b): one rounding
+  const uint32_t v = wv[0];
+  const uint32_t p[4] = {and_or(v << 6, 0x03C003C0u, 0x3C003C00u), and_or(v << 2, 0x03C003C0u, 0x3C003C00u),
+                         and_or(v >> 2, 0x03C003C0u, 0x3C003C00u), and_or(v >> 6, 0x03C003C0u, 0x3C003C00u)};
+  const half2v one = {(f16)1.0f, (f16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2v q16 = as_h2(p[i]) - one;
+    o[i] = as_u(__builtin_elementwise_fma(q16, s16, b2));
+  }
+}
+template <>
+__device__ __forceinline__ void deq_word<F_S4>(const uint32_t* wv, half2v s16, half2v b2, uint32_t* o) {
+  // 1 + u/16 - 1.5 = (u - 8)/16 exactly, times 16 s: one rounding
+  const uint32_t v = wv[0];
+  const uint32_t p[4] = {and_or(v << 6, 0x03C003C0u, 0x3C003C00u), and_or(v << 2, 0x03C003C0u, 0x3C003C00u),
+                         and_or(v >> 2, 0x03C003C0u, 0x3C003C00u), and_or(v >> 6, 0x03C003C0u, 0x3C003C00u)};
+  const half2v off = {(f16)1.5f, (f16)1.5f};
+  (void)b2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = as_u((as_h2(p[i]) - off) * s16);
+}
+
+// For the 3-bit layout, the 8 codes k = 8v..8v+7 of a chunk (v = 0..3) sit
+// in pairs 4v..4v+3; the chunk's full unpack gives them.
+template <int F>
+__device__ __forceinline__ void deq_chunk_half(const uint32_t* cw, int wsel, half2v s16, half2v b2,
+                                               uint32_t* o) {
+  if constexpr (F == F_Q3) {
+    uint32_t v[16];
+    unpack_chunk<F_Q3>(cw, v);   // 1 + q/16 pairs
+    const half2v one = {(f16)1.0f, (f16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t pv = v[0];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pv = (wsel == q) ? v[4 * q + i] : pv;
+      o[i] = as_u(__builtin_elementwise_fma(as_h2(pv) - one, s16, b2));
+    }
+  } else {
+    uint32_t wv[1];
+    wv[0] = cw[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) wv[0] = (wsel == q) ? cw[q] : wv[0];
+    deq_word<F>(wv, s16, b2, o);
+  }
+}
+
+enum { GU = 0, DN = 1 };
+
+// One workgroup: (tile, column block of 4 layout tiles); wave w = layout tile.
+// BM = 32 * MT rows. K walked in steps of 64 (two code chunks).
+template <int F, int MODE, int MT, int ACT16>
+__device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* __restrict__ x,
+                                         int e, int m0, int mc, int nb, uint16_t* lds_a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k = a.k, H = a.H;
+  const bool shared = e == a.E;
+  const ExpertClass& ec = shared ? a.sh : a.rt;
+  const int I = ec.inter;
+  const int K = MODE == GU ? H : I;          // contraction length
+  const int T = nb * 4 + w;                  // this wave's layout tile
+  const uint8_t* blk = a.base + ec.base_off + (shared ? 0 : (uint64_t)e * ec.stride);
+  const uint8_t* codes = blk + (MODE == GU ? ec.gu_codes : ec.dn_codes);
+  const uint8_t* scales = blk + (MODE == GU ? ec.gu_scales : ec.dn_scales);
+  const int nch = K / 32, nkb = K / KBLK;
+  constexpr int BM = 32 * MT;
+  constexpr int AST = 72;                    // LDS row stride in halves (64 + 8 pad)
+  // ---- A rows this thread stages: BM rows x 64 halves per K-step; thread t
+  // handles row t / (256 / BM) ... as (row, 8-half segment) pairs
+  constexpr int SEGS = BM * 8;               // 8 halves per segment
+  constexpr int SPT = SEGS / 256;            // segments per thread
+  const uint16_t* arow[SPT];
+  int aseg[SPT], arr[SPT];
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int sidx = tid + 256 * q;
+    const int rr = sidx / 8, sg = sidx % 8;
+    const int rowc = min(rr, mc - 1);
+    const int slot = a.perm[m0 + rowc];
+    const uint16_t* src;
+    if constexpr (MODE == GU) src = x + (uint64_t)(slot / (k + 1)) * H;
+    else src = a.hbuf + (uint64_t)(m0 + rowc) * a.Imax;
+    arow[q] = src;
+    aseg[q] = sg;
+    arr[q] = rr;
+  }
+  f16v_t acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.f;
+  const int col = lane & 31, hsel = lane >> 5;
+  constexpr int GPS = KBLK / Fmt<F>::G;
+  // software pipeline: the loads of step k0 + 64 are issued before the
+  // MFMAs of step k0
+  uint4 av[SPT];
+  uint32_t cw[2][2][Fmt<F>::WORDS];
+  uint32_t sraw[2];
+  auto issue = [&](int kk0) {
+#pragma unroll
+    for (int q = 0; q < SPT; ++q) av[q] = *reinterpret_cast<const uint4*>(arow[q] + kk0 + 8 * aseg[q]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        load_chunk<F>(codes + chunk_off<F>(T, kk0 / 32 + c, nch), 32 * nt + col, cw[nt][c]);
+    const int gi = (kk0 % KBLK) / Fmt<F>::G;
+    const uint8_t* sblk = scales + sblk_off<F>(T, kk0 / KBLK, nkb);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if constexpr (Fmt<F>::AFF) sraw[nt] = reinterpret_cast<const uint32_t*>(sblk)[(32 * nt + col) * GPS + gi];
+      else sraw[nt] = reinterpret_cast<const uint16_t*>(sblk)[(32 * nt + col) * GPS + gi];
+    }
+  };
+  issue(0);
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    __syncthreads();     // the previous step's A reads are done
+#pragma unroll
+    for (int q = 0; q < SPT; ++q) {
+      uint4 v = av[q];
+      if constexpr (MODE == GU && !ACT16) {
+        // bf16 -> fp16 (exact for |x| in the fp16 normal range)
+        uint32_t* u = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          half2v h;
+          h.x = (f16)bf16_to_f(u[i] & 0xFFFFu);
+          h.y = (f16)bf16_to_f(u[i] >> 16);
+          u[i] = as_u(h);
+        }
+      }
+      *reinterpret_cast<uint4*>(lds_a + arr[q] * AST + 8 * aseg[q]) = v;
+    }
+    uint32_t cur[2][2][Fmt<F>::WORDS];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q = 0; q < Fmt<F>::WORDS; ++q) cur[nt][c][q] = cw[nt][c][q];
+    half2v s16[2], b2[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float sc, bi;
+      if constexpr (Fmt<F>::AFF) {
+        sc = bf16_to_f(sraw[nt] & 0xFFFFu);
+        bi = bf16_to_f(sraw[nt] >> 16);
+      } else {
+        sc = f16_bits_to_f(sraw[nt]);
+        bi = 0.f;
+      }
+      const f16 sh = (f16)(16.0f * sc), bh = (f16)bi;
+      s16[nt] = {sh, sh};
+      b2[nt] = {bh, bh};
+    }
+    if (k0 + 64 < K) issue(k0 + 64);
+    __syncthreads();
+    // 4 MFMA k-steps of 16: chunk c = kk / 2, word = 2 * (kk % 2) + hsel
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk >> 1, wsel = 2 * (kk & 1) + hsel;
+      half8v_t bf[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        uint32_t d[4];
+        deq_chunk_half<F>(cur[nt][c], wsel, s16[nt], b2[nt], d);
+        bf[nt] = __builtin_bit_cast(half8v_t, *reinterpret_cast<uint4*>(d));
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint4 af = *reinterpret_cast<const uint4*>(lds_a + (32 * mt + col) * AST + 16 * kk + 8 * hsel);
+        const half8v_t ah = __builtin_bit_cast(half8v_t, af);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bf[nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  }
+  // ---- epilogue
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 32 * mt + 8 * (v / 4) + 4 * hsel + (v % 4);
+      if (row >= mc) continue;
+      const int pos = m0 + row;
+      if constexpr (MODE == GU) {
+        const float g = acc[mt][0][v], u = acc[mt][1][v];
+        const float hv = silu_mul(g, u);
+        const int j = 32 * T + col;
+        a.hbuf[(uint64_t)pos * a.Imax + j] = __builtin_bit_cast(uint16_t, (f16)hv);
+        if (a.tap_gu || a.tap_h) {
+          const uint64_t s = (uint64_t)a.perm[pos];
+          if (a.tap_gu) {
+            a.tap_gu[(s * 2 + 0) * a.Imax + j] = g;
+            a.tap_gu[(s * 2 + 1) * a.Imax + j] = u;
+          }
+          if (a.tap_h) a.tap_h[s * a.Imax + j] = hv;
+        }
+      } else {
+        const uint64_t s = (uint64_t)a.perm[pos];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int n = 64 * T + 32 * nt + col;
+          a.e_ws[s * H + n] = acc[mt][nt][v];
+          if (a.tap_e) a.tap_e[s * H + n] = acc[mt][nt][v];
+        }
+      }
+    }
+  }
+}
+
+// grid: (tiles of the list) x (column blocks); list 0 = 128-row tiles, 1 = 32-row tiles
+template <int FR, int FS, int MODE, int MT, int ACT16>
+__global__ __launch_bounds__(256) void k_grp_gemm(GroupedArgs a, const uint16_t* __restrict__ x, int list) {
+  __shared__ __align__(16) uint16_t lds_a[32 * MT * 72];
+  const int nblk = a.gemm_nblk;
+  const int wg = blockIdx.x;
+  const int ti = wg / nblk, nb = wg % nblk;
+  const int ntiles = a.meta[list];
+  if (ti >= ntiles) return;
+  const int* t = a.tiles + 3 * (list ? a.max_tiles + ti : ti);
+  const int e = t[0], m0 = t[1], mc = t[2];
+  if (e < 0 || e > a.E || mc <= 0) return;
+  const bool shared = e == a.E;
+  const int I = shared ? a.sh.inter : a.rt.inter;
+  const int nlt = MODE == GU ? 2 * I / 64 : a.H / 64;   // layout tiles of this expert along N
+  if (nb * 4 >= nlt) return;
+  if (shared) grp_tile<FS, MODE, MT, ACT16>(a, x, e, m0, mc, nb, lds_a);
+  else grp_tile<FR, MODE, MT, ACT16>(a, x, e, m0, mc, nb, lds_a);
+}
+
+// ------------------------------------------------------------------ combine
+__global__ __launch_bounds__(256) void k_grp_combine(GroupedArgs a) {
+  const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  const int H = a.H, k = a.k;
+  if (i >= (uint64_t)a.R * H) return;
+  const int r = (int)(i / H), n = (int)(i % H);
+  const float* e = a.e_ws + (uint64_t)r * (k + 1) * H + n;
+  float y = 0.f;
+  for (int j = 0; j < k; ++j) y = fmaf(a.p[r * k + j], e[(uint64_t)j * H], y);
+  y = fmaf(a.sg[r], e[(uint64_t)k * H], y);
+  a.y[i] = y;
+}
+
+// ------------------------------------------------------------------ launch
+template <int FR, int FS, int MODE, int ACT16>
+static hipError_t launch_gemm(const GroupedArgs& a, hipStream_t s, int nblk) {
+  GroupedArgs b = a;
+  b.gemm_nblk = nblk;
+  // upper bounds of the two lists: every expert's rows split in tiles
+  const int slots = a.R * (a.k + 1);
+  // an expert of c >= 96 rows takes ceil(c / 128) <= c / 128 + c / 96 tiles
+  const int max_big = slots / 128 + slots / BIG_MIN_ROWS + 1;
+  const int max_small = slots / 32 + a.E + 1;
+  hipLaunchKernelGGL((k_grp_gemm<FR, FS, MODE, 4, ACT16>), dim3(max_big * nblk), dim3(256), 0, s, b, a.x, 0);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((k_grp_gemm<FR, FS, MODE, 1, ACT16>), dim3(max_small * nblk), dim3(256), 0, s, b, a.x, 1);
+  return hipGetLastError();
+}
+
+template <int FR, int FS, int ACT16>
+static hipError_t launch_grouped_t(const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
+  const int Imax = a.Imax;
+  mark(ev, 0, s);
+  hipLaunchKernelGGL(k_grp_sort, dim3(1), dim3(1024), 0, s, a);
+  mark(ev, 1, s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  mark(ev, 2, s);
+  err = launch_gemm<FR, FS, GU, ACT16>(a, s, (2 * Imax / 64 + 3) / 4);
+  mark(ev, 3, s);
+  if (err != hipSuccess) return err;
+  mark(ev, 4, s);
+  err = launch_gemm<FR, FS, DN, ACT16>(a, s, (a.H / 64 + 3) / 4);
+  mark(ev, 5, s);
+  if (err != hipSuccess) return err;
+  mark(ev, 6, s);
+  const uint64_t n = (uint64_t)a.R * a.H;
+  hipLaunchKernelGGL(k_grp_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  mark(ev, 7, s);
+  return hipGetLastError();
+}
+
+template <int FR, int FS>
+static hipError_t launch_grouped_a(const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
+  return a.act_fp16 ? launch_grouped_t<FR, FS, 1>(a, s, ev) : launch_grouped_t<FR, FS, 0>(a, s, ev);
+}
+
+template <int FR>
+static hipError_t launch_grouped_s(int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
+  switch (fs) {
+    case F_Q4: return launch_grouped_a<FR, F_Q4>(a, s, ev);
+    case F_Q3: return launch_grouped_a<FR, F_Q3>(a, s, ev);
+    case F_S4: return launch_grouped_a<FR, F_S4>(a, s, ev);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
+  switch (fr) {
+    case F_Q4: return launch_grouped_s<F_Q4>(fs, a, s, ev);
+    case F_Q3: return launch_grouped_s<F_Q3>(fs, a, s, ev);
+    case F_S4: return launch_grouped_s<F_S4>(fs, a, s, ev);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace moe

@@ -54,12 +54,11 @@ DecodeWs decode_ws_layout(const moe_layer_desc* d, int rows);
 
 // Per-kind workspace layout of the grouped path.
 struct GroupedWs {
-  uint64_t meta_off;   // after the route scratch   // int32 counts[E+1], offsets[E+2], tiles...
+  uint64_t meta_off;   // after the route scratch: int32 tile counts, offsets[E+2]
   uint64_t perm_off;   // int32 [R*k + R]: expert-major position -> slot index (r*(k+1)+j)
-  uint64_t xs_off;     // f16 [R, H]: x converted once
   uint64_t h_off;      // f16 [R*(k+1), Imax] in expert-major order
   uint64_t e_off;      // f32 [R*(k+1), H] in slot order (r*(k+1)+j)
-  uint64_t tiles_off;  // int32 tile descriptors
+  uint64_t tiles_off;  // int32 [2][max_tiles][3] tile lists
   uint64_t total;
   int max_tiles;
 };

@@ -54,11 +54,11 @@ struct GroupedArgs {
   const float* sg;
   int32_t* meta;     // counts/offsets/tile count
   int32_t* perm;     // expert-major position -> slot index r*(k+1)+j
-  uint16_t* xs;      // [R, H] fp16 bits
   uint16_t* hbuf;    // [R*(k+1), Imax] fp16 bits (expert-major order)
   float* e_ws;       // [R*(k+1), H] slot order
-  int32_t* tiles;    // tile descriptors
-  int max_tiles;
+  int32_t* tiles;    // two tile lists of (expert, first position, rows)
+  int max_tiles;     // capacity of each list
+  int gemm_nblk;     // column blocks of the GEMM being launched
   float* y;
   float* tap_gu;
   float* tap_h;

@@ -370,15 +370,14 @@ GroupedWs grouped_ws_layout(const moe_layer_desc* d, int rows) {
   const uint64_t slots = (uint64_t)rows * (k + 1);
   GroupedWs w;
   uint64_t o = route_ws_bytes(d, rows);
-  w.meta_off = o; o = align256(o + (3 * (E + 2) + 64) * 4);
+  w.meta_off = o; o = align256(o + (8 + E + 2) * 4);
   w.perm_off = o; o = align256(o + slots * 4);
-  w.xs_off = o; o = align256(o + (uint64_t)rows * H * 2);
   w.h_off = o; o = align256(o + slots * Imax * 2);
   w.e_off = o; o = align256(o + slots * H * 4);
-  // tiles: every expert (and the shared one) splits its rows into M-tiles of
-  // at least 16 rows: at most slots/16 + (E + 1) tiles
-  w.max_tiles = (int)(slots / 16 + E + 1);
-  w.tiles_off = o; o = align256(o + (uint64_t)w.max_tiles * 16);
+  // tile lists: an expert's rows split into M-tiles of 32 or 128 rows
+  // (128 only from 96 rows on): each list holds at most slots/32 + E + 1
+  w.max_tiles = (int)(slots / 32 + E + 2);
+  w.tiles_off = o; o = align256(o + (uint64_t)w.max_tiles * 2 * 3 * 4);
   w.total = o;
   return w;
 }
