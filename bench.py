@@ -79,7 +79,7 @@ def build_layers(spec, n_layers, B, to_abi, synth, keep_host=0):
     return layers, host_keep
 
 
-def cpu_baseline(spec, Lh, rows, budget_s=20.0):
+def cpu_baseline(spec, Lh, rows, budget_s=15.0):
     """The FP64 oracle (as it stands) on one layer x `rows` rows, BLAS on 1 thread."""
     import contextlib
 
@@ -102,8 +102,161 @@ def cpu_baseline(spec, Lh, rows, budget_s=20.0):
                 break
         dt = time.perf_counter() - t0
     return dict(value=done / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{done} decode rows x 1 layer of the same workload (per-row fp64 form, "
-                       f"experts dequantised on first use), {dt:.1f} s")
+                sample=f"{done} decode rows (x of the workload's first layer) through that "
+                       f"layer, per-row fp64 form, experts dequantised on first use, {dt:.1f} s")
+
+
+def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream):
+    """One prompt chunk through one layer: route + grouped experts, timed as a
+    HIP graph; per-phase times from events inside the library's launches."""
+    spec = synth.CONFIGS[cfg_id]
+    R, k, H, E = spec.rows[0], spec.top_k, spec.hidden, spec.n_experts
+    I, Is = spec.inter, spec.shared_inter
+    Lh = synth.make_layer(spec, 0)
+    layer = B.pack_layer(B.layer_desc(*to_abi.desc_args(spec)), to_abi.tensors(Lh))
+    bias = torch.from_numpy(Lh.logit_bias).to(dev) if Lh.logit_bias is not None else None
+    del Lh
+    x = torch.from_numpy(synth.make_x(spec, 0, R, rep=0).view(np.int16)).to(dev)
+    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
+    p = torch.empty((R, k), dtype=torch.float32, device=dev)
+    sg = torch.empty((R,), dtype=torch.float32, device=dev)
+    y = torch.empty((R, H), dtype=torch.float32, device=dev)
+    ws = B.new_workspace(layer, R, True, dev)
+
+    def chunk(events=None):
+        B.route(layer, x, bias, taps=dict(events=events[:2]) if events else None,
+                out=(ids, p, sg), ws=ws, stream=stream)
+        B.experts(layer, x, ids, p, sg, True, ws=ws, y=y,
+                  taps=dict(events=events[2:]) if events else None, stream=stream)
+
+    with torch.cuda.stream(stream):
+        chunk()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            chunk()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / steps * 1e3
+    # per phase: route | sort | gate/up GEMMs | down GEMMs | combine
+    n_ev = 10
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for es in evs:
+            for e in es:
+                e.record(stream)
+        for es in evs:
+            chunk(events=es)
+        torch.cuda.synchronize()
+    ph = np.zeros(5)
+    for es in evs:
+        for i in range(5):
+            ph[i] += es[2 * i].elapsed_time(es[2 * i + 1])
+    ph = ph / steps * 1e3
+    slots = R * k
+    f_gu = 2.0 * (slots * 2 * I + R * 2 * Is) * H
+    f_dn = 2.0 * (slots * I + R * Is) * H
+    f_rt = 2.0 * R * H * (E + 1)
+    ids_h = ids.cpu().numpy()
+    cnt = np.bincount(ids_h.reshape(-1), minlength=E)
+    tf = lambda f, t: f / (t * 1e-6) / 1e12
+    res = {
+        "workload": spec.name, "rows": R, "us_per_chunk": us, "tokens_per_s": R / (us * 1e-6),
+        "flop": f_gu + f_dn + f_rt, "tflops": tf(f_gu + f_dn + f_rt, us),
+        "frac_mfma_peak": tf(f_gu + f_dn + f_rt, us) / MFMA_F16_PEAK_TFLOPS,
+        "phase_us": {"route": ph[0], "sort": ph[1], "gate_up": ph[2], "down": ph[3],
+                     "combine": ph[4]},
+        "gate_up_tflops": tf(f_gu, ph[2]), "down_tflops": tf(f_dn, ph[3]),
+        "rows_per_expert": {"max": int(cnt.max()), "mean": float(cnt.mean()),
+                            "empty": int((cnt == 0).sum())},
+    }
+    log(f"[bench] prefill {spec.name}: {us:.1f} us/chunk, {res['tokens_per_s']:.0f} tokens/s, "
+        f"{res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma_peak']:.1f}% of f16 MFMA); "
+        + ", ".join(f"{k_} {v:.1f}" for k_, v in res["phase_us"].items()))
+    return res
+
+
+def kernel_source_hash():
+    """sha256 over the decode kernel sources: a stored counter figure applies
+    only to the kernel it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode.hip", "moe_kernels.h", "moe_launch.h"):
+        with open(os.path.join(ROOT, "quantized_routed_expert_fp32_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE passes, scaled by the copy-kernel factors),
+    or None when the summary is absent or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_decode-8rows-40layers_pmc.md")
+    try:
+        with open(path) as fh:
+            kv = dict(l.strip("- \n").split(": ", 1) for l in fh if l.startswith("- ") and ": " in l)
+        if kv.get("source_sha256") != kernel_source_hash():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain copy of known size (3 x 1 GiB), for scaling the HBM counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n}), flush=True)
+
+
+def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel, commands):
+    """Markdown summary of the HBM byte counters of `kernel`: mean FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch) scaled by what the same counters read
+    for a plain copy of 1 GiB."""
+    import csv
+
+    def mean_kib(path, name):
+        v = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+             if name in r["Kernel_Name"]]
+        return sum(v) / len(v), len(v)
+
+    f_kib, nf = mean_kib(fetch_csv, kernel)
+    w_kib, nw = mean_kib(write_csv, kernel)
+    cf_kib, _ = mean_kib(copy_fetch_csv, "copyBuffer")
+    cw_kib, _ = mean_kib(copy_write_csv, "copyBuffer")
+    gib_kib = float(1 << 20)
+    f_scale, w_scale = gib_kib / cf_kib, gib_kib / cw_kib
+    total = (f_kib * f_scale + w_kib * w_scale) * 1024
+    lines = [f"# HBM traffic of {kernel}, decode 8 rows x 40 layers (4-bit g64)", "",
+             "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "Figures:", "",
+              f"- kernel: {kernel}",
+              f"- dispatches: {nf} (FETCH_SIZE pass), {nw} (WRITE_SIZE pass)",
+              f"- fetch_kib_per_dispatch: {f_kib:.1f}",
+              f"- write_kib_per_dispatch: {w_kib:.1f}",
+              f"- copy_1GiB_fetch_kib: {cf_kib:.1f}",
+              f"- copy_1GiB_write_kib: {cw_kib:.1f}",
+              f"- fetch_scale: {f_scale:.4f}",
+              f"- write_scale: {w_scale:.4f}",
+              f"- hbm_bytes_per_launch: {total:.0f}",
+              f"- source_sha256: {kernel_source_hash()}"]
+    return "\n".join(lines) + "\n"
 
 
 def main():
@@ -114,7 +267,32 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="override the 40 layers (debug)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="only the prompt-chunk lines (debug)")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a plain 1 GiB copy (scales the HBM byte counters)")
+    ap.add_argument("--counter-summary", nargs=4, metavar="CSV",
+                    help="print the counter summary of k_dec_gateup from the FETCH_SIZE, "
+                         "WRITE_SIZE, copy FETCH_SIZE and copy WRITE_SIZE counter CSVs")
     args = ap.parse_args()
+    if args.copy_calib:
+        copy_calibration()
+        return
+    if args.counter_summary:
+        cmds = [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcF -o f -- "
+            "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-prefill --no-graph",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcW -o w -- "
+            "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-prefill --no-graph",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/cpF -o f -- "
+            "python3 bench.py --copy-calib",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/cpW -o w -- "
+            "python3 bench.py --copy-calib",
+            "python3 bench.py --counter-summary gpurun_out/pmcF/f_counter_collection.csv "
+            "gpurun_out/pmcW/w_counter_collection.csv gpurun_out/cpF/f_counter_collection.csv "
+            "gpurun_out/cpW/w_counter_collection.csv"]
+        sys.stdout.write(counter_summary(*args.counter_summary, "k_dec_gateup", cmds))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not run "
               "(the routed-expert FFN is benchmarked on a single MI355X).", file=sys.stderr)
@@ -129,6 +307,14 @@ def main():
     torch.cuda.init()
     dev = torch.device("cuda:0")
 
+    stream = torch.cuda.Stream()
+    prefill = None
+    if not args.no_prefill:
+        prefill = [bench_prefill(c, 20, 3, B, to_abi, synth, torch, dev, stream) for c in (3, 4)]
+        if args.prefill_only:
+            print(json.dumps({"prefill": prefill}), flush=True)
+            return
+
     spec = synth.CONFIGS[1]
     L = args.layers or spec.layers
     R, k, H = spec.rows[0], spec.top_k, spec.hidden
@@ -142,7 +328,6 @@ def main():
     sg = torch.empty((R,), dtype=torch.float32, device=dev)
     y = torch.empty((R, H), dtype=torch.float32, device=dev)
     ws = B.new_workspace(layers[0], R, False, dev)
-    stream = torch.cuda.Stream()
 
     def step(s, events=None):
         for l in range(L):
@@ -233,7 +418,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
-        cpu = cpu_baseline(spec, host[0], R)
+        cpu = cpu_baseline(spec, host[0], 64)
         log(f"[bench] cpu baseline {cpu['value']:.3f} tokens/s")
 
     out = {
@@ -255,7 +440,8 @@ def main():
                    "timing": "hip graph replay" if graphs else "eager"},
         "roofline": {"bound": "hbm", "kernel": "k_dec_gateup", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "mean_us": gu_ms * 1e3, "bytes_per_launch": gu_bytes},
+                     "traffic": stored_traffic("k_dec_gateup"), "mean_us": gu_ms * 1e3,
+                     "bytes_per_launch": gu_bytes},
         "step_hbm": {"algorithmic_bytes": mean_step_bytes,
                      "gbs": mean_step_bytes / ms_step / 1e6,
                      "frac": mean_step_bytes / ms_step / 1e6 / HBM_PEAK_GBS,
@@ -263,6 +449,7 @@ def main():
                      "kernel_us": {"route": kus[0], "decode_gateup": kus[1],
                                    "decode_down_combine": kus[2]},
                      "mean_unique_experts": float(uniq.mean())},
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

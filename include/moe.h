@@ -130,10 +130,13 @@ typedef struct moe_taps {
   float* gu;
   float* h;
   float* e;
-  /* Optional timing: kernel_events[2i] / [2i+1] (hipEvent_t, may be NULL) are
-   * recorded on the stream just before / after the i-th kernel the call
-   * enqueues (route: 1 kernel; decode: gate/up, down + combine;
-   * grouped: see moe_experts_grouped). */
+  /* Optional timing: kernel_events[2i] / [2i+1] (hipEvent_t, may be NULL)
+   * take the start / end time of the i-th kernel's own dispatch (the kernel
+   * is launched with hipExtLaunchKernel), so hipEventElapsedTime gives the
+   * kernel's execution time. Kernels: route: 1; decode: gate/up, then
+   * down + combine; grouped: sort, gate/up GEMMs, down GEMMs, combine (a
+   * phase of two launches takes the first one's start and the second one's
+   * end). Events are used only outside stream capture. */
   void* kernel_events[8];
 } moe_taps;
 

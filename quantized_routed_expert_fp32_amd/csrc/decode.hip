@@ -27,6 +27,7 @@
 // agree on: the per-row kernels keep one stream's sum order).
 #include "moe_kernels.h"
 #include "moe_launch.h"
+#include "moe_dispatch.h"
 
 namespace moe {
 
@@ -256,18 +257,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t
   const int units = a.R * a.k + a.R;
   const int gu_tiles = 2 * a.Imax / 64;
   const size_t smem = (size_t)nw * 64 * 4 + (size_t)nw * 512;
-  mark(ev, 0, s);
   if (a.act_fp16)
-    hipLaunchKernelGGL((k_dec_gateup<FR, FS, 1>), dim3(gu_tiles, units), dim3(64 * nw), smem, s, a, a.x);
+    launch_k(k_dec_gateup<FR, FS, 1>, dim3(gu_tiles, units), dim3(64 * nw), smem, s, ev, 0, a, a.x);
   else
-    hipLaunchKernelGGL((k_dec_gateup<FR, FS, 0>), dim3(gu_tiles, units), dim3(64 * nw), smem, s, a, a.x);
-  mark(ev, 1, s);
+    launch_k(k_dec_gateup<FR, FS, 0>, dim3(gu_tiles, units), dim3(64 * nw), smem, s, ev, 0, a, a.x);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  mark(ev, 2, s);
-  hipLaunchKernelGGL((k_dec_down<FR, FS>), dim3((a.H / 64) * a.R), dim3(64 * a.k), 0, s, a,
-                     a.hhi, a.hlo, a.hc);
-  mark(ev, 3, s);
+  launch_k(k_dec_down<FR, FS>, dim3((a.H / 64) * a.R), dim3(64 * a.k), 0, s, ev, 2, a,
+           (const uint16_t*)a.hhi, (const uint16_t*)a.hlo, (const float*)a.hc);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@
 //  per-row form, so it is judged by tolerance, not bits.)
 #include "moe_kernels.h"
 #include "moe_launch.h"
+#include "moe_dispatch.h"
 
 namespace moe {
 
@@ -372,41 +373,34 @@ __global__ __launch_bounds__(256) void k_grp_combine(GroupedArgs a) {
 
 // ------------------------------------------------------------------ launch
 template <int FR, int FS, int MODE, int ACT16>
-static hipError_t launch_gemm(const GroupedArgs& a, hipStream_t s, int nblk) {
+static hipError_t launch_gemm(const GroupedArgs& a, hipStream_t s, int nblk, hipEvent_t* ev, int i) {
   GroupedArgs b = a;
   b.gemm_nblk = nblk;
-  // upper bounds of the two lists: every expert's rows split in tiles
+  // upper bounds of the two lists: every expert's rows split in tiles; an
+  // expert of c >= 96 rows takes ceil(c / 128) <= c / 128 + c / 96 tiles
   const int slots = a.R * (a.k + 1);
-  // an expert of c >= 96 rows takes ceil(c / 128) <= c / 128 + c / 96 tiles
   const int max_big = slots / 128 + slots / BIG_MIN_ROWS + 1;
   const int max_small = slots / 32 + a.E + 1;
-  hipLaunchKernelGGL((k_grp_gemm<FR, FS, MODE, 4, ACT16>), dim3(max_big * nblk), dim3(256), 0, s, b, a.x, 0);
+  hipEvent_t e0[2] = {ev ? ev[i] : nullptr, nullptr}, e1[2] = {nullptr, ev ? ev[i + 1] : nullptr};
+  launch_k(k_grp_gemm<FR, FS, MODE, 4, ACT16>, dim3(max_big * nblk), dim3(256), 0, s, e0, 0, b, a.x, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((k_grp_gemm<FR, FS, MODE, 1, ACT16>), dim3(max_small * nblk), dim3(256), 0, s, b, a.x, 1);
+  launch_k(k_grp_gemm<FR, FS, MODE, 1, ACT16>, dim3(max_small * nblk), dim3(256), 0, s, e1, 0, b, a.x, 1);
   return hipGetLastError();
 }
 
 template <int FR, int FS, int ACT16>
 static hipError_t launch_grouped_t(const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
   const int Imax = a.Imax;
-  mark(ev, 0, s);
-  hipLaunchKernelGGL(k_grp_sort, dim3(1), dim3(1024), 0, s, a);
-  mark(ev, 1, s);
+  launch_k(k_grp_sort, dim3(1), dim3(1024), 0, s, ev, 0, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  mark(ev, 2, s);
-  err = launch_gemm<FR, FS, GU, ACT16>(a, s, (2 * Imax / 64 + 3) / 4);
-  mark(ev, 3, s);
+  err = launch_gemm<FR, FS, GU, ACT16>(a, s, (2 * Imax / 64 + 3) / 4, ev, 2);
   if (err != hipSuccess) return err;
-  mark(ev, 4, s);
-  err = launch_gemm<FR, FS, DN, ACT16>(a, s, (a.H / 64 + 3) / 4);
-  mark(ev, 5, s);
+  err = launch_gemm<FR, FS, DN, ACT16>(a, s, (a.H / 64 + 3) / 4, ev, 4);
   if (err != hipSuccess) return err;
-  mark(ev, 6, s);
   const uint64_t n = (uint64_t)a.R * a.H;
-  hipLaunchKernelGGL(k_grp_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
-  mark(ev, 7, s);
+  launch_k(k_grp_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ev, 6, a);
   return hipGetLastError();
 }
 

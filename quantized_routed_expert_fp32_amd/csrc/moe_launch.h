@@ -70,8 +70,4 @@ hipError_t launch_route(int fr, int fg, const RouteArgs& a, hipStream_t s, hipEv
 hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev);
 
-inline void mark(hipEvent_t* ev, int i, hipStream_t s) {
-  if (ev && ev[i]) hipEventRecord(ev[i], s);
-}
-
 }  // namespace moe

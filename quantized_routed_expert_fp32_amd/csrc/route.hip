@@ -11,6 +11,7 @@
 // exp(l - l_top) / sum and sigmoid(gate).
 #include "moe_kernels.h"
 #include "moe_launch.h"
+#include "moe_dispatch.h"
 
 namespace moe {
 
@@ -210,12 +211,10 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
 template <int FR, int FG>
 static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
   const int nw = min(8, a.H / KBLK);
-  mark(ev, 0, s);
   if (a.act_fp16)
-    hipLaunchKernelGGL((k_route<FR, FG, 1>), dim3(a.E / 64, a.R), dim3(64 * nw), 0, s, a, a.x);
+    launch_k(k_route<FR, FG, 1>, dim3(a.E / 64, a.R), dim3(64 * nw), 0, s, ev, 0, a, a.x);
   else
-    hipLaunchKernelGGL((k_route<FR, FG, 0>), dim3(a.E / 64, a.R), dim3(64 * nw), 0, s, a, a.x);
-  mark(ev, 1, s);
+    launch_k(k_route<FR, FG, 0>, dim3(a.E / 64, a.R), dim3(64 * nw), 0, s, ev, 0, a, a.x);
   return hipGetLastError();
 }
 
