@@ -51,6 +51,7 @@ static ExpertClass expert_class(const moe_layer* L, bool shared) {
     c.gu_scales = L->sh_gu.scales;
     c.dn_codes = L->sh_dn.codes;
     c.dn_scales = L->sh_dn.scales;
+    c.blk_bytes = (uint32_t)(L->bytes - L->shared_off);
     c.inter = L->d.shared_inter;
   } else {
     c.base_off = L->experts_off;
@@ -59,6 +60,7 @@ static ExpertClass expert_class(const moe_layer* L, bool shared) {
     c.gu_scales = L->gu.scales;
     c.dn_codes = L->dn.codes;
     c.dn_scales = L->dn.scales;
+    c.blk_bytes = (uint32_t)L->expert_stride;
     c.inter = L->d.inter;
   }
   return c;
@@ -165,9 +167,9 @@ int moe_route(const moe_layer* layer, const void* x, int rows, const float* logi
   a.logits = taps ? taps->logits : nullptr;
   const RouteWs rw = route_ws_layout(&layer->d, rows);
   uint8_t* wb = static_cast<uint8_t*>(ws);
-  a.cnt = reinterpret_cast<unsigned*>(wb + rw.cnt_off);
-  a.gl_ws = reinterpret_cast<float*>(wb + rw.gl_off);
   a.lg_ws = reinterpret_cast<float*>(wb + rw.lg_off);
+  a.gl_ws = reinterpret_cast<float*>(wb + rw.gl_off);
+  a.cnt = reinterpret_cast<unsigned*>(wb + rw.cnt_off);
   hipError_t e = launch_route(fr.kid, fg.kid, a, static_cast<hipStream_t>(stream), taps_events(taps));
   if (e != hipSuccess) return hip_fail("moe_route: launch", e);
   return MOE_OK;

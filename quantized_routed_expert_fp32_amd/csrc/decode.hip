@@ -1,190 +1,439 @@
 // Decode path: routed + shared experts for up to 16 independent rows.
 //
-// gate/up (k_dec_gateup): one workgroup per (unit, 64-row tile of the
-// interleaved gate/up matrix), one wave per 256-wide K slice. A unit is a
-// slot (row r, pick j) whose expert no earlier slot picked, or the shared
-// expert for one row: it streams the tile's packed codes once (coalesced 128-bit loads,
-// lane = weight row) for every row that picked the expert, so rows sharing
-// an expert share its reads ("Native server: --backend xpu for Nemotron on
-// Intel Arc", review comments: each extra row costs more because more
-// distinct experts are read; the gain needs expert reads shared across
-// rows). Each wave finds its unit from the picks with one ballot (no LDS, no
-// barrier) and reads activations with uniform loads straight into
-// v_dot2_f32_bf16 / v_dot2_f32_f16. Output: h = silu(g)*u split into fp16
-// hi + lo parts (22 significant bits) plus per-32 chunk sums, for down.
+// gate/up (k_dec_gateup): a persistent grid. A unit is an expert picked by
+// some row, found from the picks as the first slot (row r, pick j) that
+// holds it, or the shared expert for one row; an item is (unit, 64-row tile
+// of the interleaved gate/up matrix). Workgroup b takes items b, b + G, ...;
+// wave w owns the 256-wide K slice w, one weight row per lane, and streams
+// the tile's packed codes once (coalesced 128-bit loads) for every row that
+// picked the expert, so rows sharing an expert share its reads ("Native
+// server: --backend xpu for Nemotron on Intel Arc", review comments: each
+// extra row costs more because more distinct experts are read). The codes
+// and scale words of the next item are in flight while the current one is
+// computed. The activations of all rows sit in LDS (loaded once per
+// workgroup) with their 32-wide chunk sums. Output: h = silu(g)*u split into
+// fp16 hi + lo parts (22 significant bits) plus per-32 chunk sums, for down.
 //
-// down + combine (k_dec_down): one workgroup per (row, 64-column tile of y),
-// k waves. Wave j computes routed slot j's output columns over the full
-// intermediate axis plus 1/k of the shared expert's (added in wave order);
-// wave 0 then forms y = sum_j p_j e_j + sigma e_shared in slot order. Blocks
-// are mapped so the rows of one tile run on one XCD and share the shared
-// expert's tile in that XCD's L2.
+// down + combine (k_dec_down): one workgroup per (row, 64-column tile of y)
+// with KS waves per routed slot, each over 1/KS of the intermediate axis,
+// plus a share of the shared expert's groups; the row's h sits in LDS. The
+// slot parts are added in part order, the shared parts in wave order; wave 0
+// forms y = sum_j p_j e_j + sigma e_shared in slot order. Blocks are mapped so
+// the rows of one tile run on one XCD and share expert tiles in its L2.
 //
-// Every row's arithmetic is fixed (K slices owned by fixed waves, chunks
-// and groups in K order, slices reduced in slice order, slots combined in
-// pick order, shared last) and independent of the other rows, so a row's y
-// is bit-identical alone or in a batch ("Sage-A1.5 ... #1329", Limits to
-// agree on: the per-row kernels keep one stream's sum order).
+// Every row's arithmetic is fixed (K slices owned by fixed waves, chunks and
+// groups in K order, slices reduced in slice order, slots combined in pick
+// order, shared last) and independent of the other rows, so a row's y is
+// bit-identical alone or in a batch ("Sage-A1.5 ... #1329", Limits to agree
+// on: the per-row kernels keep one stream's sum order).
 #include "moe_kernels.h"
 #include "moe_launch.h"
 #include "moe_dispatch.h"
 
+#include <algorithm>
+
 namespace moe {
 
-// Rows of one unit, one at a time: the wave's codes stay in registers (one
-// K slice per wave when H <= 2048) and each row re-runs the unpack, which is
-// free for the usual single-row unit.
-template <int F, int ACT16>
-__device__ __forceinline__ void gu_body(const DecodeArgs& a, const uint16_t* __restrict__ x,
-                                        const uint8_t* codes, const uint8_t* scales,
-                                        int t, int nrows, int shared_row, uint64_t m0, uint64_t m1,
-                                        float* red, uint32_t* lx) {
-  // wave wv owns the K slices wv, wv + nw, ...
-  const int H = a.H, k = a.k, nsl = H / KBLK, nch = H / 32;
-  const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
-  uint32_t w[8][Fmt<F>::WORDS];
-  if (wv < nsl) {
+// Codes (8 chunks of one K slice) and scale words of one lane.
+struct SliceBuf {
+  uint32_t w[8][4];
+  uint32_t sc[4];
+};
+
+// Codes and scale words of K slice sl of tile t of a matrix in the range
+// behind r (codes / scales: byte offsets of the matrix's parts in it).
+template <int F>
+__device__ __forceinline__ void load_slice(rsrc_t r, uint32_t codes, uint32_t scales, int t, int sl, int nch,
+                                           int nkb, int lane, SliceBuf& b) {
+  const uint32_t vc = chunk_voff<F>(lane), vs = scale_voff<F>(lane);
+  // scale words first: group 0's arithmetic then waits only for its chunks
+  load_scales_rs<F>(r, vs, scales + (uint32_t)sblk_off<F>(t, sl, nkb), b.sc);
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) load_chunk<F>(codes + chunk_off<F>(t, wv * 8 + cc, nch), lane, w[cc]);
+  for (int cc = 0; cc < 8; ++cc)
+    load_chunk_rs<F>(r, vc, codes + (uint32_t)chunk_off<F>(t, sl * 8 + cc, nch), b.w[cc]);
+}
+
+// The picks seen by one wave: lane l holds slots l and l + 64.
+struct Picks {
+  int id0, id1;
+  bool first0, first1;   // the slot is the first to hold its expert
+  int rank0, rank1;      // its unit index among the first slots
+  int nrt;               // routed units
+};
+
+// Slot lanes holding the same expert, from one ballot per id bit (ids < 256).
+__device__ __forceinline__ Picks find_units(int id0, int id1, int E, int lane) {
+  Picks P;
+  P.id0 = id0;
+  P.id1 = id1;
+  const bool v0 = P.id0 >= 0 && P.id0 < E, v1 = P.id1 >= 0 && P.id1 < E;
+  uint64_t M0 = __ballot(v0), N0 = __ballot(v1), M1 = M0, N1 = N0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool b0 = (P.id0 >> b) & 1, b1 = (P.id1 >> b) & 1;
+    const uint64_t B0 = __ballot(v0 && b0), B1 = __ballot(v1 && b1);
+    M0 &= b0 ? B0 : ~B0;
+    N0 &= b0 ? B1 : ~B1;
+    M1 &= b1 ? B0 : ~B0;
+    N1 &= b1 ? B1 : ~B1;
   }
-  for (int i = 0; i < nrows; ++i) {
-    int r = shared_row, j = k;
-    if (shared_row < 0) {
+  (void)N0;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  P.first0 = v0 && (M0 & lt) == 0;
+  P.first1 = v1 && M1 == 0 && (N1 & lt) == 0;
+  const uint64_t F0 = __ballot(P.first0), F1 = __ballot(P.first1);
+  P.rank0 = __popcll(F0 & lt);
+  P.rank1 = __popcll(F0) + __popcll(F1 & lt);
+  P.nrt = __popcll(F0) + __popcll(F1);
+  return P;
+}
+
+// Expert of routed unit u (uniform).
+__device__ __forceinline__ int unit_expert(const Picks& P, int u) {
+  const uint64_t s0 = __ballot(P.first0 && P.rank0 == u);
+  if (s0) return __builtin_amdgcn_readlane(P.id0, __ffsll((unsigned long long)s0) - 1);
+  const uint64_t s1 = __ballot(P.first1 && P.rank1 == u);
+  return __builtin_amdgcn_readlane(P.id1, __ffsll((unsigned long long)s1) - 1);
+}
+
+struct GuItem {
+  rsrc_t r;     // the expert block
+  uint32_t codes, scales;   // gate/up codes and scale words inside it
+  int t;        // layout tile (64 rows: 32 gate + 32 up)
+  int tl;       // tile actually loaded (t clamped into the class)
+  int shared;
+  int e;        // expert (routed) or the row (shared)
+};
+
+__device__ __forceinline__ GuItem gu_item(const DecodeArgs& a, const Picks& P, int item, int Tmax) {
+  GuItem it;
+  const int u = item / Tmax;
+  it.t = item % Tmax;
+  it.shared = u >= P.nrt;
+  const ExpertClass& ec = it.shared ? a.sh : a.rt;
+  it.e = it.shared ? u - P.nrt : unit_expert(P, u);
+  const uint8_t* blk = a.base + ec.base_off + (it.shared ? 0 : (uint64_t)it.e * ec.stride);
+  it.r = make_rsrc(blk, ec.blk_bytes);
+  it.codes = (uint32_t)ec.gu_codes;
+  it.scales = (uint32_t)ec.gu_scales;
+  it.tl = min(it.t, 2 * ec.inter / 64 - 1);
+  return it;
+}
+
+template <int FR, int FS>
+__device__ __forceinline__ void gu_issue(const GuItem& it, int wv, int nch, int nkb, int lane, SliceBuf& b) {
+  if (it.shared) load_slice<FS>(it.r, it.codes, it.scales, it.tl, wv, nch, nkb, lane, b);
+  else load_slice<FR>(it.r, it.codes, it.scales, it.tl, wv, nch, nkb, lane, b);
+}
+
+// One row of an item: the wave's slice dot from the activations in LDS.
+// Chunks are unpacked one at a time (the group's pair dots chain in order).
+template <int F, int ACT16>
+__device__ __forceinline__ float gu_slice_dot(const uint32_t (*w)[4], const uint32_t* sc, const uint32_t* xrow,
+                                              const float* csrow, int sl, float out) {
+  constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
+#pragma unroll
+  for (int gi = 0; gi < GPS; ++gi) {
+    float ms, bm;
+    coef_reg<F>(sc, gi, ms, bm);
+    float acc = 0.f, X = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < CPG; ++cc) {
+      const int c = gi * CPG + cc;
+      uint32_t v[16], av[16], wc[Fmt<F>::WORDS];
+#pragma unroll
+      for (int q = 0; q < Fmt<F>::WORDS; ++q) {
+        wc[q] = w[c][q];
+        // opaque to loop-invariant motion: the unpack stays beside its use
+        // instead of being hoisted out of the row loop for every chunk
+        asm volatile("" : "+v"(wc[q]));
+      }
+      unpack_for<F, ACT16>(wc, v);
+      const uint4* q = reinterpret_cast<const uint4*>(xrow + (sl * KBLK + 32 * c) / 2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint4 tq = q[u];
+        av[4 * u] = tq.x; av[4 * u + 1] = tq.y; av[4 * u + 2] = tq.z; av[4 * u + 3] = tq.w;
+      }
+      acc = ACT16 ? dot_chunk_h(v, av, acc) : dot_chunk_bf(v, av, acc);
+      X += csrow[sl * 8 + c];
+    }
+    out = fmaf(ms, acc, out);
+    out = fmaf(bm, X, out);
+  }
+  return out;
+}
+
+// Wave 0 after the barrier: g and u of the tile's 32 intermediate indices
+// (slices added in slice order), h = silu(g) u, split and stored.
+__device__ __forceinline__ void gu_finish(const DecodeArgs& a, const float* red, int nw, int r, int j,
+                                          int t, int lane) {
+  const int k = a.k;
+  const int c = lane & 31;
+  float g = 0.f, u = 0.f;
+  for (int q = 0; q < nw; ++q) {
+    g += red[q * 64 + c];
+    u += red[q * 64 + 32 + c];
+  }
+  const float hv = silu_mul(g, u);
+  const f16 hi = (f16)hv, lo = (f16)(hv - (float)hi);
+  // chunk sum of hi + lo over the 32 columns: 16-lane rows by DPP, then
+  // the two rows in order (lanes 0..31 and 32..63 hold the same values)
+  const float s16 = sum16((float)hi + (float)lo);
+  const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 0)) +
+                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 16));
+  if (lane < 32) {
+    const uint64_t rs = (uint64_t)r * (k + 1) + j;
+    const int col = 32 * t + c;
+    a.hhi[rs * a.Imax + col] = __builtin_bit_cast(uint16_t, hi);
+    a.hlo[rs * a.Imax + col] = __builtin_bit_cast(uint16_t, lo);
+    if (c == 0) a.hc[rs * (a.Imax / 32) + t] = sv;
+    if (a.tap_gu) {
+      a.tap_gu[(rs * 2 + 0) * a.Imax + col] = g;
+      a.tap_gu[(rs * 2 + 1) * a.Imax + col] = u;
+    }
+    if (a.tap_h) a.tap_h[rs * a.Imax + col] = hv;
+  }
+}
+
+template <int F, int ACT16>
+__device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P, const GuItem& it,
+                                             const SliceBuf& b, const uint32_t* xl, const float* cs,
+                                             float* red, int& rb, int wv, int nw, int lane) {
+  const int H = a.H, nch = H / 32, nsl = H / KBLK, k = a.k;
+  uint64_t m0 = 0, m1 = 0;
+  int n = 1;
+  if (!it.shared) {
+    m0 = __ballot(P.id0 == it.e);
+    m1 = __ballot(P.id1 == it.e);
+    n = __popcll(m0) + __popcll(m1);
+  }
+  for (int i = 0; i < n; ++i) {
+    int r = it.e, j = k;
+    if (!it.shared) {
       int s;
       if (m0) { s = __ffsll((unsigned long long)m0) - 1; m0 &= m0 - 1; }
       else { s = 64 + __ffsll((unsigned long long)m1) - 1; m1 &= m1 - 1; }
       r = s / k;
       j = s % k;
     }
-    float out = 0.f;
-    for (int sl = wv; sl < nsl; sl += nw) {
-      if (sl != wv) {
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) load_chunk<F>(codes + chunk_off<F>(t, sl * 8 + cc, nch), lane, w[cc]);
-      }
-      const uint16_t* xs[1] = {x + (uint64_t)r * H + sl * KBLK};
-      float part[1];
-      slice_dot<F, 1, ACT16>(w, scales + sblk_off<F>(t, sl, nsl), lane, xs, 1, lx + wv * 128, part);
-      out += part[0];
+    const uint32_t* xrow = xl + (uint64_t)r * (H / 2);
+    const float* csrow = cs + r * nch;
+    float out = gu_slice_dot<F, ACT16>(b.w, b.sc, xrow, csrow, wv, 0.f);
+    for (int sl = wv + nw; sl < nsl; sl += nw) {     // hidden > 256 * waves: further slices in place
+      SliceBuf c2;
+      load_slice<F>(it.r, it.codes, it.scales, it.tl, sl, nch, nsl, lane, c2);
+      out = gu_slice_dot<F, ACT16>(c2.w, c2.sc, xrow, csrow, sl, out);
     }
-    red[wv * 64 + lane] = out;
+    float* rbuf = red + rb * (nw * 64);
+    rbuf[wv * 64 + lane] = out;
     __syncthreads();
-    if (tid < 64) {
-      const int c = tid & 31;
-      float g = 0.f, u = 0.f;
-      for (int q = 0; q < nw; ++q) {
-        g += red[q * 64 + c];
-        u += red[q * 64 + 32 + c];
-      }
-      const float hv = silu_mul(g, u);
-      const f16 hi = (f16)hv, lo = (f16)(hv - (float)hi);
-      // chunk sum of hi + lo over the 32 columns: 16-lane rows by DPP, then
-      // the two rows in order (lanes 0..31 and 32..63 hold the same values)
-      const float s16 = sum16((float)hi + (float)lo);
-      const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 0)) +
-                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 16));
-      if (tid < 32) {
-        const uint64_t rs = (uint64_t)r * (k + 1) + j;
-        const int col = 32 * t + c;
-        a.hhi[rs * a.Imax + col] = __builtin_bit_cast(uint16_t, hi);
-        a.hlo[rs * a.Imax + col] = __builtin_bit_cast(uint16_t, lo);
-        if (c == 0) a.hc[rs * (a.Imax / 32) + t] = sv;
-        if (a.tap_gu) {
-          a.tap_gu[(rs * 2 + 0) * a.Imax + col] = g;
-          a.tap_gu[(rs * 2 + 1) * a.Imax + col] = u;
-        }
-        if (a.tap_h) a.tap_h[rs * a.Imax + col] = hv;
-      }
-    }
-    __syncthreads();
+    if (wv == 0) gu_finish(a, rbuf, nw, r, j, it.t, lane);
+    rb ^= 1;   // the other buffer next: its readers passed this barrier
   }
 }
 
-// grid (gate/up tiles, R*k + R units): unit u < R*k is slot u when no earlier
-// slot picked its expert; unit R*k + r is the shared expert for row r. With
-// the linear block index t + 16u, every unit of tile t runs on XCD t % 8, so
-// the shared expert's rows re-read its tile from that XCD's L2.
 template <int FR, int FS, int ACT16>
-__global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a, const uint16_t* __restrict__ x) {
-  extern __shared__ __align__(16) float red[];   // [waves][64], then per-wave x slices
-  uint32_t* lx = reinterpret_cast<uint32_t*>(red + (blockDim.x >> 6) * 64);
-  const int t = blockIdx.x, u = blockIdx.y, lane = threadIdx.x & 63;
-  const int nslot = a.R * a.k;
-  if (u < nslot) {
-    const int e = a.ids[u];
-    if (e < 0 || e >= a.E) return;
-    if (t >= 2 * a.rt.inter / 64) return;
-    const int id0 = lane < nslot ? a.ids[lane] : -1;
-    const int id1 = lane + 64 < nslot ? a.ids[lane + 64] : -1;
-    const uint64_t m0 = __ballot(id0 == e), m1 = __ballot(id1 == e);
-    const int first = m0 ? __ffsll((unsigned long long)m0) - 1 : 64 + __ffsll((unsigned long long)m1) - 1;
-    if (first != u) return;        // an earlier slot's unit serves this expert
-    const uint8_t* blk = a.base + a.rt.base_off + (uint64_t)e * a.rt.stride;
-    gu_body<FR, ACT16>(a, x, blk + a.rt.gu_codes, blk + a.rt.gu_scales, t, __popcll(m0) + __popcll(m1),
-                       -1, m0, m1, red, lx);
+__device__ __forceinline__ void gu_process(const DecodeArgs& a, const Picks& P, const GuItem& it,
+                                           const SliceBuf& b, const uint32_t* xl, const float* cs,
+                                           float* red, int& rb, int wv, int nw, int lane) {
+  if (it.t != it.tl) return;      // tile beyond this class (intermediates differ)
+  if (it.shared) gu_process_t<FS, ACT16>(a, P, it, b, xl, cs, red, rb, wv, nw, lane);
+  else gu_process_t<FR, ACT16>(a, P, it, b, xl, cs, red, rb, wv, nw, lane);
+}
+
+
+// Prologue of the gate/up kernel: the picks (lane l: slots l, l + 64) and
+// the units, the first item's loads, then the activations of all rows into
+// LDS and their 32-wide chunk sums (4 consecutive activations per lane, then
+// aligned 8-lane groups). With XV > 0 the activations come through XV
+// unconditional 16-byte register loads per thread (indexes clamped), issued
+// before the item's loads, so the compiler can count what is outstanding and
+// the wait for them leaves the item's loads in flight; XV == 0 (many rows)
+// copies them straight into LDS instead. LDS: activations [R][H] u16, chunk
+// sums [R][H/32] f32, two reduction buffers [nw][64] f32.
+struct GuCtx {
+  uint32_t* xl;
+  float* cs;
+  float* red;
+  int nw, wv, lane, nch, nsl, Tmax, n_items;
+};
+
+// Persistent grid G (a multiple of 8); block 64 * nw threads,
+// nw = min(8, H / 256): wave w owns the K slices w, w + nw, ... Item
+// i = (unit i / Tmax, tile i % Tmax); workgroup b takes items b, b + G, ...
+// and the next item's loads are in flight during the current one's
+// arithmetic. With Tmax and G multiples of 8, every item of tile t runs on
+// XCD t % 8, so the per-row shared units re-read the shared expert's tiles
+// from that L2.
+template <int FR, int FS, int ACT16, int XV>
+__global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  GuCtx c;
+  const int H = a.H, R = a.R;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  c.nw = nthr >> 6;
+  c.lane = tid & 63;
+  c.wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.nch = H / 32;
+  c.nsl = H / KBLK;
+  c.xl = reinterpret_cast<uint32_t*>(smem);
+  c.cs = reinterpret_cast<float*>(smem + (size_t)R * H * 2);
+  c.red = c.cs + R * c.nch;
+  const int nslot = R * a.k, nx = R * H / 8;     // slots, 16-byte activation pieces
+  // four named registers (not an array, which would live in scratch)
+  const uint4* xg = reinterpret_cast<const uint4*>(a.x);
+  uint4 xv0, xv1, xv2, xv3;
+  const int i0 = a.ids[min(c.lane, nslot - 1)];
+  const int i1 = a.ids[min(c.lane + 64, nslot - 1)];
+  if constexpr (XV > 0) {
+    xv0 = xg[tid % nx];        // surplus threads re-read other pieces (distinct lines)
+    xv1 = xg[(tid + nthr) % nx];
+    xv2 = xg[(tid + 2 * nthr) % nx];
+    xv3 = xg[(tid + 3 * nthr) % nx];
+    asm volatile("" ::: "memory");   // these loads go out before the item's loads
+  }
+  Picks P = find_units(c.lane < nslot ? i0 : -1, c.lane + 64 < nslot ? i1 : -1, a.E, c.lane);
+  c.Tmax = 2 * a.Imax / 64;
+  c.n_items = (P.nrt + R) * c.Tmax;
+  int it_i = blockIdx.x;
+  if (it_i >= c.n_items) return;
+  const int G = gridDim.x;
+  SliceBuf A, B;
+  GuItem ia = gu_item(a, P, it_i, c.Tmax);
+  gu_issue<FR, FS>(ia, c.wv, c.nch, c.nsl, c.lane, A);
+  if constexpr (XV > 0) {
+    // surplus threads rewrite a piece with the same bytes
+    uint4* xd = reinterpret_cast<uint4*>(c.xl);
+    xd[tid % nx] = xv0;
+    xd[(tid + nthr) % nx] = xv1;
+    xd[(tid + 2 * nthr) % nx] = xv2;
+    xd[(tid + 3 * nthr) % nx] = xv3;
   } else {
-    if (t >= 2 * a.sh.inter / 64) return;
-    const uint8_t* blk = a.base + a.sh.base_off;
-    gu_body<FS, ACT16>(a, x, blk + a.sh.gu_codes, blk + a.sh.gu_scales, t, 1, u - nslot, 0, 0, red, lx);
+    for (int base = c.wv * 64; base < nx; base += nthr) {
+      if (base + c.lane < nx)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(a.x) + base + c.lane,
+                                         (__attribute__((address_space(3))) void*)(reinterpret_cast<uint4*>(c.xl) + base),
+                                         16, 0, 0);
+    }
+  }
+  __syncthreads();
+  for (int r = 0; r < R; ++r) {
+    for (int sl = c.wv; sl < c.nsl; sl += c.nw) {
+      const uint2 v = reinterpret_cast<const uint2*>(c.xl + (uint64_t)r * (H / 2) + sl * (KBLK / 2))[c.lane];
+      const float sm = sum8(sum4<ACT16>(v));
+      if ((c.lane & 7) == 0) c.cs[r * c.nch + sl * 8 + (c.lane >> 3)] = sm;
+    }
+  }
+  __syncthreads();
+  int rb = 0;
+  for (;;) {
+    // the next item's loads go out before this item's arithmetic; past the
+    // end, the current item is re-issued (its lines are in L2)
+    int nx1 = it_i + G;
+    GuItem ib = nx1 < c.n_items ? gu_item(a, P, nx1, c.Tmax) : ia;
+    gu_issue<FR, FS>(ib, c.wv, c.nch, c.nsl, c.lane, B);
+    gu_process<FR, FS, ACT16>(a, P, ia, A, c.xl, c.cs, c.red, rb, c.wv, c.nw, c.lane);
+    if (nx1 >= c.n_items) break;
+    it_i = nx1;
+    int nx2 = it_i + G;
+    ia = nx2 < c.n_items ? gu_item(a, P, nx2, c.Tmax) : ib;
+    gu_issue<FR, FS>(ia, c.wv, c.nch, c.nsl, c.lane, A);
+    gu_process<FR, FS, ACT16>(a, P, ib, B, c.xl, c.cs, c.red, rb, c.wv, c.nw, c.lane);
+    if (nx2 >= c.n_items) break;
+    it_i = nx2;
   }
 }
 
-// Part of one slot's 64 output columns of tile t over chunks c0 .. c0+n-1 of
-// the intermediate axis (chunk c covers 32 intermediate indices): load the
-// codes (dn_load), then the dot in chunk order (dn_dot). n <= MAXC.
-template <int F, int MAXC>
-__device__ __forceinline__ void dn_load(const uint8_t* codes, int I, int t, int lane, int c0, int n,
-                                        uint32_t (&w)[MAXC][Fmt<F>::WORDS]) {
-  const int nch = I / 32;
+// ------------------------------------------------------------------ down
+constexpr int DN_KS = 2;   // waves per routed slot (each 1/KS of the intermediate axis)
+
+// Routed part: one 256-wide block (8 chunks) of one slot's h against the
+// lane's weight row. hh/hl: fp16 pairs of the block in LDS, hc: chunk sums.
+template <int F>
+__device__ __forceinline__ float dn_block(const uint32_t (&w)[8][Fmt<F>::WORDS], const uint32_t* sc,
+                                          const uint32_t* hh, const uint32_t* hl, const float* hc,
+                                          float out) {
+  constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
 #pragma unroll
-  for (int q = 0; q < MAXC; ++q)
-    if (q < n) load_chunk<F>(codes + chunk_off<F>(t, c0 + q, nch), lane, w[q]);
-}
-template <int F, int MAXC>
-__device__ __forceinline__ float dn_dot(const uint32_t (&w)[MAXC][Fmt<F>::WORDS],
-                                        const uint32_t* __restrict__ hh, const uint32_t* __restrict__ hl,
-                                        const float* __restrict__ hc, const uint8_t* scales, int I,
-                                        int t, int lane, int c0, int n) {
-  constexpr int CPG = Fmt<F>::G / 32;
-  const int nkb = I / KBLK;
-  float out = 0.f;
+  for (int gi = 0; gi < GPS; ++gi) {
+    float ms, bm;
+    coef_reg<F>(sc, gi, ms, bm);
+    float acc = 0.f, X = 0.f;
 #pragma unroll
-  for (int q0 = 0; q0 < MAXC; q0 += CPG) {
-    if (q0 < n) {
-      // one group: CPG chunks from chunk c0 + q0 (c0 is a multiple of CPG)
-      const int c = c0 + q0, sl = c / 8, gi = (c % 8) / CPG;
-      float ms, bm;
-      group_coef<F>(scales + sblk_off<F>(t, sl, nkb), lane, gi, ms, bm);
-      float acc = 0.f, X = 0.f;
+    for (int cc = 0; cc < CPG; ++cc) {
+      const int c = gi * CPG + cc;
+      uint32_t v[16], ph[16], pl[16];
+      unpack_chunk<F>(w[c], v);
+      const uint4* qh = reinterpret_cast<const uint4*>(hh + 16 * c);
+      const uint4* ql = reinterpret_cast<const uint4*>(hl + 16 * c);
 #pragma unroll
-      for (int cc = 0; cc < CPG; ++cc) {
-        uint32_t v[16], ph[16], pl[16];
-        unpack_chunk<F>(w[q0 + cc], v);
-#pragma unroll
-        for (int p = 0; p < 16; ++p) { ph[p] = hh[16 * (c + cc) + p]; pl[p] = hl[16 * (c + cc) + p]; }
-        acc = dot_chunk_h(v, ph, acc);
-        acc = dot_chunk_h(v, pl, acc);
-        X += hc[c + cc];
+      for (int u = 0; u < 4; ++u) {
+        const uint4 th = qh[u], tl = ql[u];
+        ph[4 * u] = th.x; ph[4 * u + 1] = th.y; ph[4 * u + 2] = th.z; ph[4 * u + 3] = th.w;
+        pl[4 * u] = tl.x; pl[4 * u + 1] = tl.y; pl[4 * u + 2] = tl.z; pl[4 * u + 3] = tl.w;
       }
-      out = fmaf(ms, acc, out);
-      out = fmaf(bm, X, out);
+      acc = dot_chunk_h(v, ph, acc);
+      acc = dot_chunk_h(v, pl, acc);
+      X += hc[c];
     }
+    out = fmaf(ms, acc, out);
+    out = fmaf(bm, X, out);
   }
   return out;
 }
 
-// down + combine: one workgroup per (row, 64-column tile of y) with k waves.
-// Wave j computes routed slot j over the full intermediate axis and 1/k of
-// the shared expert's chunks; the k shared parts are added in wave order.
-// Wave 0 then forms y = sum_j p_j e_j + sigma e_shared in slot order.
-template <int FR, int FS>
-__global__ __launch_bounds__(512) void k_dec_down(DecodeArgs a, const uint16_t* __restrict__ hhi,
-                                                  const uint16_t* __restrict__ hlo,
-                                                  const float* __restrict__ hcs) {
-  __shared__ float es[8][64];
-  __shared__ float ps[8][64];
-  const int T = a.H / 64, R = a.R, k = a.k;
+// One group (CPG chunks) of the shared expert: codes and its scale word.
+template <int F>
+__device__ __forceinline__ float dn_group(const uint32_t (*w)[Fmt<F>::WORDS], uint32_t scw, int gi,
+                                          const uint32_t* hh, const uint32_t* hl, const float* hc) {
+  constexpr int CPG = Fmt<F>::G / 32;
+  uint32_t sc[4] = {scw, scw, scw, scw};
+  float ms, bm;
+  // the word holds this group's entry: affine one u32, symmetric the u16 at gi % 2
+  coef_reg<F>(sc, Fmt<F>::AFF ? 0 : (gi & 1), ms, bm);
+  float acc = 0.f, X = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < CPG; ++cc) {
+    uint32_t v[16], ph[16], pl[16];
+    unpack_chunk<F>(w[cc], v);
+    const uint4* qh = reinterpret_cast<const uint4*>(hh + 16 * cc);
+    const uint4* ql = reinterpret_cast<const uint4*>(hl + 16 * cc);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 th = qh[u], tl = ql[u];
+      ph[4 * u] = th.x; ph[4 * u + 1] = th.y; ph[4 * u + 2] = th.z; ph[4 * u + 3] = th.w;
+      pl[4 * u] = tl.x; pl[4 * u + 1] = tl.y; pl[4 * u + 2] = tl.z; pl[4 * u + 3] = tl.w;
+    }
+    acc = dot_chunk_h(v, ph, acc);
+    acc = dot_chunk_h(v, pl, acc);
+    X += hc[cc];
+  }
+  return fmaf(bm, X, fmaf(ms, acc, 0.f));
+}
+
+// Per-lane byte offset, inside its scale block, of the 4-byte word holding
+// group g's entry: affine the group's u32, symmetric the u32 holding both
+// fp16 scales of the block (the entry at half g % 2).
+template <int F>
+__device__ __forceinline__ uint32_t group_word_voff(int g, int lane) {
+  constexpr int GPS = KBLK / Fmt<F>::G;
+  if constexpr (Fmt<F>::AFF) return (uint32_t)(lane * GPS + (g % GPS)) * 4;
+  else return (uint32_t)lane * 4;
+}
+
+// down + combine: one workgroup per (row, 64-column tile of y), k * KS waves.
+// LDS: the row's h (hi, lo pairs) and chunk sums for the k + 1 slots.
+template <int FR, int FS, int HV>
+__global__ __launch_bounds__(1024) void k_dec_down(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int T = a.H / 64, R = a.R, k = a.k, Imax = a.Imax;
+  const int nwv = k * DN_KS;
+  uint32_t* hhl = reinterpret_cast<uint32_t*>(smem);                     // [k+1][Imax/2]
+  uint32_t* hll = hhl + (k + 1) * (Imax / 2);                             // [k+1][Imax/2]
+  float* hcl = reinterpret_cast<float*>(hll + (k + 1) * (Imax / 2));     // [k+1][Imax/32]
+  float* es = hcl + (k + 1) * (Imax / 32);                                // [nwv][64]
+  float* ps = es + nwv * 64;                                              // [nwv][64]
   const int wg = blockIdx.x;
   int t, r;
   if (T % 8 == 0) {          // rows of one tile on one XCD (round-robin dispatch over 8 XCDs)
@@ -195,76 +444,170 @@ __global__ __launch_bounds__(512) void k_dec_down(DecodeArgs a, const uint16_t* 
     t = wg / R;
     r = wg % R;
   }
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int j = __builtin_amdgcn_readfirstlane(tid >> 6);   // slot of this wave, uniform
-  // routed slot j: all its chunks (blocks of 16 when inter > 512); the
-  // wave's share of the shared expert (whole groups, split over k waves) is
-  // loaded together with the first block
-  const uint64_t rsj = (uint64_t)r * (k + 1) + j, rsk = (uint64_t)r * (k + 1) + k;
-  const int e = a.ids[r * k + j];
+  const int tid = threadIdx.x, lane = tid & 63, nthr = blockDim.x;
+  const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = wi / DN_KS, kp = wi % DN_KS;
+  // the slot's expert through the scalar cache (uniform), so that waiting for
+  // it does not wait for the h pieces below
+  const int e = ((const __attribute__((address_space(4))) int32_t*)(a.ids))[r * k + j];
+  // the row's h (hi, lo: (k+1) * Imax halves each) and chunk sums as 16-byte
+  // pieces: HV unconditional register loads per thread (indexes clamped)
+  // issued before the weight loads, stored to LDS once they land; HV == 0
+  // copies them straight into LDS
+  const int nh = (k + 1) * Imax / 8, nc = (k + 1) * Imax / 128;   // pieces of hi / lo, of the sums
+  const uint4* hsrc_h = reinterpret_cast<const uint4*>(a.hhi + (uint64_t)r * (k + 1) * Imax);
+  const uint4* hsrc_l = reinterpret_cast<const uint4*>(a.hlo + (uint64_t)r * (k + 1) * Imax);
+  const uint4* hsrc_c = reinterpret_cast<const uint4*>(a.hc + (uint64_t)r * (k + 1) * (Imax / 32));
+  // three named registers (not an array, which would live in scratch)
+  const int hlast = 2 * nh + nc - 1;
+  auto hpiece = [&](int i) -> uint4 {
+    i = i % (hlast + 1);      // surplus threads re-read other pieces (distinct lines)
+    return *(i < nh ? hsrc_h + i : (i < 2 * nh ? hsrc_l + (i - nh) : hsrc_c + (i - 2 * nh)));
+  };
+  uint4 hv0, hv1, hv2;
+  if constexpr (HV > 0) {
+    hv0 = hpiece(tid);
+    hv1 = hpiece(tid + nthr);
+    hv2 = hpiece(tid + 2 * nthr);
+    asm volatile("" ::: "memory");   // these loads go out before the weight loads
+  } else {
+    const uint4* src[3] = {hsrc_h, hsrc_l, hsrc_c};
+    uint4* dst[3] = {reinterpret_cast<uint4*>(hhl), reinterpret_cast<uint4*>(hll), reinterpret_cast<uint4*>(hcl)};
+    const int np[3] = {nh, nh, nc};
+#pragma unroll
+    for (int part = 0; part < 3; ++part)
+      for (int base = wi * 64; base < np[part]; base += nthr) {
+        if (base + lane < np[part])
+          __builtin_amdgcn_global_load_lds(src[part] + base + lane,
+                                           (__attribute__((address_space(3))) void*)(dst[part] + base), 16, 0, 0);
+      }
+  }
+  // routed slot j, blocks kp, kp + KS, ... of its intermediate axis
   const bool valid = e >= 0 && e < a.E;
-  const uint8_t* rblk = a.base + a.rt.base_off + (uint64_t)(valid ? e : 0) * a.rt.stride;
-  const uint8_t* sblk = a.base + a.sh.base_off;
-  const int gch = Fmt<FS>::G / 32, ngr = (a.sh.inter / 32) / gch, per = (ngr + k - 1) / k;
-  const int g0 = min(ngr, j * per), g1 = min(ngr, g0 + per);
-  const int sc0 = g0 * gch, sn = min(8, (g1 - g0) * gch);
-  const int rn = a.rt.inter / 32;
-  uint32_t wr[16][Fmt<FR>::WORDS], wsh[8][Fmt<FS>::WORDS];
-  dn_load<FR, 16>(rblk + a.rt.dn_codes, a.rt.inter, t, lane, 0, min(16, rn), wr);
-  dn_load<FS, 8>(sblk + a.sh.dn_codes, a.sh.inter, t, lane, sc0, sn, wsh);
-  const uint32_t* hhj = reinterpret_cast<const uint32_t*>(hhi + rsj * a.Imax);
-  const uint32_t* hlj = reinterpret_cast<const uint32_t*>(hlo + rsj * a.Imax);
-  float e_out = dn_dot<FR, 16>(wr, hhj, hlj, hcs + rsj * (a.Imax / 32), rblk + a.rt.dn_scales,
-                               a.rt.inter, t, lane, 0, min(16, rn));
-  for (int cb = 16; cb < rn; cb += 16) {
-    dn_load<FR, 16>(rblk + a.rt.dn_codes, a.rt.inter, t, lane, cb, min(16, rn - cb), wr);
-    e_out += dn_dot<FR, 16>(wr, hhj, hlj, hcs + rsj * (a.Imax / 32), rblk + a.rt.dn_scales,
-                            a.rt.inter, t, lane, cb, min(16, rn - cb));
+  const rsrc_t rr = make_rsrc(a.base + a.rt.base_off + (uint64_t)(valid ? e : 0) * a.rt.stride, a.rt.blk_bytes);
+  const uint32_t rcodes = (uint32_t)a.rt.dn_codes, rscales = (uint32_t)a.rt.dn_scales;
+  const int rnch = a.rt.inter / 32, rnkb = a.rt.inter / KBLK;
+  uint32_t wr[8][Fmt<FR>::WORDS], scr[4];
+  // loads are unconditional (a wave without a block or group of its own
+  // loads a valid one and ignores it) so that the wait counts stay exact
+  const bool has_blk = kp < rnkb;
+  const int kb0 = min(kp, rnkb - 1);
+  load_scales_rs<FR>(rr, scale_voff<FR>(lane), rscales + (uint32_t)sblk_off<FR>(t, kb0, rnkb), scr);
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc)
+    load_chunk_rs<FR>(rr, chunk_voff<FR>(lane), rcodes + (uint32_t)chunk_off<FR>(t, kb0 * 8 + cc, rnch), wr[cc]);
+  // shared expert: groups wi, wi + nwv, ... (first one loaded here)
+  constexpr int SCPG = Fmt<FS>::G / 32;
+  const rsrc_t rs = make_rsrc(a.base + a.sh.base_off, a.sh.blk_bytes);
+  const uint32_t scodes = (uint32_t)a.sh.dn_codes, sscales = (uint32_t)a.sh.dn_scales;
+  const int snch = a.sh.inter / 32, snkb = a.sh.inter / KBLK, sng = a.sh.inter / Fmt<FS>::G;
+  uint32_t wsh[SCPG][Fmt<FS>::WORDS], scs = 0;
+  {
+    const int g0 = min(wi, sng - 1);
+    scs = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)group_word_voff<FS>(g0, lane),
+                                               (int)(sscales + (uint32_t)sblk_off<FS>(t, g0 / (KBLK / Fmt<FS>::G), snkb)), 0);
+#pragma unroll
+    for (int cc = 0; cc < SCPG; ++cc)
+      load_chunk_rs<FS>(rs, chunk_voff<FS>(lane), scodes + (uint32_t)chunk_off<FS>(t, g0 * SCPG + cc, snch), wsh[cc]);
+  }
+  if constexpr (HV > 0) {
+    // hi, lo and the sums are contiguous in LDS as they are in the workspace
+    // surplus threads rewrite a piece with the same bytes
+    uint4* hd = reinterpret_cast<uint4*>(hhl);
+    hd[tid % (hlast + 1)] = hv0;
+    hd[(tid + nthr) % (hlast + 1)] = hv1;
+    hd[(tid + 2 * nthr) % (hlast + 1)] = hv2;
+  }
+  __syncthreads();
+  float e_out = 0.f;
+  if (has_blk) {
+    const uint32_t* hh = hhl + j * (Imax / 2) + kp * (KBLK / 2);
+    const uint32_t* hl = hll + j * (Imax / 2) + kp * (KBLK / 2);
+    e_out = dn_block<FR>(wr, scr, hh, hl, hcl + j * (Imax / 32) + kp * 8, e_out);
+    for (int kb = kp + DN_KS; kb < rnkb; kb += DN_KS) {
+      load_scales_rs<FR>(rr, scale_voff<FR>(lane), rscales + (uint32_t)sblk_off<FR>(t, kb, rnkb), scr);
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc)
+        load_chunk_rs<FR>(rr, chunk_voff<FR>(lane), rcodes + (uint32_t)chunk_off<FR>(t, kb * 8 + cc, rnch), wr[cc]);
+      e_out = dn_block<FR>(wr, scr, hhl + j * (Imax / 2) + kb * (KBLK / 2),
+                           hll + j * (Imax / 2) + kb * (KBLK / 2), hcl + j * (Imax / 32) + kb * 8, e_out);
+    }
   }
   if (!valid) e_out = 0.f;
   float s_out = 0.f;
-  if (sn > 0) {
-    const uint32_t* hhk = reinterpret_cast<const uint32_t*>(hhi + rsk * a.Imax);
-    const uint32_t* hlk = reinterpret_cast<const uint32_t*>(hlo + rsk * a.Imax);
-    s_out = dn_dot<FS, 8>(wsh, hhk, hlk, hcs + rsk * (a.Imax / 32), sblk + a.sh.dn_scales, a.sh.inter,
-                          t, lane, sc0, sn);
-    for (int cb = sc0 + sn; cb < g1 * gch; cb += 8) {
-      const int m = min(8, g1 * gch - cb);
-      dn_load<FS, 8>(sblk + a.sh.dn_codes, a.sh.inter, t, lane, cb, m, wsh);
-      s_out += dn_dot<FS, 8>(wsh, hhk, hlk, hcs + rsk * (a.Imax / 32), sblk + a.sh.dn_scales,
-                             a.sh.inter, t, lane, cb, m);
+  for (int g = wi; g < sng; g += nwv) {
+    if (g != wi) {
+#pragma unroll
+      for (int cc = 0; cc < SCPG; ++cc)
+        load_chunk_rs<FS>(rs, chunk_voff<FS>(lane), scodes + (uint32_t)chunk_off<FS>(t, g * SCPG + cc, snch), wsh[cc]);
+      scs = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)group_word_voff<FS>(g, lane),
+                                                 (int)(sscales + (uint32_t)sblk_off<FS>(t, g / (KBLK / Fmt<FS>::G), snkb)), 0);
     }
+    s_out += dn_group<FS>(wsh, scs, g, hhl + k * (Imax / 2) + g * (Fmt<FS>::G / 2),
+                          hll + k * (Imax / 2) + g * (Fmt<FS>::G / 2), hcl + k * (Imax / 32) + g * SCPG);
   }
-  es[j][lane] = e_out;
-  ps[j][lane] = s_out;
-  if (a.tap_e) a.tap_e[((uint64_t)r * (k + 1) + j) * a.H + 64 * t + lane] = e_out;
+  es[wi * 64 + lane] = e_out;
+  ps[wi * 64 + lane] = s_out;
   __syncthreads();
-  if (j == 0) {
+  if (wi == 0) {
     float sh = 0.f;
-    for (int q = 0; q < k; ++q) sh += ps[q][lane];
-    if (a.tap_e) a.tap_e[((uint64_t)r * (k + 1) + k) * a.H + 64 * t + lane] = sh;
+    for (int q = 0; q < nwv; ++q) sh += ps[q * 64 + lane];
     float y = 0.f;
-    for (int q = 0; q < k; ++q) y = fmaf(a.p[r * k + q], es[q][lane], y);
+    for (int q = 0; q < k; ++q) {
+      float eq = 0.f;
+#pragma unroll
+      for (int p = 0; p < DN_KS; ++p) eq += es[(q * DN_KS + p) * 64 + lane];
+      if (a.tap_e) a.tap_e[((uint64_t)r * (k + 1) + q) * a.H + 64 * t + lane] = eq;
+      y = fmaf(a.p[r * k + q], eq, y);
+    }
+    if (a.tap_e) a.tap_e[((uint64_t)r * (k + 1) + k) * a.H + 64 * t + lane] = sh;
     y = fmaf(a.sg[r], sh, y);
     a.y[(uint64_t)r * a.H + 64 * t + lane] = y;
   }
 }
 
 // ------------------------------------------------------------------ launch
+constexpr int GU_GRID = 256;   // persistent gate/up workgroups (a multiple of 8)
+
+size_t decode_gu_smem(int R, int H) {
+  return (size_t)R * H * 2 + (size_t)R * (H / 32) * 4 + 2 * (size_t)std::min(8, H / KBLK) * 64 * 4;
+}
+size_t decode_dn_smem(int k, int Imax) {
+  return (size_t)(k + 1) * Imax * 2 * 2 + (size_t)(k + 1) * (Imax / 32) * 4 + 2 * (size_t)k * DN_KS * 64 * 4;
+}
+
+template <typename K>
+static hipError_t allow_smem(K kern, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+template <int FR, int FS, int ACT16>
+static hipError_t launch_gateup(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev, int nw, size_t gsm) {
+  hipError_t err;
+  if (a.R * a.H / 8 <= 4 * 64 * nw) {
+    if ((err = allow_smem(k_dec_gateup<FR, FS, ACT16, 4>, gsm)) != hipSuccess) return err;
+    launch_k(k_dec_gateup<FR, FS, ACT16, 4>, dim3(GU_GRID), dim3(64 * nw), (uint32_t)gsm, s, ev, 0, a);
+  } else {
+    if ((err = allow_smem(k_dec_gateup<FR, FS, ACT16, 0>, gsm)) != hipSuccess) return err;
+    launch_k(k_dec_gateup<FR, FS, ACT16, 0>, dim3(GU_GRID), dim3(64 * nw), (uint32_t)gsm, s, ev, 0, a);
+  }
+  return hipGetLastError();
+}
+
 template <int FR, int FS>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
-  const int nw = min(8, a.H / KBLK);
-  const int units = a.R * a.k + a.R;
-  const int gu_tiles = 2 * a.Imax / 64;
-  const size_t smem = (size_t)nw * 64 * 4 + (size_t)nw * 512;
-  if (a.act_fp16)
-    launch_k(k_dec_gateup<FR, FS, 1>, dim3(gu_tiles, units), dim3(64 * nw), smem, s, ev, 0, a, a.x);
-  else
-    launch_k(k_dec_gateup<FR, FS, 0>, dim3(gu_tiles, units), dim3(64 * nw), smem, s, ev, 0, a, a.x);
-  hipError_t err = hipGetLastError();
+  const int nw = std::min(8, a.H / KBLK);
+  const size_t gsm = decode_gu_smem(a.R, a.H), dsm = decode_dn_smem(a.k, a.Imax);
+  hipError_t err = a.act_fp16 ? launch_gateup<FR, FS, 1>(a, s, ev, nw, gsm) : launch_gateup<FR, FS, 0>(a, s, ev, nw, gsm);
   if (err != hipSuccess) return err;
-  launch_k(k_dec_down<FR, FS>, dim3((a.H / 64) * a.R), dim3(64 * a.k), 0, s, ev, 2, a,
-           (const uint16_t*)a.hhi, (const uint16_t*)a.hlo, (const float*)a.hc);
+  const int dthr = 64 * a.k * DN_KS;
+  const int hpieces = (a.k + 1) * a.Imax / 4 + (a.k + 1) * a.Imax / 128;
+  if (hpieces <= 3 * dthr)
+    launch_k(k_dec_down<FR, FS, 3>, dim3((a.H / 64) * a.R), dim3(dthr), (uint32_t)dsm, s, ev, 2, a);
+  else
+    launch_k(k_dec_down<FR, FS, 0>, dim3((a.H / 64) * a.R), dim3(dthr), (uint32_t)dsm, s, ev, 2, a);
   return hipGetLastError();
 }
 

@@ -147,6 +147,48 @@ template <> __device__ __forceinline__ void load_chunk<F_Q8>(const uint8_t* blk,
   w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
+// Buffer resource of one byte range (an expert block, a router): loads
+// through it take a per-lane offset in a VGPR and a uniform offset in an
+// SGPR, and return 0 instead of touching memory past `bytes`.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // GFX9 raw buffer: stride 0, num_records in bytes, 32-bit data format word
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One lane's chunk words: voff = lane * CB (per lane), soff = byte offset of
+// the chunk block inside the range (uniform).
+template <int F> __device__ __forceinline__ void load_chunk_rs(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w) {
+  if constexpr (F == F_Q3) {
+    const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)voff, (int)soff, 0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z;
+  } else if constexpr (F == F_Q8) {
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff / 2), (int)soff, 0);
+    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff / 2), (int)(soff + 64 * 16), 0);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+}
+// One lane's scale words of a 256-wide block (see load_scales): voff = lane *
+// (256/G) * SCB, soff = byte offset of the scale block inside the range.
+template <int F> __device__ __forceinline__ void load_scales_rs(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* sc) {
+  if constexpr (Fmt<F>::AFF) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+  } else {
+    sc[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+  }
+}
+template <int F> __device__ __forceinline__ uint32_t chunk_voff(int lane) { return (uint32_t)lane * Fmt<F>::CB; }
+template <int F> __device__ __forceinline__ uint32_t scale_voff(int lane) {
+  return (uint32_t)lane * (KBLK / Fmt<F>::G) * Fmt<F>::SCB;
+}
+
 // Byte offset of chunk c of tile t (K/32 chunks per row).
 template <int F> __device__ __forceinline__ uint64_t chunk_off(int t, int c, int nchunks) {
   return ((uint64_t)t * nchunks + c) * (uint64_t)(64 * Fmt<F>::CB);
@@ -154,22 +196,6 @@ template <int F> __device__ __forceinline__ uint64_t chunk_off(int t, int c, int
 // Byte offset of the scale block kb of tile t (K/256 blocks per row).
 template <int F> __device__ __forceinline__ uint64_t sblk_off(int t, int kb, int nkb) {
   return ((uint64_t)t * nkb + kb) * (uint64_t)(64 * (KBLK / Fmt<F>::G) * Fmt<F>::SCB);
-}
-
-// Multiplier M*s and offset (b - M s) of one group for one lane.
-template <int F> __device__ __forceinline__ void group_coef(const uint8_t* sblk, int lane, int gi,
-                                                            float& ms, float& bm) {
-  if constexpr (Fmt<F>::AFF) {
-    const uint32_t v = reinterpret_cast<const uint32_t*>(sblk)[lane * (KBLK / Fmt<F>::G) + gi];
-    const float s = bf16_to_f(v & 0xFFFFu), b = bf16_to_f(v >> 16);
-    ms = (float)Fmt<F>::M * s;
-    bm = b - ms;
-  } else {
-    const uint16_t v = reinterpret_cast<const uint16_t*>(sblk)[lane * (KBLK / Fmt<F>::G) + gi];
-    const float s = f16_bits_to_f(v);
-    ms = (float)Fmt<F>::M * s;
-    bm = -8.0f * s - ms;       // symmetric: w = s*(u - 8)
-  }
 }
 
 // sum over the 16 pairs of a chunk: acc += v_p . a_p (fixed order p = 0..15)
@@ -236,23 +262,6 @@ __device__ __forceinline__ float dot_chunk_h(const uint32_t* v, const uint32_t* 
   return acc;
 }
 
-// Activations and h do not change while a kernel reads them: reading them
-// through the constant address space lets uniform addresses become scalar
-// loads into SGPRs.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(4))) u32x4* cu32x4_p;
-typedef const __attribute__((address_space(4))) float* cfloat_p;
-
-// 16 uint32 activation pairs of one chunk; every lane reads the same address
-__device__ __forceinline__ void load_pairs(const uint16_t* p, uint32_t* o) {
-  const cu32x4_p q = (cu32x4_p)(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4 v = q[i];
-    o[4 * i] = v.x; o[4 * i + 1] = v.y; o[4 * i + 2] = v.z; o[4 * i + 3] = v.w;
-  }
-}
-
 // ------------------------------------------------------------- DPP moves
 // VALU-only lane moves (no LDS round trip). dpp_ctrl codes of the GCN/CDNA
 // DPP encoding: quad_perm(1,0,3,2) = 0xB1, quad_perm(2,3,0,1) = 0x4E,
@@ -278,19 +287,6 @@ __device__ __forceinline__ float sum16(float s) {
   s = sum8(s);
   s += dpp_f<0x140>(s);
   return s;
-}
-
-// Sum of 4 consecutive activations per lane, then over aligned groups of 8
-// lanes: lane 8c then holds the sum of chunk c of a 256-wide slice (all 8
-// lanes of a group hold the same bits). Fixed order.
-template <int ACT16>
-__device__ __forceinline__ float slice_chunk_sums(const uint16_t* xs, int lane) {
-  const uint2 v = *reinterpret_cast<const uint2*>(xs + 4 * lane);
-  float s = act_to_f((uint16_t)(v.x & 0xFFFFu), ACT16);
-  s += act_to_f((uint16_t)(v.x >> 16), ACT16);
-  s += act_to_f((uint16_t)(v.y & 0xFFFFu), ACT16);
-  s += act_to_f((uint16_t)(v.y >> 16), ACT16);
-  return sum8(s);
 }
 
 // Order-preserving key of a logit for the pick: NaN above +inf above every
@@ -356,18 +352,95 @@ __device__ __forceinline__ void wave_best(float& v, int& id) {
   id = bi;
 }
 
+// Lane's scale words of one 256-wide K block, loaded ahead of use: affine
+// formats 4 u32 (bf16 s | bf16 b << 16, one per group of 64), symmetric one
+// u32 (two fp16 scales, groups of 128).
+template <int F> __device__ __forceinline__ void load_scales(const uint8_t* sblk, int lane, uint32_t* sc) {
+  if constexpr (Fmt<F>::AFF) {
+    const uint4 v = *reinterpret_cast<const uint4*>(sblk + lane * 16);
+    sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+  } else {
+    sc[0] = *reinterpret_cast<const uint32_t*>(sblk + lane * 4);
+  }
+}
+// Multiplier M*s and offset (b - M s) of group gi of a block from its words.
+template <int F> __device__ __forceinline__ void coef_reg(const uint32_t* sc, int gi, float& ms, float& bm) {
+  if constexpr (Fmt<F>::AFF) {
+    const uint32_t v = sc[gi];
+    const float s = bf16_to_f(v & 0xFFFFu), b = bf16_to_f(v >> 16);
+    ms = (float)Fmt<F>::M * s;
+    bm = b - ms;
+  } else {
+    const float s = f16_bits_to_f((sc[0] >> (16 * gi)) & 0xFFFFu);
+    ms = (float)Fmt<F>::M * s;
+    bm = -8.0f * s - ms;       // symmetric: w = s*(u - 8)
+  }
+}
+
+// Sum of a lane's 4 consecutive activations (fixed order).
+template <int ACT16> __device__ __forceinline__ float sum4(uint2 v) {
+  float s = act_to_f((uint16_t)(v.x & 0xFFFFu), ACT16);
+  s += act_to_f((uint16_t)(v.x >> 16), ACT16);
+  s += act_to_f((uint16_t)(v.y & 0xFFFFu), ACT16);
+  s += act_to_f((uint16_t)(v.y >> 16), ACT16);
+  return s;
+}
+
+// One group of one row: acc = sum over the group's chunks of the pair dots
+// (chunks in K order, pairs in order), then out = fma(M s, acc, out),
+// out = fma(b - M s, X, out) with X the group's activation sum (8-bit codes
+// with bf16 activations: two nibble sets). v: the unpacked pairs of the
+// group's chunks, a: pointer to the row's activation pairs of the first
+// chunk (16 u32 per chunk), X: the group's chunk sums added in order.
+template <int F, int ACT16, int CPG>
+__device__ __forceinline__ float group_dot(const uint32_t (*v)[F == F_Q8 ? 32 : 16], const uint32_t* a,
+                                           float X, float ms, float bm, float out) {
+  float acc = 0.f, acc2 = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < CPG; ++cc) {
+    uint32_t av[16];
+    const uint4* q = reinterpret_cast<const uint4*>(a + 16 * cc);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 t = q[u];
+      av[4 * u] = t.x; av[4 * u + 1] = t.y; av[4 * u + 2] = t.z; av[4 * u + 3] = t.w;
+    }
+    if constexpr (ACT16) {
+      acc = dot_chunk_h(v[cc], av, acc);
+    } else {
+      acc = dot_chunk_bf(v[cc], av, acc);
+      if constexpr (F == F_Q8) acc2 = dot_chunk_bf(v[cc] + 16, av, acc2);
+    }
+  }
+  if constexpr (F == F_Q8 && !ACT16) {
+    // q = lo + 16 hi: s*sum(q a) + b*X = 16s*A_lo + 256s*A_hi + (b - 272 s)*X
+    const float s = ms * (1.0f / 256.0f), b = bm + ms;
+    out = fmaf(16.0f * s, acc, out);
+    out = fmaf(256.0f * s, acc2, out);
+    return fmaf(b - 272.0f * s, X, out);
+  }
+  out = fmaf(ms, acc, out);
+  return fmaf(bm, X, out);
+}
+
+// unpack of one chunk in the pair format the activations need
+template <int F, int ACT16>
+__device__ __forceinline__ void unpack_for(const uint32_t* w, uint32_t* v) {
+  if constexpr (ACT16) unpack_chunk<F>(w, v); else unpack_chunk_bf<F>(w, v);
+}
+
 // One wave, one 256-wide K slice: for up to NR activation rows, the dot of
 // each lane's weight row with the row's slice. w: the lane's 8 chunks of
-// codes; sblk: the slice's scale block; xs[i]: global slice base of row i;
-// lx: this wave's LDS staging area (NR x 512 bytes). Each lane loads 4
-// activations of a row (coalesced), writes them to LDS and sums them; the
-// dot then reads each chunk's 16 pairs back as a broadcast. Only this wave
-// touches lx, and LDS serves one wave's operations in order, so no barrier.
-// Per group: (M s) * sum(v a) + (b - M s) * X (8-bit: two nibble sets).
+// codes; sc: the slice's scale words (load_scales); xv[i]: the lane's 4
+// activations of row i's slice (lane l holds elements 4l..4l+3), loaded by
+// the caller; lx: this wave's LDS staging area (NR x 512 bytes). Each lane
+// writes its activations to LDS and sums them; the dot then reads each
+// chunk's 16 pairs back as a broadcast. Only this wave touches lx, and LDS
+// serves one wave's operations in order, so no barrier. Chunk sums: 4
+// consecutive activations per lane, then over aligned groups of 8 lanes.
 template <int F, int NR, int ACT16>
-__device__ __forceinline__ void slice_dot(const uint32_t (&w)[8][Fmt<F>::WORDS], const uint8_t* sblk,
-                                          int lane, const uint16_t* const* xs, int nr, uint32_t* lx,
-                                          float* out) {
+__device__ __forceinline__ void slice_dot(const uint32_t (&w)[8][Fmt<F>::WORDS], const uint32_t* sc,
+                                          int lane, const uint2* xv, int nr, uint32_t* lx, float* out) {
   constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
   float csum[NR];
 #pragma unroll
@@ -375,65 +448,93 @@ __device__ __forceinline__ void slice_dot(const uint32_t (&w)[8][Fmt<F>::WORDS],
     out[i] = 0.f;
     csum[i] = 0.f;
     if (i < nr) {
-      const uint2 v = *reinterpret_cast<const uint2*>(xs[i] + 4 * lane);
-      reinterpret_cast<uint2*>(lx + i * 128)[lane] = v;
-      float sm = act_to_f((uint16_t)(v.x & 0xFFFFu), ACT16);
-      sm += act_to_f((uint16_t)(v.x >> 16), ACT16);
-      sm += act_to_f((uint16_t)(v.y & 0xFFFFu), ACT16);
-      sm += act_to_f((uint16_t)(v.y >> 16), ACT16);
-      csum[i] = sum8(sm);
+      reinterpret_cast<uint2*>(lx + i * 128)[lane] = xv[i];
+      csum[i] = sum8(sum4<ACT16>(xv[i]));
     }
   }
 #pragma unroll
   for (int gi = 0; gi < GPS; ++gi) {
     float ms, bm;
-    group_coef<F>(sblk, lane, gi, ms, bm);
-    float acc[NR], acc2[NR], X[NR];
+    coef_reg<F>(sc, gi, ms, bm);
+    uint32_t v[CPG][F == F_Q8 ? 32 : 16];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) acc[i] = acc2[i] = X[i] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < CPG; ++cc) {
-      const int c = gi * CPG + cc;
-      uint32_t v[F == F_Q8 ? 32 : 16];
-      if constexpr (ACT16) unpack_chunk<F>(w[c], v); else unpack_chunk_bf<F>(w[c], v);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if (i < nr) {
-          uint32_t a[16];
-          const uint4* q = reinterpret_cast<const uint4*>(lx + i * 128 + 16 * c);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint4 t = q[u];
-            a[4 * u] = t.x; a[4 * u + 1] = t.y; a[4 * u + 2] = t.z; a[4 * u + 3] = t.w;
-          }
-          if constexpr (ACT16) {
-            acc[i] = dot_chunk_h(v, a, acc[i]);
-          } else {
-            acc[i] = dot_chunk_bf(v, a, acc[i]);
-            if constexpr (F == F_Q8) acc2[i] = dot_chunk_bf(v + 16, a, acc2[i]);
-          }
-          X[i] += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(csum[i]), 8 * c));
-        }
-      }
-    }
+    for (int cc = 0; cc < CPG; ++cc) unpack_for<F, ACT16>(w[gi * CPG + cc], v[cc]);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       if (i < nr) {
-        if constexpr (F == F_Q8) {
-          if constexpr (!ACT16) {
-            // q = lo + 16 hi: s*sum(q a) + b*X = 16s*A_lo + 256s*A_hi + (b - 272 s)*X
-            const float s = ms * (1.0f / 256.0f), b = bm + ms;
-            out[i] = fmaf(16.0f * s, acc[i], out[i]);
-            out[i] = fmaf(256.0f * s, acc2[i], out[i]);
-            out[i] = fmaf(b - 272.0f * s, X[i], out[i]);
-            continue;
-          }
-        }
-        out[i] = fmaf(ms, acc[i], out[i]);
-        out[i] = fmaf(bm, X[i], out[i]);
+        float X = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CPG; ++cc)
+          X += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(csum[i]), 8 * (gi * CPG + cc)));
+        out[i] = group_dot<F, ACT16, CPG>(v, lx + i * 128 + 16 * gi * CPG, X, ms, bm, out[i]);
       }
     }
   }
+}
+
+// The k best of up to 256 candidates held by one wave (lane l holds
+// candidates l + 64 i, i = 0..3, with their order keys; key 0 = absent),
+// ranked by (key desc, id asc). Every lane must be active. Steps:
+//  1. T = the k-th largest key, bit by bit from the top: a bit stays set when
+//     at least k keys are >= the prefix with it (one ballot per candidate
+//     column and bit);
+//  2. the picks are every key > T plus the lowest ids among the keys == T;
+//  3. they are compacted in id order into the wave's LDS scratch (8 entries)
+//     and lane j < k reads entry j, then takes its slot from the other
+//     picks' keys and ids.
+// On return lane j < k holds slot s_j (distinct, 0..k-1) with its id and
+// value; lanes >= k hold slot k.
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[4], const float (&val)[4], int lane, int k,
+                                          uint32_t* scratch /* wave-private LDS, 24 u32 */, int& slot,
+                                          int& id, float& v) {
+  uint32_t T = 0;
+#pragma unroll 4
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    T = cnt >= k ? c : T;
+  }
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int need = k, before = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) need -= __popcll(__ballot(key[i] > T));
+  bool sel[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t eq = __ballot(key[i] == T);
+    const int tie_rank = before + __popcll(eq & lt);
+    sel[i] = key[i] > T || (key[i] == T && tie_rank < need);
+    before += __popcll(eq);
+  }
+  int pos = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t sm = __ballot(sel[i]);
+    if (sel[i]) {
+      const int p = pos + __popcll(sm & lt);
+      scratch[p] = key[i];
+      scratch[8 + p] = (uint32_t)(lane + 64 * i);
+      scratch[16 + p] = __float_as_uint(val[i]);
+    }
+    pos += __popcll(sm);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int e = lane < k ? lane : 0;
+  const uint32_t mk = scratch[e];
+  id = (int)scratch[8 + e];
+  v = __uint_as_float(scratch[16 + e]);
+  int s = 0;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    if (m < k) {
+      const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)mk, m);
+      const int im = __builtin_amdgcn_readlane(id, m);
+      s += (km > mk || (km == mk && im < id)) ? 1 : 0;
+    }
+  }
+  slot = lane < k ? s : k;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

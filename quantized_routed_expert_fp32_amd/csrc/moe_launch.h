@@ -23,7 +23,8 @@ struct RouteArgs {
 // Offsets of one expert class (routed or shared) inside the packed layer.
 struct ExpertClass {
   uint64_t base_off, stride;          // expert e at base_off + e*stride
-  uint64_t gu_codes, gu_scales, dn_codes, dn_scales;
+  uint64_t gu_codes, gu_scales, dn_codes, dn_scales;   // inside an expert block
+  uint32_t blk_bytes;                 // bytes of one expert block
   int inter;
 };
 

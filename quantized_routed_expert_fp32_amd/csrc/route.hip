@@ -3,19 +3,27 @@
 // ("qwen3_5_moe on native CUDA with 3-bit routed experts #803", Activity,
 // comment "Progress on the 4-bit gate").
 //
-// The logits are spread over the chip: one workgroup per (tile of 64
-// experts, row), lanes owning router rows exactly as the expert kernels own
-// weight rows, activations through scalar loads. The last tile workgroup of
-// a row picks the top k as k rounds of a wave-wide arg-max under the total
-// order (NaN, value desc, id asc) built from DPP moves, then forms
-// exp(l - l_top) / sum and sigmoid(gate).
+// Logits: one workgroup per (tile of 64 experts, group of NR rows); lanes
+// own router rows exactly as the expert kernels own weight rows, wave w sums
+// the K slices w, w + nw, ... and the waves are added in wave order.
+// Pick (wave_topk): a bit-by-bit search for the k-th largest order key
+// (NaN above +inf above every finite logit), the keys above it plus the
+// lowest ids among its ties, slots by (key desc, id asc); then
+// exp(l - l_top) / sum in slot order and sigmoid of the gate logit.
+//  * decode batches (k_route): one launch; the logits go out with
+//    write-through stores, and the last of a row's tile workgroups to arrive
+//    (a per-row counter in the workspace, reset by that workgroup) picks.
+//  * prompt chunks (k_route_logits + k_route_pick): NR = 8 rows per logits
+//    workgroup, then one wave per row picks in a second launch.
+// Each row's arithmetic is the same whatever NR and the other rows are, so
+// picks and weights of a row do not depend on the batch.
 #include "moe_kernels.h"
 #include "moe_launch.h"
 #include "moe_dispatch.h"
 
 namespace moe {
 
-// gate-row logit part of one lane (chunks lane, lane+64, ...), before the
+// Gate-row logit part of one lane (chunks lane, lane+64, ...), before the
 // wave sum. The row is stored as one tile row: chunk c at c * CB bytes.
 template <int FG, int ACT16>
 __device__ __forceinline__ float gate_row_part(const RouteArgs& a, const uint16_t* xr, int lane) {
@@ -92,110 +100,67 @@ __device__ __forceinline__ float gate_row_part(const RouteArgs& a, const uint16_
   return part;
 }
 
-// One workgroup per (tile of 64 experts, row); wave w sums the slices
-// w, w + nw, ... in ascending order, the waves are added in wave order. The
-// last of a row's tile workgroups to finish (a per-row arrival counter in the
-// workspace, reset by that workgroup) picks the row's top k.
-template <int FR, int FG, int ACT16>
-__global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __restrict__ x) {
-  __shared__ float red[8][64];
-  __shared__ int s_last;
-  __shared__ __align__(16) uint32_t lxs[8][128];    // per-wave activation slice
-  const int H = a.H, E = a.E, k = a.k, nsl = H / KBLK, nch = H / 32;
-  const int t = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+// Logits of NR rows for one tile of 64 experts. Wave w sums the K slices
+// w, w + nw, ... in ascending order; the waves are added in wave order.
+template <int FR, int ACT16, int NR>
+__global__ __launch_bounds__(512) void k_route_logits(RouteArgs a, const uint16_t* __restrict__ x) {
+  __shared__ float red[8][NR][64];
+  __shared__ __align__(16) uint32_t lxs[8][NR * 128];    // per-wave activation slices
+  const int H = a.H, E = a.E, nsl = H / KBLK, nch = H / 32;
+  const int t = blockIdx.x, r0 = blockIdx.y * NR, tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
-  const int nw = blockDim.x >> 6, ntile = E / 64;
-  const uint16_t* xr = x + (uint64_t)row * H;
+  const int nw = blockDim.x >> 6;
+  const int nr = min(NR, a.R - r0);
   const uint8_t* rc = a.base + a.r_off;
   const uint8_t* rs = a.base + a.r_soff;
-  float gpart = 0.f;
-  const bool gate_job = (t == 0 && w == nw - 1);
-  if (gate_job) gpart = gate_row_part<FG, ACT16>(a, xr, lane);
-  float out = 0.f;
+  float out[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) out[i] = 0.f;
   for (int sl = w; sl < nsl; sl += nw) {
-    uint32_t wc[8][Fmt<FR>::WORDS];
+    // activations first, then codes and scale words: the wait for the
+    // activations does not wait for the larger code loads
+    uint2 xv[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      xv[i] = *reinterpret_cast<const uint2*>(x + (uint64_t)(r0 + min(i, nr - 1)) * H + sl * KBLK + 4 * lane);
+    uint32_t wc[8][Fmt<FR>::WORDS], sc[4];
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) load_chunk<FR>(rc + chunk_off<FR>(t, sl * 8 + cc, nch), lane, wc[cc]);
-    const uint16_t* xs[1] = {xr + sl * KBLK};
-    float part[1];
-    slice_dot<FR, 1, ACT16>(wc, rs + sblk_off<FR>(t, sl, nsl), lane, xs, 1, lxs[w], part);
-    out += part[0];
+    load_scales<FR>(rs + sblk_off<FR>(t, sl, nsl), lane, sc);
+    float part[NR];
+    slice_dot<FR, NR, ACT16>(wc, sc, lane, xv, nr, lxs[w], part);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) out[i] += part[i];
   }
-  red[w][lane] = out;
-  if (gate_job) {
-    // wave sum of the gate-row parts: 16-lane rows by DPP, then the 4 rows in order
-    const float s16 = sum16(gpart);
-    float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 0));
-    c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 16));
-    c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 32));
-    c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 48));
-    if (lane == 0) a.gl_ws[row] = c;
-  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) red[w][i][lane] = out[i];
   __syncthreads();
-  if (w == 0) {
+  // wave i sums row i (rows beyond nw: waves take several)
+  for (int i = w; i < nr; i += nw) {
     float l = 0.f;
-    for (int q = 0; q < nw; ++q) l += red[q][lane];
-    a.lg_ws[(uint64_t)row * E + 64 * t + lane] = l;
+    for (int q = 0; q < nw; ++q) l += red[q][i][lane];
+    a.lg_ws[(uint64_t)(r0 + i) * E + 64 * t + lane] = l;
   }
-  __threadfence();                         // logits visible device-wide before the arrival
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = atomicAdd(&a.cnt[row], 1u);
-    s_last = old == (unsigned)(ntile - 1);
-    if (s_last) a.cnt[row] = 0u;           // every tile of this row has arrived
+}
+
+// Top k of one row from its keys and values (lane l: experts l + 64 i),
+// then weights exp(l_j - l_top) / sum over the k picks in slot order, and
+// sigmoid of the gate logit c. One wave.
+__device__ __forceinline__ void pick_and_store(const RouteArgs& a, int row, const uint32_t (&key)[4],
+                                               const float (&v)[4], float c, int lane, uint32_t* scr) {
+  const int k = a.k;
+  int slot, id;
+  float val;
+  wave_topk(key, v, lane, k, scr, slot, id, val);
+  // into slot order
+  if (lane < k) {
+    scr[slot] = (uint32_t)id;
+    scr[8 + slot] = __float_as_uint(val);
   }
-  __syncthreads();
-  if (!s_last || w != 0) return;
-  __threadfence();
-  // wave 0 of the last tile workgroup: the pick
-  float v[4], bias[4], lv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = min(lane + 64 * i, E - 1);
-    lv[i] = __hip_atomic_load(&a.lg_ws[(uint64_t)row * E + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bias[i] = a.bias ? a.bias[e] : 0.f;
-  }
-  const float c = __hip_atomic_load(&a.gl_ws[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // candidates of this lane: experts lane + 64 i; key 0 marks taken/absent
-  uint32_t key[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = a.bias ? lv[i] + bias[i] : lv[i];
-    key[i] = e < E ? pick_key(v[i]) : 0u;
-  }
-  if (a.logits) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) a.logits[(uint64_t)row * (E + 1) + lane + 64 * i] = v[i];
-    if (lane == 0) a.logits[(uint64_t)row * (E + 1) + E] = c;
-  }
-  // k rounds (fully unrolled, k <= 8): the wave-wide largest key, ties to the
-  // lowest id; lane j keeps the j-th pick
-  float my_v = 0.f, top = 0.f;
-  int my_i = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < k) {
-      const uint32_t bk = max(max(key[0], key[1]), max(key[2], key[3]));
-      const uint32_t m = wave_max_u32(bk);
-      // lowest id holding the best key (ids lane + 64 i grow with i)
-      uint32_t cid = 0xFFFFFFFFu;
-#pragma unroll
-      for (int i = 3; i >= 0; --i) cid = key[i] == m ? (uint32_t)(lane + 64 * i) : cid;
-      const int bi = (int)wave_min_u32(cid);
-      float bv = v[0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) bv = (bi == lane + 64 * i) ? v[i] : bv;
-      bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), bi & 63));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) key[i] = (bi == lane + 64 * i) ? 0u : key[i];
-      if (j == 0) top = bv;
-      my_v = lane == j ? bv : my_v;
-      my_i = lane == j ? bi : my_i;
-    }
-  }
-  // weights exp(l_j - l_top) / sum over the k picks, summed in pick order
+  __builtin_amdgcn_wave_barrier();
+  const int my_i = (int)scr[lane < k ? lane : 0];
+  const float my_v = __uint_as_float(scr[8 + (lane < k ? lane : 0)]);
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
   const float ex = expf(my_v - top);
   float S = 0.f;
 #pragma unroll
@@ -208,32 +173,156 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
   if (lane == 0) a.sg[row] = 1.0f / (1.0f + expf(-c));
 }
 
-template <int FR, int FG>
+// Decode batches: logits of one (tile of 64 experts, row) workgroup go to
+// the workspace with write-through stores (visible device-wide once the
+// store has completed); each wave waits for its stores, then one thread
+// counts the row's arrivals; the last tile workgroup reads the row back
+// (loads that bypass this XCD's L2) and picks. Tile 0's last wave also
+// forms the gate-row logit.
+template <int FR, int FG, int ACT16>
+__global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __restrict__ x) {
+  __shared__ float red[8][64];
+  __shared__ __align__(16) uint32_t lxs[8][128];
+  __shared__ uint32_t scr[24];
+  __shared__ int s_last;
+  const int H = a.H, E = a.E, nsl = H / KBLK, nch = H / 32, ntile = E / 64;
+  const int t = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = blockDim.x >> 6;
+  const uint16_t* xr = x + (uint64_t)row * H;
+  const uint8_t* rc = a.base + a.r_off;
+  const uint8_t* rs = a.base + a.r_soff;
+  float out = 0.f;
+  for (int sl = w; sl < nsl; sl += nw) {
+    uint2 xv[1];
+    xv[0] = *reinterpret_cast<const uint2*>(xr + sl * KBLK + 4 * lane);
+    uint32_t wc[8][Fmt<FR>::WORDS], sc[4];
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) load_chunk<FR>(rc + chunk_off<FR>(t, sl * 8 + cc, nch), lane, wc[cc]);
+    load_scales<FR>(rs + sblk_off<FR>(t, sl, nsl), lane, sc);
+    float part[1];
+    slice_dot<FR, 1, ACT16>(wc, sc, lane, xv, 1, lxs[w], part);
+    out += part[0];
+  }
+  red[w][lane] = out;
+  if (t == 0 && w == nw - 1) {
+    const float s16 = sum16(gate_row_part<FG, ACT16>(a, xr, lane));
+    float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 0));
+    c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 16));
+    c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 32));
+    c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 48));
+    if (lane == 0) __hip_atomic_store(&a.gl_ws[row], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (w == 0) {
+    float l = 0.f;
+    for (int q = 0; q < nw; ++q) l += red[q][lane];
+    __hip_atomic_store(&a.lg_ws[(uint64_t)row * E + 64 * t + lane], l, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __hip_atomic_fetch_add(&a.cnt[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == (unsigned)(ntile - 1);
+    if (s_last) __hip_atomic_store(&a.cnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last || w != 0) return;
+  float v[4];
+  uint32_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    const int ec = min(e, E - 1);
+    const float l = __hip_atomic_load(&a.lg_ws[(uint64_t)row * E + ec], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v[i] = a.bias ? l + a.bias[ec] : l;
+    key[i] = e < E ? pick_key(v[i]) : 0u;
+  }
+  const float c = __hip_atomic_load(&a.gl_ws[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (a.logits) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) a.logits[(uint64_t)row * (E + 1) + lane + 64 * i] = v[i];
+    if (lane == 0) a.logits[(uint64_t)row * (E + 1) + E] = c;
+  }
+  pick_and_store(a, row, key, v, c, lane, scr);
+}
+
+// One wave per row: gate-row logit, top k, weights, sigmoid gate.
+template <int FG, int ACT16>
+__global__ __launch_bounds__(256) void k_route_pick(RouteArgs a, const uint16_t* __restrict__ x) {
+  const int E = a.E, k = a.k;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + wv;
+  __shared__ uint32_t scratch[4][24];
+  uint32_t* scr = scratch[wv];
+  if (row >= a.R) return;
+  float v[4];
+  uint32_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    const int ec = min(e, E - 1);
+    const float l = a.lg_ws[(uint64_t)row * E + ec];
+    v[i] = a.bias ? l + a.bias[ec] : l;
+    key[i] = e < E ? pick_key(v[i]) : 0u;     // key 0 marks taken / absent
+  }
+  // gate-row logit: lane parts, 16-lane rows by DPP, then the 4 rows in order
+  const float s16 = sum16(gate_row_part<FG, ACT16>(a, x + (uint64_t)row * a.H, lane));
+  float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 0));
+  c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 16));
+  c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 32));
+  c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 48));
+  if (a.logits) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) a.logits[(uint64_t)row * (E + 1) + lane + 64 * i] = v[i];
+    if (lane == 0) a.logits[(uint64_t)row * (E + 1) + E] = c;
+  }
+  pick_and_store(a, row, key, v, c, lane, scr);
+}
+
+// decode batches up to this many rows take the one-launch router
+constexpr int ROUTE_FUSED_MAX_ROWS = 32;
+
+template <int FR, int FG, int ACT16>
 static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
   const int nw = min(8, a.H / KBLK);
-  if (a.act_fp16)
-    launch_k(k_route<FR, FG, 1>, dim3(a.E / 64, a.R), dim3(64 * nw), 0, s, ev, 0, a, a.x);
-  else
-    launch_k(k_route<FR, FG, 0>, dim3(a.E / 64, a.R), dim3(64 * nw), 0, s, ev, 0, a, a.x);
+  if (a.R <= ROUTE_FUSED_MAX_ROWS) {
+    launch_k(k_route<FR, FG, ACT16>, dim3(a.E / 64, a.R), dim3(64 * nw), 0, s, ev, 0, a, a.x);
+    return hipGetLastError();
+  }
+  hipEvent_t e0[2] = {ev ? ev[0] : nullptr, nullptr}, e1[2] = {nullptr, ev ? ev[1] : nullptr};
+  launch_k(k_route_logits<FR, ACT16, 8>, dim3(a.E / 64, (a.R + 7) / 8), dim3(64 * nw), 0, s, e0, 0, a, a.x);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  launch_k(k_route_pick<FG, ACT16>, dim3((a.R + 3) / 4), dim3(256), 0, s, e1, 0, a, a.x);
   return hipGetLastError();
 }
 
-template <int FR>
+template <int FR, int ACT16>
 static hipError_t launch_route_g(int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
   switch (fg) {
-    case F_Q4: return launch_route_t<FR, F_Q4>(a, s, ev);
-    case F_Q8: return launch_route_t<FR, F_Q8>(a, s, ev);
-    case F_S4: return launch_route_t<FR, F_S4>(a, s, ev);
-    case F_DENSE: return launch_route_t<FR, F_DENSE>(a, s, ev);
+    case F_Q4: return launch_route_t<FR, F_Q4, ACT16>(a, s, ev);
+    case F_Q8: return launch_route_t<FR, F_Q8, ACT16>(a, s, ev);
+    case F_S4: return launch_route_t<FR, F_S4, ACT16>(a, s, ev);
+    case F_DENSE: return launch_route_t<FR, F_DENSE, ACT16>(a, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
+template <int FR>
+static hipError_t launch_route_a(int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
+  return a.act_fp16 ? launch_route_g<FR, 1>(fg, a, s, ev) : launch_route_g<FR, 0>(fg, a, s, ev);
+}
+
 hipError_t launch_route(int fr, int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
   switch (fr) {
-    case F_Q4: return launch_route_g<F_Q4>(fg, a, s, ev);
-    case F_Q8: return launch_route_g<F_Q8>(fg, a, s, ev);
-    case F_S4: return launch_route_g<F_S4>(fg, a, s, ev);
+    case F_Q4: return launch_route_a<F_Q4>(fg, a, s, ev);
+    case F_Q8: return launch_route_a<F_Q8>(fg, a, s, ev);
+    case F_S4: return launch_route_a<F_S4>(fg, a, s, ev);
   }
   return hipErrorInvalidValue;
 }
