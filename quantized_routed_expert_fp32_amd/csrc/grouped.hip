@@ -36,80 +36,150 @@ constexpr int BIG_MIN_ROWS = 96;   // experts with at least this many rows take 
 constexpr int META_OFF = 8;
 
 // ------------------------------------------------------------------ sort
+// Exclusive prefix sum of n <= 320 LDS counters by one wave (lane l owns
+// entries 5l .. 5l+4); returns the total.
+__device__ __forceinline__ int wave_exclusive_scan(const int* in, int* out, int n, int lane) {
+  int v[5], loc = 0;
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int i = 5 * lane + q;
+    v[q] = i < n ? in[i] : 0;
+    loc += v[q];
+  }
+  int inc = loc;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  int run = inc - loc;
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int i = 5 * lane + q;
+    if (i < n) out[i] = run;
+    run += v[q];
+  }
+  return __shfl(inc, 63);
+}
+
+// Ranks of this round's lanes among the lanes holding the same expert (the
+// ballots over the id bits), and the lanes' group sizes.
+__device__ __forceinline__ void round_match(int e, bool ok, int lane, int& rank, int& size) {
+  unsigned long long m = __ballot(ok);
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const unsigned long long bal = __ballot(ok && ((e >> b) & 1));
+    m &= ((e >> b) & 1) ? bal : ~bal;
+  }
+  rank = __popcll(m & ((1ull << lane) - 1ull));
+  size = __popcll(m);
+}
+
+// One workgroup of 1024 threads (16 waves). Wave w owns the contiguous slot
+// range [w S, (w+1) S), S = ceil(R k / 16), walked 64 slots a round:
+//  1. per-wave expert histograms (rank-0 lanes of each round add their
+//     group's size; a wave's own LDS row, so no atomics);
+//  2. exclusive scan over the experts (shared expert E with every row), then
+//     each wave's base per expert: the offset plus the earlier waves' counts;
+//  3. the same walk again scatters each slot (row r, pick j) to base + the
+//     count of earlier slots of its expert in the wave (stable order);
+//  4. the tile lists: experts with many rows get 128-row M-tiles, the rest
+//     32-row M-tiles (the Zipf-skewed chunk has one hot expert with most rows
+//     and a long tail of small ones), each list laid out by a scan over the
+//     experts' tile counts.
 __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
-  __shared__ int cnt[260];
-  __shared__ int run[260];
-  __shared__ int off[260];
-  __shared__ int wc[16][258];
-  __shared__ int s_nt[2];
+  __shared__ int cnt[320];
+  __shared__ int off[320];
+  __shared__ int tb[320], ts[320];       // tiles per expert (big / small lists), then their offsets
+  __shared__ int wh[16][258];            // per-wave counts, then per-wave running positions
+  __shared__ int s_tot[2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int E = a.E, k = a.k, R = a.R, nslot = R * k;
-  for (int e = tid; e < 260; e += 1024) { cnt[e] = 0; run[e] = 0; }
+  const int S = (nslot + 15) / 16, s0 = w * S, s1 = min(nslot, s0 + S);
+  for (int q = tid; q < 16 * 258; q += 1024) (&wh[0][0])[q] = 0;
   __syncthreads();
-  for (int i = tid; i < nslot; i += 1024) {
-    const int e = a.ids[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    cnt[E] = R;
-    int s = 0;
-    for (int e = 0; e <= E; ++e) { off[e] = s; s += cnt[e]; }
-    off[E + 1] = s;
-    for (int e = 0; e <= E + 1; ++e) a.meta[META_OFF + e] = off[e];
-  }
-  __syncthreads();
-  // stable scatter, 1024 slots at a time
-  for (int base = 0; base < nslot; base += 1024) {
-    for (int q = tid; q < 16 * 258; q += 1024) (&wc[0][0])[q] = 0;
-    __syncthreads();
-    const int i = base + tid;
-    const int e = i < nslot ? a.ids[i] : -1;
+  // 1. histograms (the next round's picks are loaded before this round's work)
+  int e_nx = s0 + lane < s1 ? a.ids[s0 + lane] : -1;
+  for (int base = s0; base < s1; base += 64) {
+    const int e = e_nx;
+    e_nx = base + 64 + lane < s1 ? a.ids[base + 64 + lane] : -1;
     const bool ok = e >= 0 && e < E;
-    // lanes of this wave holding the same expert
-    unsigned long long m = __ballot(ok);
-#pragma unroll
-    for (int b = 0; b < 9; ++b) {
-      const unsigned long long bal = __ballot(ok && ((e >> b) & 1));
-      m &= ((e >> b) & 1) ? bal : ~bal;
+    int rank, size;
+    round_match(e, ok, lane, rank, size);
+    if (ok && rank == 0) wh[w][e] += size;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    int c = 0;
+    for (int q = 0; q < 16; ++q) c += wh[q][e];
+    cnt[e] = c;
+  }
+  __syncthreads();
+  // 2. offsets, per-wave bases
+  if (w == 0) {
+    if (lane == 0) cnt[E] = R;
+    __builtin_amdgcn_wave_barrier();
+    const int tot = wave_exclusive_scan(cnt, off, E + 1, lane);
+    if (lane == 0) off[E + 1] = tot;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    int run = off[e];
+    for (int q = 0; q < 16; ++q) {
+      const int c = wh[q][e];
+      wh[q][e] = run;
+      run += c;
     }
-    const int rank = __popcll(m & ((1ull << lane) - 1ull));
-    if (ok && rank == 0) wc[w][e] = __popcll(m);
-    __syncthreads();
+  }
+  for (int e = tid; e <= E + 1; e += 1024) a.meta[META_OFF + e] = off[e];
+  for (int e = tid; e <= E; e += 1024) {
+    const int c = cnt[e];
+    const bool big = c >= BIG_MIN_ROWS;
+    tb[e] = big ? (c + 127) / 128 : 0;
+    ts[e] = big ? 0 : (c + 31) / 32;
+  }
+  __syncthreads();
+  // 3. stable scatter (a wave's rounds in slot order, its own LDS row)
+  e_nx = s0 + lane < s1 ? a.ids[s0 + lane] : -1;
+  for (int base = s0; base < s1; base += 64) {
+    const int i = base + lane;
+    const int e = e_nx;
+    e_nx = base + 64 + lane < s1 ? a.ids[base + 64 + lane] : -1;
+    const bool ok = e >= 0 && e < E;
+    int rank, size;
+    round_match(e, ok, lane, rank, size);
     if (ok) {
-      int before = run[e];
-      for (int q = 0; q < w; ++q) before += wc[q][e];
-      const int pos = off[e] + before + rank;
-      const int r = i / k, j = i % k;
-      a.perm[pos] = r * (k + 1) + j;
+      a.perm[wh[w][e] + rank] = (i / k) * (k + 1) + i % k;
     }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += 1024) {
-      int s = 0;
-      for (int q = 0; q < 16; ++q) s += wc[q][ee];
-      run[ee] += s;
-    }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    if (ok && rank == 0) wh[w][e] += size;
+    __builtin_amdgcn_wave_barrier();
   }
   for (int r = tid; r < R; r += 1024) a.perm[off[E] + r] = r * (k + 1) + k;
-  // tile lists: entry = (expert, first position, rows)
-  if (tid == 0) {
-    int nb = 0, ns = 0;
-    for (int e = 0; e <= E; ++e) {
-      const int c = cnt[e];
-      if (c == 0) continue;
-      const bool big = c >= BIG_MIN_ROWS;
-      const int bm = big ? 128 : 32;
-      for (int m0 = 0; m0 < c; m0 += bm) {
-        const int rows = min(bm, c - m0);
-        int* t = big ? a.tiles + 3 * nb++ : a.tiles + 3 * (a.max_tiles + ns++);
-        t[0] = e;
-        t[1] = off[e] + m0;
-        t[2] = rows;
-      }
+  // 4. tile lists: entry = (expert, first position, rows)
+  if (w == 0) {
+    const int nb = wave_exclusive_scan(tb, tb, E + 1, lane);
+    if (lane == 0) s_tot[0] = nb;
+  } else if (w == 1) {
+    const int ns = wave_exclusive_scan(ts, ts, E + 1, lane);
+    if (lane == 0) s_tot[1] = ns;
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += 1024) {
+    const int c = cnt[e];
+    if (c == 0) continue;
+    const bool big = c >= BIG_MIN_ROWS;
+    const int bm = big ? 128 : 32;
+    int* t = big ? a.tiles + 3 * tb[e] : a.tiles + 3 * (a.max_tiles + ts[e]);
+    for (int m0 = 0; m0 < c; m0 += bm, t += 3) {
+      t[0] = e;
+      t[1] = off[e] + m0;
+      t[2] = min(bm, c - m0);
     }
-    a.meta[0] = nb;
-    a.meta[1] = ns;
+  }
+  if (tid == 0) {
+    a.meta[0] = s_tot[0];
+    a.meta[1] = s_tot[1];
   }
 }
 
@@ -340,7 +410,7 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
 
 // grid: (tiles of the list) x (column blocks); list 0 = 128-row tiles, 1 = 32-row tiles
 template <int FR, int FS, int MODE, int MT, int ACT16>
-__global__ __launch_bounds__(256) void k_grp_gemm(GroupedArgs a, const uint16_t* __restrict__ x, int list) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_grp_gemm(GroupedArgs a, const uint16_t* __restrict__ x, int list) {
   __shared__ __align__(16) uint16_t lds_a[32 * MT * 72];
   const int nblk = a.gemm_nblk;
   const int wg = blockIdx.x;
@@ -359,16 +429,30 @@ __global__ __launch_bounds__(256) void k_grp_gemm(GroupedArgs a, const uint16_t*
 }
 
 // ------------------------------------------------------------------ combine
+// y = sum_j p_j e_j + sigma e_shared, slots in pick order; 4 columns per
+// thread (16-byte loads of the slot outputs).
 __global__ __launch_bounds__(256) void k_grp_combine(GroupedArgs a) {
-  const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
-  const int H = a.H, k = a.k;
-  if (i >= (uint64_t)a.R * H) return;
-  const int r = (int)(i / H), n = (int)(i % H);
+  const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;   // 4-column group
+  const int H = a.H, k = a.k, H4 = H / 4;
+  if (i >= (uint64_t)a.R * H4) return;
+  const int r = (int)(i / H4), n = (int)(i % H4) * 4;
   const float* e = a.e_ws + (uint64_t)r * (k + 1) * H + n;
-  float y = 0.f;
-  for (int j = 0; j < k; ++j) y = fmaf(a.p[r * k + j], e[(uint64_t)j * H], y);
-  y = fmaf(a.sg[r], e[(uint64_t)k * H], y);
-  a.y[i] = y;
+  float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float pj = a.p[r * k + j];
+    const float4 v = *reinterpret_cast<const float4*>(e + (uint64_t)j * H);
+    y.x = fmaf(pj, v.x, y.x);
+    y.y = fmaf(pj, v.y, y.y);
+    y.z = fmaf(pj, v.z, y.z);
+    y.w = fmaf(pj, v.w, y.w);
+  }
+  const float sg = a.sg[r];
+  const float4 v = *reinterpret_cast<const float4*>(e + (uint64_t)k * H);
+  y.x = fmaf(sg, v.x, y.x);
+  y.y = fmaf(sg, v.y, y.y);
+  y.z = fmaf(sg, v.z, y.z);
+  y.w = fmaf(sg, v.w, y.w);
+  *reinterpret_cast<float4*>(a.y + (uint64_t)r * H + n) = y;
 }
 
 // ------------------------------------------------------------------ launch
@@ -399,7 +483,7 @@ static hipError_t launch_grouped_t(const GroupedArgs& a, hipStream_t s, hipEvent
   if (err != hipSuccess) return err;
   err = launch_gemm<FR, FS, DN, ACT16>(a, s, (a.H / 64 + 3) / 4, ev, 4);
   if (err != hipSuccess) return err;
-  const uint64_t n = (uint64_t)a.R * a.H;
+  const uint64_t n = (uint64_t)a.R * (a.H / 4);
   launch_k(k_grp_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ev, 6, a);
   return hipGetLastError();
 }

@@ -249,6 +249,129 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
   pick_and_store(a, row, key, v, c, lane, scr);
 }
 
+// Prompt chunks: logits of 32 rows x 64 experts per workgroup on 16-bit
+// MFMA, the K axis split over 4 waves (quarters, reduced in order). The
+// codes enter as exact fp16 values q/16 (affine) or (u - 8)/16 (symmetric),
+// the activations as fp16 (bf16 converts exactly in fp16's normal range), so
+// every product is exact and each group's MFMA sum is folded in fp32:
+// logit += 16 s * acc_g (+ b * sum_g x for affine). Same values as the
+// per-row form up to the order of the fp32 sums.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+template <int FR, int ACT16>
+__global__ __launch_bounds__(256) void k_route_mfma(RouteArgs a, const uint16_t* __restrict__ x) {
+  static_assert(FR == F_Q4 || FR == F_S4, "16-bit MFMA router reads 4-bit codes");
+  constexpr int G = Fmt<FR>::G, GPS = KBLK / G;
+  __shared__ float part[4][32][64];
+  __shared__ __align__(16) float xs[4][32];
+  const int H = a.H, E = a.E, nch = H / 32, nkb = H / KBLK;
+  const int t = blockIdx.x, r0 = blockIdx.y * 32;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, hsel = lane >> 5;
+  const int arow = min(r0 + col, a.R - 1);
+  const uint16_t* xr = x + (uint64_t)arow * H;
+  const uint8_t* codes = a.base + a.r_off;
+  const uint8_t* scales = a.base + a.r_soff;
+  const int KQ = H / 4, k_begin = w * KQ;
+  float16_t tot[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tot[nt][v] = 0.f;
+  for (int g0 = k_begin; g0 < k_begin + KQ; g0 += G) {
+    float16_t acc[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[nt][v] = 0.f;
+    float xsum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < G / 16; ++kk) {
+      const int k0 = g0 + 16 * kk;
+      // A: 8 activations of row col, k = k0 + 8 hsel ..
+      const uint4 xv = *reinterpret_cast<const uint4*>(xr + k0 + 8 * hsel);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      uint32_t ah[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = act_to_f((uint16_t)(xw[i] & 0xFFFFu), ACT16);
+        const float hi = act_to_f((uint16_t)(xw[i] >> 16), ACT16);
+        xsum += lo;
+        xsum += hi;
+        if constexpr (ACT16) {
+          ah[i] = xw[i];
+        } else {
+          half2v hp;
+          hp.x = (f16)lo;
+          hp.y = (f16)hi;
+          ah[i] = as_u(hp);
+        }
+      }
+      const half8_t A = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(ah));
+      // B: 8 codes of expert 32 nt + col: word 2 ((k0 % 32) / 16) + hsel of its chunk
+      const int c = k0 / 32, word = 2 * ((k0 % 32) / 16) + hsel;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint32_t cw = *reinterpret_cast<const uint32_t*>(
+            codes + chunk_off<FR>(t, c, nch) + (uint64_t)(32 * nt + col) * Fmt<FR>::CB + 4 * word);
+        uint32_t o[4], pv[16];
+        const uint32_t wv[4] = {cw, 0u, 0u, 0u};
+        unpack_chunk<F_Q4>(wv, pv);      // pairs 0..3 (this word): 1 + q/16
+        const half2v off = Fmt<FR>::AFF ? half2v{(f16)1.0f, (f16)1.0f} : half2v{(f16)1.5f, (f16)1.5f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = as_u(as_h2(pv[i]) - off);
+        const half8_t B = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(o));
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B, acc[nt], 0, 0, 0);
+      }
+    }
+    // group fold: 16 s * acc (+ b * X for affine); X of the accumulator rows
+    const float xs_row = xsum + __shfl_xor(xsum, 32);
+    if (hsel == 0) xs[w][col] = xs_row;
+    __builtin_amdgcn_wave_barrier();
+    const int gi = (g0 % KBLK) / G, kb = g0 / KBLK;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int er = 32 * nt + col;
+      float s, b;
+      if constexpr (Fmt<FR>::AFF) {
+        const uint32_t sv = reinterpret_cast<const uint32_t*>(scales + sblk_off<FR>(t, kb, nkb))[er * GPS + gi];
+        s = bf16_to_f(sv & 0xFFFFu);
+        b = bf16_to_f(sv >> 16);
+      } else {
+        s = f16_bits_to_f(reinterpret_cast<const uint16_t*>(scales + sblk_off<FR>(t, kb, nkb))[er * GPS + gi]);
+        b = 0.f;
+      }
+      const float s16 = 16.0f * s;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = 8 * (v / 4) + 4 * hsel + (v % 4);
+        float tv = fmaf(s16, acc[nt][v], tot[nt][v]);
+        if constexpr (Fmt<FR>::AFF) tv = fmaf(b, xs[w][rr], tv);
+        tot[nt][v] = tv;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part[w][16 * nt + v][lane] = tot[nt][v];
+  __syncthreads();
+  // quarters added in order; 256 threads write the 32 x 64 tile
+  for (int q = threadIdx.x; q < 32 * 64; q += 256) {
+    const int slot = q / 64, ln = q % 64;            // (nt, v) index and lane
+    const int nt = slot / 16, v = slot % 16;
+    const int rr = 8 * (v / 4) + 4 * (ln >> 5) + (v % 4);
+    const int row = r0 + rr, e = t * 64 + 32 * nt + (ln & 31);
+    float l = part[0][slot][ln];
+    l += part[1][slot][ln];
+    l += part[2][slot][ln];
+    l += part[3][slot][ln];
+    if (row < a.R && e < E) a.lg_ws[(uint64_t)row * E + e] = l;
+  }
+}
+
 // One wave per row: gate-row logit, top k, weights, sigmoid gate.
 template <int FG, int ACT16>
 __global__ __launch_bounds__(256) void k_route_pick(RouteArgs a, const uint16_t* __restrict__ x) {
@@ -295,7 +418,14 @@ static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s, hipEvent_t* 
     return hipGetLastError();
   }
   hipEvent_t e0[2] = {ev ? ev[0] : nullptr, nullptr}, e1[2] = {nullptr, ev ? ev[1] : nullptr};
-  launch_k(k_route_logits<FR, ACT16, 8>, dim3(a.E / 64, (a.R + 7) / 8), dim3(64 * nw), 0, s, e0, 0, a, a.x);
+  if constexpr (FR == F_Q4 || FR == F_S4) {
+    if (a.H % 1024 == 0)     // four K quarters of whole 256-wide blocks
+      launch_k(k_route_mfma<FR, ACT16>, dim3(a.E / 64, (a.R + 31) / 32), dim3(256), 0, s, e0, 0, a, a.x);
+    else
+      launch_k(k_route_logits<FR, ACT16, 8>, dim3(a.E / 64, (a.R + 7) / 8), dim3(64 * nw), 0, s, e0, 0, a, a.x);
+  } else {
+    launch_k(k_route_logits<FR, ACT16, 8>, dim3(a.E / 64, (a.R + 7) / 8), dim3(64 * nw), 0, s, e0, 0, a, a.x);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   launch_k(k_route_pick<FG, ACT16>, dim3((a.R + 3) / 4), dim3(256), 0, s, e1, 0, a, a.x);
