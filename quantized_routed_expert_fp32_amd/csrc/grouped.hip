@@ -246,7 +246,7 @@ enum { GU = 0, DN = 1 };
 // BM = 32 * MT rows. K walked in steps of 64 (two code chunks).
 template <int F, int MODE, int MT, int ACT16>
 __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* __restrict__ x,
-                                         int e, int m0, int mc, int nb, uint16_t* lds_a) {
+                                         int e, int m0, int mc, int nb, uint16_t* lds_a, int* slot_l) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = a.k, H = a.H;
@@ -273,6 +273,7 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
     const int rr = sidx / 8, sg = sidx % 8;
     const int rowc = min(rr, mc - 1);
     const int slot = a.perm[m0 + rowc];
+    if (sg == 0) slot_l[rr] = slot;       // the tile's slot indexes, for the epilogue
     const uint16_t* src;
     if constexpr (MODE == GU) src = x + (uint64_t)(slot / (k + 1)) * H;
     else src = a.hbuf + (uint64_t)(m0 + rowc) * a.Imax;
@@ -353,10 +354,17 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
     }
     if (k0 + 64 < K) issue(k0 + 64);
     __syncthreads();
-    // 4 MFMA k-steps of 16: chunk c = kk / 2, word = 2 * (kk % 2) + hsel
+    // 4 MFMA k-steps of 16 (chunk c = kk / 2, word = 2 * (kk % 2) + hsel):
+    // the A fragments of a k-step are read from LDS together, ahead of the
+    // dequantisation, so their latency overlaps it
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int c = kk >> 1, wsel = 2 * (kk & 1) + hsel;
+      half8v_t ah[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        ah[mt] = __builtin_bit_cast(
+            half8v_t, *reinterpret_cast<const uint4*>(lds_a + (32 * mt + col) * AST + 16 * kk + 8 * hsel));
       half8v_t bf[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -365,30 +373,29 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
         bf[nt] = __builtin_bit_cast(half8v_t, *reinterpret_cast<uint4*>(d));
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint4 af = *reinterpret_cast<const uint4*>(lds_a + (32 * mt + col) * AST + 16 * kk + 8 * hsel);
-        const half8v_t ah = __builtin_bit_cast(half8v_t, af);
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bf[nt], acc[mt][nt], 0, 0, 0);
-      }
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[mt], bf[nt], acc[mt][nt], 0, 0, 0);
     }
   }
-  // ---- epilogue
+  // ---- epilogue (slot indexes of the tile's rows from LDS; 32-bit offsets:
+  // positions < R (k+1) <= 589824 and Imax, H <= 4096 keep them below 2^32)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int row = 32 * mt + 8 * (v / 4) + 4 * hsel + (v % 4);
       if (row >= mc) continue;
-      const int pos = m0 + row;
+      const uint32_t pos = (uint32_t)(m0 + row);
       if constexpr (MODE == GU) {
         const float g = acc[mt][0][v], u = acc[mt][1][v];
-        const float hv = silu_mul(g, u);
-        const int j = 32 * T + col;
-        a.hbuf[(uint64_t)pos * a.Imax + j] = __builtin_bit_cast(uint16_t, (f16)hv);
+        // silu(g) u with the hardware exp and reciprocal (h is rounded to fp16)
+        const float hv = g * __frcp_rn(1.0f + __expf(-g)) * u;
+        const uint32_t j = 32 * T + col;
+        a.hbuf[pos * (uint32_t)a.Imax + j] = __builtin_bit_cast(uint16_t, (f16)hv);
         if (a.tap_gu || a.tap_h) {
-          const uint64_t s = (uint64_t)a.perm[pos];
+          const uint64_t s = (uint64_t)slot_l[row];
           if (a.tap_gu) {
             a.tap_gu[(s * 2 + 0) * a.Imax + j] = g;
             a.tap_gu[(s * 2 + 1) * a.Imax + j] = u;
@@ -396,12 +403,12 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
           if (a.tap_h) a.tap_h[s * a.Imax + j] = hv;
         }
       } else {
-        const uint64_t s = (uint64_t)a.perm[pos];
+        const uint32_t s = (uint32_t)slot_l[row];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const int n = 64 * T + 32 * nt + col;
-          a.e_ws[s * H + n] = acc[mt][nt][v];
-          if (a.tap_e) a.tap_e[s * H + n] = acc[mt][nt][v];
+          const uint32_t n = 64 * T + 32 * nt + col;
+          a.e_ws[s * (uint32_t)H + n] = acc[mt][nt][v];
+          if (a.tap_e) a.tap_e[(uint64_t)s * H + n] = acc[mt][nt][v];
         }
       }
     }
@@ -412,6 +419,7 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
 template <int FR, int FS, int MODE, int MT, int ACT16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_grp_gemm(GroupedArgs a, const uint16_t* __restrict__ x, int list) {
   __shared__ __align__(16) uint16_t lds_a[32 * MT * 72];
+  __shared__ int slot_l[32 * MT];
   const int nblk = a.gemm_nblk;
   const int wg = blockIdx.x;
   const int ti = wg / nblk, nb = wg % nblk;
@@ -424,8 +432,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int I = shared ? a.sh.inter : a.rt.inter;
   const int nlt = MODE == GU ? 2 * I / 64 : a.H / 64;   // layout tiles of this expert along N
   if (nb * 4 >= nlt) return;
-  if (shared) grp_tile<FS, MODE, MT, ACT16>(a, x, e, m0, mc, nb, lds_a);
-  else grp_tile<FR, MODE, MT, ACT16>(a, x, e, m0, mc, nb, lds_a);
+  if (shared) grp_tile<FS, MODE, MT, ACT16>(a, x, e, m0, mc, nb, lds_a, slot_l);
+  else grp_tile<FR, MODE, MT, ACT16>(a, x, e, m0, mc, nb, lds_a, slot_l);
 }
 
 // ------------------------------------------------------------------ combine
