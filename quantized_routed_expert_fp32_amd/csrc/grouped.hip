@@ -1,7 +1,7 @@
 // Grouped (prompt-chunk) path: the prefill form for chunks of many rows.
 //
 //  1. k_grp_sort (one workgroup): expert histogram of the picks, exclusive
-//     prefix scan, stable scatter of the slots (row r, pick j) into
+//     prefix scan, scatter of the slots (row r, pick j) into
 //     expert-major order; the shared expert follows as expert E with every
 //     row. Then the tile lists: experts with many rows get 128-row M-tiles,
 //     the rest 32-row M-tiles (the Zipf-skewed chunk has one hot expert
@@ -62,27 +62,16 @@ __device__ __forceinline__ int wave_exclusive_scan(const int* in, int* out, int 
   return __shfl(inc, 63);
 }
 
-// Ranks of this round's lanes among the lanes holding the same expert (the
-// ballots over the id bits), and the lanes' group sizes.
-__device__ __forceinline__ void round_match(int e, bool ok, int lane, int& rank, int& size) {
-  unsigned long long m = __ballot(ok);
-#pragma unroll
-  for (int b = 0; b < 9; ++b) {
-    const unsigned long long bal = __ballot(ok && ((e >> b) & 1));
-    m &= ((e >> b) & 1) ? bal : ~bal;
-  }
-  rank = __popcll(m & ((1ull << lane) - 1ull));
-  size = __popcll(m);
-}
-
 // One workgroup of 1024 threads (16 waves). Wave w owns the contiguous slot
-// range [w S, (w+1) S), S = ceil(R k / 16), walked 64 slots a round:
-//  1. per-wave expert histograms (rank-0 lanes of each round add their
-//     group's size; a wave's own LDS row, so no atomics);
+// range [w S, (w+1) S), S = ceil(R k / 16), read 1024 slots at a time:
+//  1. per-wave expert histograms (LDS atomics on the wave's own row);
 //  2. exclusive scan over the experts (shared expert E with every row), then
 //     each wave's base per expert: the offset plus the earlier waves' counts;
-//  3. the same walk again scatters each slot (row r, pick j) to base + the
-//     count of earlier slots of its expert in the wave (stable order);
+//  3. the same walk again scatters each slot (row r, pick j) to the position
+//     its atomic increment of the wave's counter returns. Rows of one expert
+//     stay within the wave's range in slot order only up to the order the
+//     hardware serves one instruction's lanes; a row's output does not depend
+//     on its position in a tile, so results are the same either way;
 //  4. the tile lists: experts with many rows get 128-row M-tiles, the rest
 //     32-row M-tiles (the Zipf-skewed chunk has one hot expert with most rows
 //     and a long tail of small ones), each list laid out by a scan over the
@@ -98,15 +87,20 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
   const int S = (nslot + 15) / 16, s0 = w * S, s1 = min(nslot, s0 + S);
   for (int q = tid; q < 16 * 258; q += 1024) (&wh[0][0])[q] = 0;
   __syncthreads();
-  // 1. histograms (the next round's picks are loaded before this round's work)
-  int e_nx = s0 + lane < s1 ? a.ids[s0 + lane] : -1;
-  for (int base = s0; base < s1; base += 64) {
-    const int e = e_nx;
-    e_nx = base + 64 + lane < s1 ? a.ids[base + 64 + lane] : -1;
-    const bool ok = e >= 0 && e < E;
-    int rank, size;
-    round_match(e, ok, lane, rank, size);
-    if (ok && rank == 0) wh[w][e] += size;
+  // 1. histograms: the picks of 16 rounds are loaded at once (one latency
+  // per 1024 slots of a wave)
+  for (int bb = s0; bb < s1; bb += 1024) {
+    int ev[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = bb + 64 * q + lane;
+      ev[q] = i < s1 ? a.ids[i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = ev[q];
+      if (e >= 0 && e < E) atomicAdd(&wh[w][e], 1);
+    }
   }
   __syncthreads();
   for (int e = tid; e < E; e += 1024) {
@@ -139,21 +133,20 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
     ts[e] = big ? 0 : (c + 31) / 32;
   }
   __syncthreads();
-  // 3. stable scatter (a wave's rounds in slot order, its own LDS row)
-  e_nx = s0 + lane < s1 ? a.ids[s0 + lane] : -1;
-  for (int base = s0; base < s1; base += 64) {
-    const int i = base + lane;
-    const int e = e_nx;
-    e_nx = base + 64 + lane < s1 ? a.ids[base + 64 + lane] : -1;
-    const bool ok = e >= 0 && e < E;
-    int rank, size;
-    round_match(e, ok, lane, rank, size);
-    if (ok) {
-      a.perm[wh[w][e] + rank] = (i / k) * (k + 1) + i % k;
+  // 3. scatter (positions from the wave's own LDS row)
+  for (int bb = s0; bb < s1; bb += 1024) {
+    int ev[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = bb + 64 * q + lane;
+      ev[q] = i < s1 ? a.ids[i] : -1;
     }
-    __builtin_amdgcn_wave_barrier();
-    if (ok && rank == 0) wh[w][e] += size;
-    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = bb + 64 * q + lane;
+      const int e = ev[q];
+      if (e >= 0 && e < E) a.perm[atomicAdd(&wh[w][e], 1)] = (i / k) * (k + 1) + i % k;
+    }
   }
   for (int r = tid; r < R; r += 1024) a.perm[off[E] + r] = r * (k + 1) + k;
   // 4. tile lists: entry = (expert, first position, rows)
