@@ -14,7 +14,9 @@
 //     is staged through LDS as fp16; B (the packed codes) goes from memory
 //     straight to registers and is dequantised there to fp16
 //     (affine: s*q + b; symmetric: s*(u - 8)); v_mfma_f32_32x32x16_f16
-//     accumulates in fp32. Output h in fp16, expert-major.
+//     accumulates in fp32. Output h in fp16, expert-major. The 128-row and
+//     32-row tile lists share one launch, so the few large tiles (the shared
+//     expert, hot experts) run beside the many small ones.
 //  3. k_grp_gemm<DN>: the same on h and the down matrices; output e in fp32
 //     in slot order.
 //  4. k_grp_combine: y = sum_j p_j e_j + sigma e_shared, slots in pick order.
@@ -235,9 +237,130 @@ __device__ __forceinline__ void deq_chunk_half(const uint32_t* cw, int wsel, hal
 
 enum { GU = 0, DN = 1 };
 
+constexpr int AST = 72;    // LDS row stride of the A tile in halves (64 + 8 pad)
+
+// 4-bit codes: the lane of half hsel takes words 2 hsel, 2 hsel + 1 of each
+// chunk row (8 contiguous bytes), i.e. k = 16 hsel .. 16 hsel + 15 of the
+// chunk, and the A fragments follow the same k. The 3-bit rows hold a
+// chunk's codes across all 3 words, so their lanes load the full row.
+template <int F> struct BFrag {
+  static constexpr bool HALF = F == F_Q4 || F == F_S4;
+  static constexpr int W = HALF ? 2 : Fmt<F>::WORDS;   // words per chunk per lane
+};
+
+// One pipeline stage: the A segments a thread stages, the code words and
+// the scale word (per n-tile) of the wave's layout tile for one 64-k step.
+template <int F, int SPT>
+struct GrpStage {
+  uint4 av[SPT];
+  uint32_t bw[2][2][BFrag<F>::W];
+  uint32_t sr[2];
+};
+
+template <int F, int SPT>
+__device__ __forceinline__ void grp_issue(GrpStage<F, SPT>& st, const uint16_t* const (&arow)[SPT],
+                                          const int (&aseg)[SPT], const uint8_t* codes, const uint8_t* scales,
+                                          int T, int nch, int nkb, int col, int hsel, int kk0) {
+  constexpr int GPS = KBLK / Fmt<F>::G;
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) st.av[q] = *reinterpret_cast<const uint4*>(arow[q] + kk0 + 8 * aseg[q]);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint8_t* blk = codes + chunk_off<F>(T, kk0 / 32 + c, nch);
+      if constexpr (BFrag<F>::HALF) {
+        const uint2 v = *reinterpret_cast<const uint2*>(blk + (32 * nt + col) * Fmt<F>::CB + 8 * hsel);
+        st.bw[nt][c][0] = v.x;
+        st.bw[nt][c][1] = v.y;
+      } else {
+        load_chunk<F>(blk, 32 * nt + col, st.bw[nt][c]);
+      }
+    }
+  const int gi = (kk0 % KBLK) / Fmt<F>::G;
+  const uint8_t* sblk = scales + sblk_off<F>(T, kk0 / KBLK, nkb);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    if constexpr (Fmt<F>::AFF) st.sr[nt] = reinterpret_cast<const uint32_t*>(sblk)[(32 * nt + col) * GPS + gi];
+    else st.sr[nt] = reinterpret_cast<const uint16_t*>(sblk)[(32 * nt + col) * GPS + gi];
+  }
+}
+
+// A segments of a stage into one LDS buffer (bf16 -> fp16 on the way: exact
+// for |x| in fp16's normal range)
+template <int MODE, int ACT16, int SPT>
+__device__ __forceinline__ void grp_store_a(const uint4 (&av)[SPT], uint16_t* buf, const int (&arr)[SPT],
+                                            const int (&aseg)[SPT]) {
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    uint4 v = av[q];
+    if constexpr (MODE == GU && !ACT16) {
+      uint32_t* u = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        half2v h;
+        h.x = (f16)bf16_to_f(u[i] & 0xFFFFu);
+        h.y = (f16)bf16_to_f(u[i] >> 16);
+        u[i] = as_u(h);
+      }
+    }
+    *reinterpret_cast<uint4*>(buf + arr[q] * AST + 8 * aseg[q]) = v;
+  }
+}
+
+// The MFMAs of one 64-k step: 4 k-steps of 16 over the step's 2 chunks; the
+// A fragments of a k-step are read from LDS ahead of the dequantisation.
+template <int F, int MT, int SPT>
+__device__ __forceinline__ void grp_mma(f16v_t (&acc)[MT][2], const GrpStage<F, SPT>& st, const uint16_t* buf,
+                                        int col, int hsel) {
+  half2v s16[2], b2[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float sc, bi;
+    if constexpr (Fmt<F>::AFF) {
+      sc = bf16_to_f(st.sr[nt] & 0xFFFFu);
+      bi = bf16_to_f(st.sr[nt] >> 16);
+    } else {
+      sc = f16_bits_to_f(st.sr[nt]);
+      bi = 0.f;
+    }
+    const f16 sh = (f16)(16.0f * sc), bh = (f16)bi;
+    s16[nt] = {sh, sh};
+    b2[nt] = {bh, bh};
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // k offset of this lane's 8 values inside the 64-k step
+      const int koff = BFrag<F>::HALF ? 32 * c + 16 * hsel + 8 * j : 32 * c + 16 * j + 8 * hsel;
+      half8v_t ah[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        ah[mt] = __builtin_bit_cast(half8v_t, *reinterpret_cast<const uint4*>(buf + (32 * mt + col) * AST + koff));
+      half8v_t bf[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        uint32_t d[4];
+        if constexpr (BFrag<F>::HALF) deq_word<F>(&st.bw[nt][c][j], s16[nt], b2[nt], d);
+        else deq_chunk_half<F>(st.bw[nt][c], 2 * j + hsel, s16[nt], b2[nt], d);
+        bf[nt] = __builtin_bit_cast(half8v_t, *reinterpret_cast<uint4*>(d));
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+    }
+}
+
 // One workgroup: (tile, column block of 4 layout tiles); wave w = layout tile.
-// BM = 32 * MT rows. K walked in steps of 64 (two code chunks).
-template <int F, int MODE, int MT, int ACT16>
+// BM = 32 * MT rows. K walked in steps of 64 (two code chunks) through a ring
+// of NS register stages: the loads of step t + NS - 1 are issued before the
+// MFMAs of step t. The A tile alternates between two LDS buffers, so one
+// barrier per step orders both the buffer's writes before its reads and the
+// reads of step t - 1 before the writes of step t + 1.
+template <int F, int MODE, int MT, int ACT16, int NS>
 __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* __restrict__ x,
                                          int e, int m0, int mc, int nb, uint16_t* lds_a, int* slot_l) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -253,9 +376,8 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
   const uint8_t* scales = blk + (MODE == GU ? ec.gu_scales : ec.dn_scales);
   const int nch = K / 32, nkb = K / KBLK;
   constexpr int BM = 32 * MT;
-  constexpr int AST = 72;                    // LDS row stride in halves (64 + 8 pad)
-  // ---- A rows this thread stages: BM rows x 64 halves per K-step; thread t
-  // handles row t / (256 / BM) ... as (row, 8-half segment) pairs
+  // ---- A rows this thread stages: BM rows x 64 halves per step, as
+  // (row, 8-half segment) pairs
   constexpr int SEGS = BM * 8;               // 8 halves per segment
   constexpr int SPT = SEGS / 256;            // segments per thread
   const uint16_t* arow[SPT];
@@ -282,94 +404,23 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.f;
   const int col = lane & 31, hsel = lane >> 5;
-  constexpr int GPS = KBLK / Fmt<F>::G;
-  // software pipeline: the loads of step k0 + 64 are issued before the
-  // MFMAs of step k0
-  uint4 av[SPT];
-  uint32_t cw[2][2][Fmt<F>::WORDS];
-  uint32_t sraw[2];
-  auto issue = [&](int kk0) {
+  // K is a multiple of 256, so the step count is a multiple of NS (2 or 4);
+  // the prefetches past the last step re-read it (clamped, never used)
+  const int steps = K / 64;
+  GrpStage<F, SPT> st[NS];
 #pragma unroll
-    for (int q = 0; q < SPT; ++q) av[q] = *reinterpret_cast<const uint4*>(arow[q] + kk0 + 8 * aseg[q]);
+  for (int s = 0; s < NS - 1; ++s)
+    grp_issue<F, SPT>(st[s], arow, aseg, codes, scales, T, nch, nkb, col, hsel, 64 * min(s, steps - 1));
+  for (int base = 0; base < steps; base += NS) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        load_chunk<F>(codes + chunk_off<F>(T, kk0 / 32 + c, nch), 32 * nt + col, cw[nt][c]);
-    const int gi = (kk0 % KBLK) / Fmt<F>::G;
-    const uint8_t* sblk = scales + sblk_off<F>(T, kk0 / KBLK, nkb);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if constexpr (Fmt<F>::AFF) sraw[nt] = reinterpret_cast<const uint32_t*>(sblk)[(32 * nt + col) * GPS + gi];
-      else sraw[nt] = reinterpret_cast<const uint16_t*>(sblk)[(32 * nt + col) * GPS + gi];
-    }
-  };
-  issue(0);
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    __syncthreads();     // the previous step's A reads are done
-#pragma unroll
-    for (int q = 0; q < SPT; ++q) {
-      uint4 v = av[q];
-      if constexpr (MODE == GU && !ACT16) {
-        // bf16 -> fp16 (exact for |x| in the fp16 normal range)
-        uint32_t* u = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          half2v h;
-          h.x = (f16)bf16_to_f(u[i] & 0xFFFFu);
-          h.y = (f16)bf16_to_f(u[i] >> 16);
-          u[i] = as_u(h);
-        }
-      }
-      *reinterpret_cast<uint4*>(lds_a + arr[q] * AST + 8 * aseg[q]) = v;
-    }
-    uint32_t cur[2][2][Fmt<F>::WORDS];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int q = 0; q < Fmt<F>::WORDS; ++q) cur[nt][c][q] = cw[nt][c][q];
-    half2v s16[2], b2[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float sc, bi;
-      if constexpr (Fmt<F>::AFF) {
-        sc = bf16_to_f(sraw[nt] & 0xFFFFu);
-        bi = bf16_to_f(sraw[nt] >> 16);
-      } else {
-        sc = f16_bits_to_f(sraw[nt]);
-        bi = 0.f;
-      }
-      const f16 sh = (f16)(16.0f * sc), bh = (f16)bi;
-      s16[nt] = {sh, sh};
-      b2[nt] = {bh, bh};
-    }
-    if (k0 + 64 < K) issue(k0 + 64);
-    __syncthreads();
-    // 4 MFMA k-steps of 16 (chunk c = kk / 2, word = 2 * (kk % 2) + hsel):
-    // the A fragments of a k-step are read from LDS together, ahead of the
-    // dequantisation, so their latency overlaps it
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = kk >> 1, wsel = 2 * (kk & 1) + hsel;
-      half8v_t ah[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        ah[mt] = __builtin_bit_cast(
-            half8v_t, *reinterpret_cast<const uint4*>(lds_a + (32 * mt + col) * AST + 16 * kk + 8 * hsel));
-      half8v_t bf[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        uint32_t d[4];
-        deq_chunk_half<F>(cur[nt][c], wsel, s16[nt], b2[nt], d);
-        bf[nt] = __builtin_bit_cast(half8v_t, *reinterpret_cast<uint4*>(d));
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+    for (int s = 0; s < NS; ++s) {
+      const int step = base + s;
+      uint16_t* buf = lds_a + (s & 1) * (BM * AST);
+      grp_store_a<MODE, ACT16, SPT>(st[s].av, buf, arr, aseg);
+      grp_issue<F, SPT>(st[(s + NS - 1) % NS], arow, aseg, codes, scales, T, nch, nkb, col, hsel,
+                        64 * min(step + NS - 1, steps - 1));
+      __syncthreads();
+      grp_mma<F, MT, SPT>(acc, st[s], buf, col, hsel);
     }
   }
   // ---- epilogue (slot indexes of the tile's rows from LDS; 32-bit offsets:
@@ -408,13 +459,15 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
   }
 }
 
-// grid: (tiles of the list) x (column blocks); list 0 = 128-row tiles, 1 = 32-row tiles
+// One launch for both tile lists, so the two run side by side: workgroups
+// [0, nbig) take the 128-row list (tile wg / nblk, column block wg % nblk),
+// the rest the 32-row list. Each list is sized for its worst case; the
+// workgroups past a list's tile count exit at once.
 template <int FR, int FS, int MODE, int MT, int ACT16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_grp_gemm(GroupedArgs a, const uint16_t* __restrict__ x, int list) {
-  __shared__ __align__(16) uint16_t lds_a[32 * MT * 72];
-  __shared__ int slot_l[32 * MT];
+__device__ __forceinline__ void grp_list(const GroupedArgs& a, const uint16_t* __restrict__ x, int list, int wg,
+                                         uint16_t* lds_a, int* slot_l) {
+  constexpr int NS = MT == 1 ? 4 : 2;        // pipeline stages
   const int nblk = a.gemm_nblk;
-  const int wg = blockIdx.x;
   const int ti = wg / nblk, nb = wg % nblk;
   const int ntiles = a.meta[list];
   if (ti >= ntiles) return;
@@ -425,8 +478,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int I = shared ? a.sh.inter : a.rt.inter;
   const int nlt = MODE == GU ? 2 * I / 64 : a.H / 64;   // layout tiles of this expert along N
   if (nb * 4 >= nlt) return;
-  if (shared) grp_tile<FS, MODE, MT, ACT16>(a, x, e, m0, mc, nb, lds_a, slot_l);
-  else grp_tile<FR, MODE, MT, ACT16>(a, x, e, m0, mc, nb, lds_a, slot_l);
+  if (shared) grp_tile<FS, MODE, MT, ACT16, NS>(a, x, e, m0, mc, nb, lds_a, slot_l);
+  else grp_tile<FR, MODE, MT, ACT16, NS>(a, x, e, m0, mc, nb, lds_a, slot_l);
+}
+
+template <int FR, int FS, int MODE, int ACT16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_grp_gemm(GroupedArgs a, const uint16_t* __restrict__ x, int nbig) {
+  __shared__ __align__(16) uint16_t lds_a[2 * 128 * AST];
+  __shared__ int slot_l[128];
+  const int wg = blockIdx.x;
+  if (wg < nbig) grp_list<FR, FS, MODE, 4, ACT16>(a, x, 0, wg, lds_a, slot_l);
+  else grp_list<FR, FS, MODE, 1, ACT16>(a, x, 1, wg - nbig, lds_a, slot_l);
 }
 
 // ------------------------------------------------------------------ combine
@@ -466,11 +528,8 @@ static hipError_t launch_gemm(const GroupedArgs& a, hipStream_t s, int nblk, hip
   const int slots = a.R * (a.k + 1);
   const int max_big = slots / 128 + slots / BIG_MIN_ROWS + 1;
   const int max_small = slots / 32 + a.E + 1;
-  hipEvent_t e0[2] = {ev ? ev[i] : nullptr, nullptr}, e1[2] = {nullptr, ev ? ev[i + 1] : nullptr};
-  launch_k(k_grp_gemm<FR, FS, MODE, 4, ACT16>, dim3(max_big * nblk), dim3(256), 0, s, e0, 0, b, a.x, 0);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  launch_k(k_grp_gemm<FR, FS, MODE, 1, ACT16>, dim3(max_small * nblk), dim3(256), 0, s, e1, 0, b, a.x, 1);
+  const int nbig = max_big * nblk;
+  launch_k(k_grp_gemm<FR, FS, MODE, ACT16>, dim3(nbig + max_small * nblk), dim3(256), 0, s, ev, i, b, a.x, nbig);
   return hipGetLastError();
 }
 

@@ -13,8 +13,10 @@
 //  * decode batches (k_route): one launch; the logits go out with
 //    write-through stores, and the last of a row's tile workgroups to arrive
 //    (a per-row counter in the workspace, reset by that workgroup) picks.
-//  * prompt chunks (k_route_logits + k_route_pick): NR = 8 rows per logits
-//    workgroup, then one wave per row picks in a second launch.
+//  * prompt chunks: logits of 32 rows x 64 experts per workgroup on MFMA
+//    (k_route_mfma, 4-bit router codes) or 8 rows per workgroup on the
+//    vector units (k_route_logits), then one wave per row picks in a second
+//    launch (k_route_pick).
 // Each row's arithmetic is the same whatever NR and the other rows are, so
 // picks and weights of a row do not depend on the batch.
 #include "moe_kernels.h"
@@ -250,36 +252,59 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
 }
 
 // Prompt chunks: logits of 32 rows x 64 experts per workgroup on 16-bit
-// MFMA, the K axis split over 4 waves (quarters, reduced in order). The
-// codes enter as exact fp16 values q/16 (affine) or (u - 8)/16 (symmetric),
-// the activations as fp16 (bf16 converts exactly in fp16's normal range), so
-// every product is exact and each group's MFMA sum is folded in fp32:
-// logit += 16 s * acc_g (+ b * sum_g x for affine). Same values as the
-// per-row form up to the order of the fp32 sums.
+// MFMA. The K axis is split over 8 waves by 256-wide scale blocks (wave w
+// takes blocks w, w + 8, ...); a wave issues all loads of a block (32 rows of
+// activations, 64 rows of codes, their scales) before its first MFMA, so one
+// memory latency covers the block. The codes enter as exact fp16 values q/16
+// (affine) or (u - 8)/16 (symmetric), the activations as fp16 (bf16 converts
+// exactly in fp16's normal range), so every product is exact and each
+// group's MFMA sum is scaled in fp32: logit += 16 s * acc_g, then for affine
+// codes + b_g * sum_g x, group by group. The 8 wave partials are added in a
+// fixed order. Same values as the per-row form up to the order of the fp32
+// sums, and a row's value does not depend on the other rows of the chunk.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
+constexpr int RM_WAVES = 8;
+
+// One 256-wide block kb of one wave: xr points at the lane's activation row
+// (row col of the tile) at k offset 8 hsel.
 template <int FR, int ACT16>
-__global__ __launch_bounds__(256) void k_route_mfma(RouteArgs a, const uint16_t* __restrict__ x) {
-  static_assert(FR == F_Q4 || FR == F_S4, "16-bit MFMA router reads 4-bit codes");
-  constexpr int G = Fmt<FR>::G, GPS = KBLK / G;
-  __shared__ float part[4][32][64];
-  __shared__ __align__(16) float xs[4][32];
-  const int H = a.H, E = a.E, nch = H / 32, nkb = H / KBLK;
-  const int t = blockIdx.x, r0 = blockIdx.y * 32;
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 31, hsel = lane >> 5;
-  const int arow = min(r0 + col, a.R - 1);
-  const uint16_t* xr = x + (uint64_t)arow * H;
+__device__ __forceinline__ void route_mfma_block(const RouteArgs& a, const uint16_t* xr, int t, int kb, int nch,
+                                                 int nkb, int col, int hsel, float* xs, float16_t (&tot)[2]) {
+  constexpr int G = Fmt<FR>::G, NG = KBLK / G, KPG = G / 16;
   const uint8_t* codes = a.base + a.r_off;
-  const uint8_t* scales = a.base + a.r_soff;
-  const int KQ = H / 4, k_begin = w * KQ;
-  float16_t tot[2];
+  const uint8_t* scales = a.base + a.r_soff + sblk_off<FR>(t, kb, nkb);
+  uint4 xv[16];
+  uint32_t cw[2][16];
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) xv[kk] = *reinterpret_cast<const uint4*>(xr + KBLK * kb + 16 * kk);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) tot[nt][v] = 0.f;
-  for (int g0 = k_begin; g0 < k_begin + KQ; g0 += G) {
+    for (int kk = 0; kk < 16; ++kk)
+      cw[nt][kk] = *reinterpret_cast<const uint32_t*>(codes + chunk_off<FR>(t, 8 * kb + kk / 2, nch) +
+                                                      (uint64_t)(32 * nt + col) * Fmt<FR>::CB +
+                                                      4 * (2 * (kk % 2) + hsel));
+  // scales of rows 32 nt + col: NG groups each (bf16 scale/bias pairs, or fp16 scales)
+  uint32_t sv[2][NG];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    if constexpr (Fmt<FR>::AFF) {
+      const uint4 q = reinterpret_cast<const uint4*>(scales)[32 * nt + col];
+      sv[nt][0] = q.x; sv[nt][1] = q.y; sv[nt][2] = q.z; sv[nt][3] = q.w;
+    } else {
+      const uint32_t q = reinterpret_cast<const uint32_t*>(scales)[32 * nt + col];
+      sv[nt][0] = q & 0xFFFFu;
+      sv[nt][1] = q >> 16;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);    // every load of the block issued before the first MFMA
+  static_assert(!Fmt<FR>::AFF || NG == 4, "affine router groups of 64");
+  static_assert(Fmt<FR>::AFF || NG == 2, "symmetric router groups of 128");
+  const half2v off = Fmt<FR>::AFF ? half2v{(f16)1.0f, (f16)1.0f} : half2v{(f16)1.5f, (f16)1.5f};
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
     float16_t acc[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -287,18 +312,18 @@ __global__ __launch_bounds__(256) void k_route_mfma(RouteArgs a, const uint16_t*
       for (int v = 0; v < 16; ++v) acc[nt][v] = 0.f;
     float xsum = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < G / 16; ++kk) {
-      const int k0 = g0 + 16 * kk;
-      // A: 8 activations of row col, k = k0 + 8 hsel ..
-      const uint4 xv = *reinterpret_cast<const uint4*>(xr + k0 + 8 * hsel);
-      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    for (int j = 0; j < KPG; ++j) {
+      const int kk = KPG * gi + j;
+      const uint32_t xw[4] = {xv[kk].x, xv[kk].y, xv[kk].z, xv[kk].w};
       uint32_t ah[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float lo = act_to_f((uint16_t)(xw[i] & 0xFFFFu), ACT16);
         const float hi = act_to_f((uint16_t)(xw[i] >> 16), ACT16);
-        xsum += lo;
-        xsum += hi;
+        if constexpr (Fmt<FR>::AFF) {
+          xsum += lo;
+          xsum += hi;
+        }
         if constexpr (ACT16) {
           ah[i] = xw[i];
         } else {
@@ -309,57 +334,78 @@ __global__ __launch_bounds__(256) void k_route_mfma(RouteArgs a, const uint16_t*
         }
       }
       const half8_t A = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(ah));
-      // B: 8 codes of expert 32 nt + col: word 2 ((k0 % 32) / 16) + hsel of its chunk
-      const int c = k0 / 32, word = 2 * ((k0 % 32) / 16) + hsel;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const uint32_t cw = *reinterpret_cast<const uint32_t*>(
-            codes + chunk_off<FR>(t, c, nch) + (uint64_t)(32 * nt + col) * Fmt<FR>::CB + 4 * word);
         uint32_t o[4], pv[16];
-        const uint32_t wv[4] = {cw, 0u, 0u, 0u};
+        const uint32_t wv[4] = {cw[nt][kk], 0u, 0u, 0u};
         unpack_chunk<F_Q4>(wv, pv);      // pairs 0..3 (this word): 1 + q/16
-        const half2v off = Fmt<FR>::AFF ? half2v{(f16)1.0f, (f16)1.0f} : half2v{(f16)1.5f, (f16)1.5f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = as_u(as_h2(pv[i]) - off);
         const half8_t B = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(o));
         acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B, acc[nt], 0, 0, 0);
       }
     }
-    // group fold: 16 s * acc (+ b * X for affine); X of the accumulator rows
-    const float xs_row = xsum + __shfl_xor(xsum, 32);
-    if (hsel == 0) xs[w][col] = xs_row;
-    __builtin_amdgcn_wave_barrier();
-    const int gi = (g0 % KBLK) / G, kb = g0 / KBLK;
+    if constexpr (Fmt<FR>::AFF) {
+      const float xs_row = xsum + __shfl_xor(xsum, 32);
+      if (hsel == 0) xs[32 * gi + col] = xs_row;
+    }
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int er = 32 * nt + col;
-      float s, b;
-      if constexpr (Fmt<FR>::AFF) {
-        const uint32_t sv = reinterpret_cast<const uint32_t*>(scales + sblk_off<FR>(t, kb, nkb))[er * GPS + gi];
-        s = bf16_to_f(sv & 0xFFFFu);
-        b = bf16_to_f(sv >> 16);
-      } else {
-        s = f16_bits_to_f(reinterpret_cast<const uint16_t*>(scales + sblk_off<FR>(t, kb, nkb))[er * GPS + gi]);
-        b = 0.f;
-      }
-      const float s16 = 16.0f * s;
+      const float s16 = 16.0f * (Fmt<FR>::AFF ? bf16_to_f(sv[nt][gi] & 0xFFFFu) : f16_bits_to_f(sv[nt][gi]));
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = 8 * (v / 4) + 4 * hsel + (v % 4);
-        float tv = fmaf(s16, acc[nt][v], tot[nt][v]);
-        if constexpr (Fmt<FR>::AFF) tv = fmaf(b, xs[w][rr], tv);
-        tot[nt][v] = tv;
-      }
+      for (int v = 0; v < 16; ++v) tot[nt][v] = fmaf(s16, acc[nt][v], tot[nt][v]);
     }
+  }
+  if constexpr (Fmt<FR>::AFF) {
+    // + b_g * (sum over the group of the row's activations), accumulator rows
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float b = bf16_to_f(sv[nt][gi] >> 16);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          tot[nt][v] = fmaf(b, xs[32 * gi + 8 * (v / 4) + 4 * hsel + (v % 4)], tot[nt][v]);
+      }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+template <int FR, int ACT16>
+__global__ __launch_bounds__(64 * RM_WAVES) void k_route_mfma(RouteArgs a, const uint16_t* __restrict__ x) {
+  static_assert(FR == F_Q4 || FR == F_S4, "16-bit MFMA router reads 4-bit codes");
+  __shared__ float part[4][32][64];
+  __shared__ float xs_all[RM_WAVES][128];
+  const int H = a.H, E = a.E, nch = H / 32, nkb = H / KBLK;
+  const int t = blockIdx.x, r0 = blockIdx.y * 32;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, hsel = lane >> 5;
+  const int arow = min(r0 + col, a.R - 1);
+  const uint16_t* xr = x + (uint64_t)arow * H + 8 * hsel;
+  float16_t tot[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) part[w][16 * nt + v][lane] = tot[nt][v];
+    for (int v = 0; v < 16; ++v) tot[nt][v] = 0.f;
+  for (int kb = w; kb < nkb; kb += RM_WAVES)
+    route_mfma_block<FR, ACT16>(a, xr, t, kb, nch, nkb, col, hsel, xs_all[w], tot);
+  // partials: waves 4..7 onto waves 0..3, then the four in order
+  if (w >= 4) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[w - 4][16 * nt + v][lane] = tot[nt][v];
+  }
   __syncthreads();
-  // quarters added in order; 256 threads write the 32 x 64 tile
-  for (int q = threadIdx.x; q < 32 * 64; q += 256) {
+  if (w < 4) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[w][16 * nt + v][lane] = tot[nt][v] + part[w][16 * nt + v][lane];
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 32 * 64; q += 64 * RM_WAVES) {
     const int slot = q / 64, ln = q % 64;            // (nt, v) index and lane
     const int nt = slot / 16, v = slot % 16;
     const int rr = 8 * (v / 4) + 4 * (ln >> 5) + (v % 4);
@@ -419,8 +465,8 @@ static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s, hipEvent_t* 
   }
   hipEvent_t e0[2] = {ev ? ev[0] : nullptr, nullptr}, e1[2] = {nullptr, ev ? ev[1] : nullptr};
   if constexpr (FR == F_Q4 || FR == F_S4) {
-    if (a.H % 1024 == 0)     // four K quarters of whole 256-wide blocks
-      launch_k(k_route_mfma<FR, ACT16>, dim3(a.E / 64, (a.R + 31) / 32), dim3(256), 0, s, e0, 0, a, a.x);
+    if (a.H % KBLK == 0)     // whole 256-wide blocks over 8 waves
+      launch_k(k_route_mfma<FR, ACT16>, dim3(a.E / 64, (a.R + 31) / 32), dim3(64 * RM_WAVES), 0, s, e0, 0, a, a.x);
     else
       launch_k(k_route_logits<FR, ACT16, 8>, dim3(a.E / 64, (a.R + 7) / 8), dim3(64 * nw), 0, s, e0, 0, a, a.x);
   } else {
