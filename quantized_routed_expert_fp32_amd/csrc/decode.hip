@@ -16,10 +16,12 @@
 //
 // down + combine (k_dec_down): one workgroup per (row, 64-column tile of y)
 // with KS waves per routed slot, each over 1/KS of the intermediate axis,
-// plus a share of the shared expert's groups; the row's h sits in LDS. The
-// slot parts are added in part order, the shared parts in wave order; wave 0
-// forms y = sum_j p_j e_j + sigma e_shared in slot order. Blocks are mapped so
-// the rows of one tile run on one XCD and share expert tiles in its L2.
+// plus a share of the shared expert's groups. Each wave loads the part of
+// the row's h it reads ahead of its weights and stages it in its own LDS
+// area, so it computes as soon as its own loads have landed. The slot parts
+// are added in part order, the shared parts in wave order; wave 0 forms
+// y = sum_j p_j e_j + sigma e_shared in slot order. Blocks are mapped so the
+// rows of one tile run on one XCD and share expert tiles in its L2.
 //
 // Every row's arithmetic is fixed (K slices owned by fixed waves, chunks and
 // groups in K order, slices reduced in slice order, slots combined in pick
@@ -423,17 +425,72 @@ __device__ __forceinline__ uint32_t group_word_voff(int g, int lane) {
 }
 
 // down + combine: one workgroup per (row, 64-column tile of y), k * KS waves.
-// LDS: the row's h (hi, lo pairs) and chunk sums for the k + 1 slots.
-template <int FR, int FS, int HV>
+// Every wave stages only the h it reads (its routed block of slot j and its
+// shared groups) in a wave-private LDS area and starts as soon as its own
+// loads have landed; one barrier before the combine.
+constexpr int DN_WR = 128 + 128 + 8;   // routed block: hi pairs, lo pairs, chunk sums (words)
+constexpr int DN_WS = 136;             // shared group: up to 64 + 64 pairs + 4 chunk sums
+constexpr int DN_WW = DN_WR + DN_WS;   // words per wave
+
+// h of slot s for the 256-wide block kb, loaded (lanes 0..31 the hi pairs,
+// 32..63 the lo pairs, every lane one of the 8 sums), then stored to the
+// wave area (hi at [0, 128), lo at [128, 256), sums at [256, 264)).
+struct HBlk {
+  uint4 v;
+  uint32_t c;
+};
+__device__ __forceinline__ HBlk dn_load_block(const DecodeArgs& a, uint64_t s, int kb, int lane) {
+  const int Ih = a.Imax / 2, Ic = a.Imax / 32;
+  const uint32_t* src = (lane < 32 ? reinterpret_cast<const uint32_t*>(a.hhi) : reinterpret_cast<const uint32_t*>(a.hlo)) +
+                        s * Ih + 128 * kb + 4 * (lane & 31);
+  HBlk h;
+  h.v = *reinterpret_cast<const uint4*>(src);
+  h.c = reinterpret_cast<const uint32_t*>(a.hc)[s * Ic + 8 * kb + (lane & 7)];
+  return h;
+}
+__device__ __forceinline__ void dn_store_block(const HBlk& h, uint32_t* w, int lane) {
+  *reinterpret_cast<uint4*>(w + 4 * lane) = h.v;
+  if (lane < 8) w[256 + lane] = h.c;
+  __builtin_amdgcn_wave_barrier();
+}
+
+// h of the shared slot s for group g (G wide): hi pairs [0, G/2), lo pairs
+// [G/2, G), sums [G, G + G/32) of the wave's shared area.
+template <int G>
+struct HGrp {
+  uint32_t v[(G + G / 32 + 63) / 64];
+};
+template <int G>
+__device__ __forceinline__ HGrp<G> dn_load_group(const DecodeArgs& a, uint64_t s, int g, int lane) {
+  const int Ih = a.Imax / 2, Ic = a.Imax / 32;
+  constexpr int NW = G + G / 32;
+  const uint32_t* hh = reinterpret_cast<const uint32_t*>(a.hhi) + s * Ih + (G / 2) * g;
+  const uint32_t* hl = reinterpret_cast<const uint32_t*>(a.hlo) + s * Ih + (G / 2) * g;
+  const uint32_t* hc = reinterpret_cast<const uint32_t*>(a.hc) + s * Ic + (G / 32) * g;
+  HGrp<G> h;
+#pragma unroll
+  for (int q = 0; q < (NW + 63) / 64; ++q) {
+    const int i = min(lane + 64 * q, NW - 1);
+    h.v[q] = i < G / 2 ? hh[i] : (i < G ? hl[i - G / 2] : hc[i - G]);
+  }
+  return h;
+}
+template <int G>
+__device__ __forceinline__ void dn_store_group(const HGrp<G>& h, uint32_t* w, int lane) {
+  constexpr int NW = G + G / 32;
+#pragma unroll
+  for (int q = 0; q < (NW + 63) / 64; ++q) w[min(lane + 64 * q, NW - 1)] = h.v[q];
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int FR, int FS>
 __global__ __launch_bounds__(1024) void k_dec_down(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int T = a.H / 64, R = a.R, k = a.k, Imax = a.Imax;
+  const int T = a.H / 64, R = a.R, k = a.k;
   const int nwv = k * DN_KS;
-  uint32_t* hhl = reinterpret_cast<uint32_t*>(smem);                     // [k+1][Imax/2]
-  uint32_t* hll = hhl + (k + 1) * (Imax / 2);                             // [k+1][Imax/2]
-  float* hcl = reinterpret_cast<float*>(hll + (k + 1) * (Imax / 2));     // [k+1][Imax/32]
-  float* es = hcl + (k + 1) * (Imax / 32);                                // [nwv][64]
-  float* ps = es + nwv * 64;                                              // [nwv][64]
+  uint32_t* wl = reinterpret_cast<uint32_t*>(smem);          // [nwv][DN_WW]
+  float* es = reinterpret_cast<float*>(wl + nwv * DN_WW);    // [nwv][64]
+  float* ps = es + nwv * 64;                                  // [nwv][64]
   const int wg = blockIdx.x;
   int t, r;
   if (T % 8 == 0) {          // rows of one tile on one XCD (round-robin dispatch over 8 XCDs)
@@ -444,45 +501,13 @@ __global__ __launch_bounds__(1024) void k_dec_down(DecodeArgs a) {
     t = wg / R;
     r = wg % R;
   }
-  const int tid = threadIdx.x, lane = tid & 63, nthr = blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = wi / DN_KS, kp = wi % DN_KS;
-  // the slot's expert through the scalar cache (uniform), so that waiting for
-  // it does not wait for the h pieces below
+  uint32_t* wr_l = wl + wi * DN_WW;      // this wave's routed block area
+  uint32_t* ws_l = wr_l + DN_WR;          // and its shared group area
+  // the slot's expert through the scalar cache (uniform)
   const int e = ((const __attribute__((address_space(4))) int32_t*)(a.ids))[r * k + j];
-  // the row's h (hi, lo: (k+1) * Imax halves each) and chunk sums as 16-byte
-  // pieces: HV unconditional register loads per thread (indexes clamped)
-  // issued before the weight loads, stored to LDS once they land; HV == 0
-  // copies them straight into LDS
-  const int nh = (k + 1) * Imax / 8, nc = (k + 1) * Imax / 128;   // pieces of hi / lo, of the sums
-  const uint4* hsrc_h = reinterpret_cast<const uint4*>(a.hhi + (uint64_t)r * (k + 1) * Imax);
-  const uint4* hsrc_l = reinterpret_cast<const uint4*>(a.hlo + (uint64_t)r * (k + 1) * Imax);
-  const uint4* hsrc_c = reinterpret_cast<const uint4*>(a.hc + (uint64_t)r * (k + 1) * (Imax / 32));
-  // three named registers (not an array, which would live in scratch)
-  const int hlast = 2 * nh + nc - 1;
-  auto hpiece = [&](int i) -> uint4 {
-    i = i % (hlast + 1);      // surplus threads re-read other pieces (distinct lines)
-    return *(i < nh ? hsrc_h + i : (i < 2 * nh ? hsrc_l + (i - nh) : hsrc_c + (i - 2 * nh)));
-  };
-  uint4 hv0, hv1, hv2;
-  if constexpr (HV > 0) {
-    hv0 = hpiece(tid);
-    hv1 = hpiece(tid + nthr);
-    hv2 = hpiece(tid + 2 * nthr);
-    asm volatile("" ::: "memory");   // these loads go out before the weight loads
-  } else {
-    const uint4* src[3] = {hsrc_h, hsrc_l, hsrc_c};
-    uint4* dst[3] = {reinterpret_cast<uint4*>(hhl), reinterpret_cast<uint4*>(hll), reinterpret_cast<uint4*>(hcl)};
-    const int np[3] = {nh, nh, nc};
-#pragma unroll
-    for (int part = 0; part < 3; ++part)
-      for (int base = wi * 64; base < np[part]; base += nthr) {
-        if (base + lane < np[part])
-          __builtin_amdgcn_global_load_lds(src[part] + base + lane,
-                                           (__attribute__((address_space(3))) void*)(dst[part] + base), 16, 0, 0);
-      }
-  }
-  // routed slot j, blocks kp, kp + KS, ... of its intermediate axis
   const bool valid = e >= 0 && e < a.E;
   const rsrc_t rr = make_rsrc(a.base + a.rt.base_off + (uint64_t)(valid ? e : 0) * a.rt.stride, a.rt.blk_bytes);
   const uint32_t rcodes = (uint32_t)a.rt.dn_codes, rscales = (uint32_t)a.rt.dn_scales;
@@ -492,6 +517,15 @@ __global__ __launch_bounds__(1024) void k_dec_down(DecodeArgs a) {
   // loads a valid one and ignores it) so that the wait counts stay exact
   const bool has_blk = kp < rnkb;
   const int kb0 = min(kp, rnkb - 1);
+  const uint64_t srow = (uint64_t)r * (k + 1);
+  constexpr int SG = Fmt<FS>::G;
+  const int sng = a.sh.inter / SG;
+  const int g0 = min(wi, sng - 1);
+  // this wave's h first (the routed block, the first shared group): the
+  // wait for it before the LDS stores leaves the weight loads in flight
+  const HBlk hb = dn_load_block(a, srow + j, kb0, lane);
+  const HGrp<SG> hg = dn_load_group<SG>(a, srow + k, g0, lane);
+  asm volatile("" ::: "memory");
   load_scales_rs<FR>(rr, scale_voff<FR>(lane), rscales + (uint32_t)sblk_off<FR>(t, kb0, rnkb), scr);
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc)
@@ -500,37 +534,25 @@ __global__ __launch_bounds__(1024) void k_dec_down(DecodeArgs a) {
   constexpr int SCPG = Fmt<FS>::G / 32;
   const rsrc_t rs = make_rsrc(a.base + a.sh.base_off, a.sh.blk_bytes);
   const uint32_t scodes = (uint32_t)a.sh.dn_codes, sscales = (uint32_t)a.sh.dn_scales;
-  const int snch = a.sh.inter / 32, snkb = a.sh.inter / KBLK, sng = a.sh.inter / Fmt<FS>::G;
+  const int snch = a.sh.inter / 32, snkb = a.sh.inter / KBLK;
   uint32_t wsh[SCPG][Fmt<FS>::WORDS], scs = 0;
-  {
-    const int g0 = min(wi, sng - 1);
-    scs = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)group_word_voff<FS>(g0, lane),
-                                               (int)(sscales + (uint32_t)sblk_off<FS>(t, g0 / (KBLK / Fmt<FS>::G), snkb)), 0);
+  scs = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)group_word_voff<FS>(g0, lane),
+                                             (int)(sscales + (uint32_t)sblk_off<FS>(t, g0 / (KBLK / Fmt<FS>::G), snkb)), 0);
 #pragma unroll
-    for (int cc = 0; cc < SCPG; ++cc)
-      load_chunk_rs<FS>(rs, chunk_voff<FS>(lane), scodes + (uint32_t)chunk_off<FS>(t, g0 * SCPG + cc, snch), wsh[cc]);
-  }
-  if constexpr (HV > 0) {
-    // hi, lo and the sums are contiguous in LDS as they are in the workspace
-    // surplus threads rewrite a piece with the same bytes
-    uint4* hd = reinterpret_cast<uint4*>(hhl);
-    hd[tid % (hlast + 1)] = hv0;
-    hd[(tid + nthr) % (hlast + 1)] = hv1;
-    hd[(tid + 2 * nthr) % (hlast + 1)] = hv2;
-  }
-  __syncthreads();
+  for (int cc = 0; cc < SCPG; ++cc)
+    load_chunk_rs<FS>(rs, chunk_voff<FS>(lane), scodes + (uint32_t)chunk_off<FS>(t, g0 * SCPG + cc, snch), wsh[cc]);
+  dn_store_block(hb, wr_l, lane);
+  dn_store_group<SG>(hg, ws_l, lane);
   float e_out = 0.f;
   if (has_blk) {
-    const uint32_t* hh = hhl + j * (Imax / 2) + kp * (KBLK / 2);
-    const uint32_t* hl = hll + j * (Imax / 2) + kp * (KBLK / 2);
-    e_out = dn_block<FR>(wr, scr, hh, hl, hcl + j * (Imax / 32) + kp * 8, e_out);
+    e_out = dn_block<FR>(wr, scr, wr_l, wr_l + 128, reinterpret_cast<const float*>(wr_l + 256), e_out);
     for (int kb = kp + DN_KS; kb < rnkb; kb += DN_KS) {
       load_scales_rs<FR>(rr, scale_voff<FR>(lane), rscales + (uint32_t)sblk_off<FR>(t, kb, rnkb), scr);
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc)
         load_chunk_rs<FR>(rr, chunk_voff<FR>(lane), rcodes + (uint32_t)chunk_off<FR>(t, kb * 8 + cc, rnch), wr[cc]);
-      e_out = dn_block<FR>(wr, scr, hhl + j * (Imax / 2) + kb * (KBLK / 2),
-                           hll + j * (Imax / 2) + kb * (KBLK / 2), hcl + j * (Imax / 32) + kb * 8, e_out);
+      dn_store_block(dn_load_block(a, srow + j, kb, lane), wr_l, lane);
+      e_out = dn_block<FR>(wr, scr, wr_l, wr_l + 128, reinterpret_cast<const float*>(wr_l + 256), e_out);
     }
   }
   if (!valid) e_out = 0.f;
@@ -542,9 +564,9 @@ __global__ __launch_bounds__(1024) void k_dec_down(DecodeArgs a) {
         load_chunk_rs<FS>(rs, chunk_voff<FS>(lane), scodes + (uint32_t)chunk_off<FS>(t, g * SCPG + cc, snch), wsh[cc]);
       scs = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)group_word_voff<FS>(g, lane),
                                                  (int)(sscales + (uint32_t)sblk_off<FS>(t, g / (KBLK / Fmt<FS>::G), snkb)), 0);
+      dn_store_group<SG>(dn_load_group<SG>(a, srow + k, g, lane), ws_l, lane);
     }
-    s_out += dn_group<FS>(wsh, scs, g, hhl + k * (Imax / 2) + g * (Fmt<FS>::G / 2),
-                          hll + k * (Imax / 2) + g * (Fmt<FS>::G / 2), hcl + k * (Imax / 32) + g * SCPG);
+    s_out += dn_group<FS>(wsh, scs, g, ws_l, ws_l + Fmt<FS>::G / 2, reinterpret_cast<const float*>(ws_l + Fmt<FS>::G));
   }
   es[wi * 64 + lane] = e_out;
   ps[wi * 64 + lane] = s_out;
@@ -573,7 +595,8 @@ size_t decode_gu_smem(int R, int H) {
   return (size_t)R * H * 2 + (size_t)R * (H / 32) * 4 + 2 * (size_t)std::min(8, H / KBLK) * 64 * 4;
 }
 size_t decode_dn_smem(int k, int Imax) {
-  return (size_t)(k + 1) * Imax * 2 * 2 + (size_t)(k + 1) * (Imax / 32) * 4 + 2 * (size_t)k * DN_KS * 64 * 4;
+  (void)Imax;
+  return (size_t)k * DN_KS * (DN_WW * 4 + 2 * 64 * 4);
 }
 
 template <typename K>
@@ -603,11 +626,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t
   hipError_t err = a.act_fp16 ? launch_gateup<FR, FS, 1>(a, s, ev, nw, gsm) : launch_gateup<FR, FS, 0>(a, s, ev, nw, gsm);
   if (err != hipSuccess) return err;
   const int dthr = 64 * a.k * DN_KS;
-  const int hpieces = (a.k + 1) * a.Imax / 4 + (a.k + 1) * a.Imax / 128;
-  if (hpieces <= 3 * dthr)
-    launch_k(k_dec_down<FR, FS, 3>, dim3((a.H / 64) * a.R), dim3(dthr), (uint32_t)dsm, s, ev, 2, a);
-  else
-    launch_k(k_dec_down<FR, FS, 0>, dim3((a.H / 64) * a.R), dim3(dthr), (uint32_t)dsm, s, ev, 2, a);
+  if ((err = allow_smem(k_dec_down<FR, FS>, dsm)) != hipSuccess) return err;
+  launch_k(k_dec_down<FR, FS>, dim3((a.H / 64) * a.R), dim3(dthr), (uint32_t)dsm, s, ev, 2, a);
   return hipGetLastError();
 }
 
