@@ -6,7 +6,7 @@
 // of the interleaved gate/up matrix). Workgroup b takes items b, b + G, ...;
 // wave w owns the 256-wide K slice w, one weight row per lane, and streams
 // the tile's packed codes once (coalesced 128-bit loads) for every row that
-// picked the expert, so rows sharing an expert share its reads ("Native
+// picked the expert (the dots on 4x4x4 MFMAs, up to four rows per pass), so rows sharing an expert share its reads ("Native
 // server: --backend xpu for Nemotron on Intel Arc", review comments: each
 // extra row costs more because more distinct experts are read). The codes
 // and scale words of the next item are in flight while the current one is
@@ -128,17 +128,97 @@ __device__ __forceinline__ void gu_issue(const GuItem& it, int wv, int nch, int 
   else load_slice<FR>(it.r, it.codes, it.scales, it.tl, wv, nch, nkb, lane, b);
 }
 
-// One row of an item: the wave's slice dot from the activations in LDS.
-// Chunks are unpacked one at a time (the group's pair dots chain in order).
+// Up to 4 rows of an item against the wave's K slice on the matrix cores.
+// v_mfma_f32_4x4x4 (16 blocks): B = the weights, lane l = weight row l
+// (block l/4, column l%4), 4 consecutive k per step from its own unpacked
+// pairs; A = the activations, lane l supplies row slot l%4 of its block
+// (every block sees the same rows); result register v of lane l = slot v's
+// dot with weight row l. So each lane ends with its own row's dots for the
+// four slots, and each output element is formed from its own row and slot
+// alone. Per 64-wide group: acc = sum of the pair products over the group's
+// chunks in k order, then out += ms*acc + bm*X (X: the group's activation
+// sum), as the pair-dot form. xr: this lane's slot row in LDS; xs0..3: the
+// four slots' rows of chunk sums.
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+template <int ACT16>
+__device__ __forceinline__ f4v mfma4(uint32_t x0, uint32_t x1, uint32_t w0, uint32_t w1, f4v acc) {
+  if constexpr (ACT16) {
+    const h4v xa = __builtin_bit_cast(h4v, make_uint2(x0, x1));
+    const h4v wb = __builtin_bit_cast(h4v, make_uint2(w0, w1));
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(xa, wb, acc, 0, 0, 0);
+  } else {
+    const s4v xa = __builtin_bit_cast(s4v, make_uint2(x0, x1));
+    const s4v wb = __builtin_bit_cast(s4v, make_uint2(w0, w1));
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xa, wb, acc, 0, 0, 0);
+  }
+}
+
+// The pair unpack of one chunk for the matrix-core form: the same values
+// as unpack_for, written as plain code on masks the compiler cannot see as
+// constants, so it still selects one v_and_or_b32 per pair and, unlike for
+// inline asm, tracks the wait states a VALU write needs before a matrix-core
+// read of the same register.
+struct PairMasks {
+  uint32_t m, c, q0, q1, q2;   // field mask, 1.0 pair, 3-bit last-pair masks
+};
 template <int F, int ACT16>
-__device__ __forceinline__ float gu_slice_dot(const uint32_t (*w)[4], const uint32_t* sc, const uint32_t* xrow,
-                                              const float* csrow, int sl, float out) {
+__device__ __forceinline__ PairMasks pair_masks() {
+  PairMasks k;
+  if constexpr (F == F_Q3) {
+    k.m = ACT16 ? 0x01C001C0u : 0x00380038u;
+    k.q0 = ACT16 ? 0x00400040u : 0x00080008u;
+    k.q1 = ACT16 ? 0x00800080u : 0x00100010u;
+    k.q2 = ACT16 ? 0x01000100u : 0x00200020u;
+  } else {
+    k.m = ACT16 ? 0x03C003C0u : 0x00780078u;
+    k.q0 = k.q1 = k.q2 = 0u;
+  }
+  k.c = ACT16 ? 0x3C003C00u : 0x3F803F80u;
+  asm volatile("" : "+s"(k.m), "+s"(k.q0), "+s"(k.q1), "+s"(k.q2), "+v"(k.c));
+  return k;
+}
+template <int F, int ACT16>
+__device__ __forceinline__ void unpack_pairs(const uint32_t* w, const PairMasks& k, uint32_t* o) {
+  if constexpr (F == F_Q3) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const uint32_t v = w[i];
+      o[5 * i + 0] = ((ACT16 ? v << 6 : v << 3) & k.m) | k.c;
+      o[5 * i + 1] = ((ACT16 ? v << 3 : v) & k.m) | k.c;
+      o[5 * i + 2] = ((ACT16 ? v : v >> 3) & k.m) | k.c;
+      o[5 * i + 3] = ((ACT16 ? v >> 3 : v >> 6) & k.m) | k.c;
+      o[5 * i + 4] = ((ACT16 ? v >> 6 : v >> 9) & k.m) | k.c;
+    }
+    const uint32_t t0 = ((w[0] >> (ACT16 ? 9 : 12)) & k.q0) | k.c;
+    const uint32_t t1 = ((w[1] >> (ACT16 ? 8 : 11)) & k.q1) | t0;
+    o[15] = ((w[2] >> (ACT16 ? 7 : 10)) & k.q2) | t1;
+  } else {   // 4-bit affine or symmetric
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = w[i];
+      o[4 * i + 0] = ((ACT16 ? v << 6 : v << 3) & k.m) | k.c;
+      o[4 * i + 1] = ((ACT16 ? v << 2 : v >> 1) & k.m) | k.c;
+      o[4 * i + 2] = ((ACT16 ? v >> 2 : v >> 5) & k.m) | k.c;
+      o[4 * i + 3] = ((ACT16 ? v >> 6 : v >> 9) & k.m) | k.c;
+    }
+  }
+}
+
+template <int F, int ACT16>
+__device__ __forceinline__ f4v gu_slice_mfma(const uint32_t (*w)[4], const uint32_t* sc, const uint32_t* xr,
+                                             const float* xs0, const float* xs1, const float* xs2,
+                                             const float* xs3, int sl, f4v out) {
   constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
+  const PairMasks pk = pair_masks<F, ACT16>();
 #pragma unroll
   for (int gi = 0; gi < GPS; ++gi) {
     float ms, bm;
     coef_reg<F>(sc, gi, ms, bm);
-    float acc = 0.f, X = 0.f;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    float X0 = 0.f, X1 = 0.f, X2 = 0.f, X3 = 0.f;
 #pragma unroll
     for (int cc = 0; cc < CPG; ++cc) {
       const int c = gi * CPG + cc;
@@ -147,27 +227,34 @@ __device__ __forceinline__ float gu_slice_dot(const uint32_t (*w)[4], const uint
       for (int q = 0; q < Fmt<F>::WORDS; ++q) {
         wc[q] = w[c][q];
         // opaque to loop-invariant motion: the unpack stays beside its use
-        // instead of being hoisted out of the row loop for every chunk
+        // instead of being hoisted out of the pass loop for every chunk
         asm volatile("" : "+v"(wc[q]));
       }
-      unpack_for<F, ACT16>(wc, v);
-      const uint4* q = reinterpret_cast<const uint4*>(xrow + (sl * KBLK + 32 * c) / 2);
+      unpack_pairs<F, ACT16>(wc, pk, v);
+      const uint4* q = reinterpret_cast<const uint4*>(xr + (sl * KBLK + 32 * c) / 2);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint4 tq = q[u];
         av[4 * u] = tq.x; av[4 * u + 1] = tq.y; av[4 * u + 2] = tq.z; av[4 * u + 3] = tq.w;
       }
-      acc = ACT16 ? dot_chunk_h(v, av, acc) : dot_chunk_bf(v, av, acc);
-      X += csrow[sl * 8 + c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = mfma4<ACT16>(av[2 * i], av[2 * i + 1], v[2 * i], v[2 * i + 1], acc);
+      X0 += xs0[sl * 8 + c];
+      X1 += xs1[sl * 8 + c];
+      X2 += xs2[sl * 8 + c];
+      X3 += xs3[sl * 8 + c];
     }
-    out = fmaf(ms, acc, out);
-    out = fmaf(bm, X, out);
+    out[0] = fmaf(bm, X0, fmaf(ms, acc[0], out[0]));
+    out[1] = fmaf(bm, X1, fmaf(ms, acc[1], out[1]));
+    out[2] = fmaf(bm, X2, fmaf(ms, acc[2], out[2]));
+    out[3] = fmaf(bm, X3, fmaf(ms, acc[3], out[3]));
   }
   return out;
 }
 
-// Wave 0 after the barrier: g and u of the tile's 32 intermediate indices
-// (slices added in slice order), h = silu(g) u, split and stored.
+// One wave after the barrier, for one row: g and u of the tile's 32
+// intermediate indices (slices added in slice order), h = silu(g) u, split
+// and stored.
 __device__ __forceinline__ void gu_finish(const DecodeArgs& a, const float* red, int nw, int r, int j,
                                           int t, int lane) {
   const int k = a.k;
@@ -198,6 +285,15 @@ __device__ __forceinline__ void gu_finish(const DecodeArgs& a, const float* red,
   }
 }
 
+__device__ __forceinline__ int pick4(int v, int a0, int a1, int a2, int a3) {
+  return v == 0 ? a0 : v == 1 ? a1 : v == 2 ? a2 : a3;   // selects, not an indexed array (scratch)
+}
+
+// The rows of an item in passes of up to 4 (slot order = pick order): the
+// slice dots of a pass, the partials of every wave to LDS, one barrier, then
+// wave v finishes the pass's slot v. Slots past the pass's rows repeat its
+// first row; their results are not used. With fewer waves than slots a
+// wave finishes several.
 template <int F, int ACT16>
 __device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P, const GuItem& it,
                                              const SliceBuf& b, const uint32_t* xl, const float* cs,
@@ -210,27 +306,40 @@ __device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P
     m1 = __ballot(P.id1 == it.e);
     n = __popcll(m0) + __popcll(m1);
   }
-  for (int i = 0; i < n; ++i) {
-    int r = it.e, j = k;
-    if (!it.shared) {
-      int s;
-      if (m0) { s = __ffsll((unsigned long long)m0) - 1; m0 &= m0 - 1; }
-      else { s = 64 + __ffsll((unsigned long long)m1) - 1; m1 &= m1 - 1; }
-      r = s / k;
-      j = s % k;
+  for (int i = 0; i < n; i += 4) {
+    const int m = min(4, n - i);
+    int rr[4], jj[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      int r = it.e, j = k;
+      if (!it.shared && v < m) {
+        int s;
+        if (m0) { s = __ffsll((unsigned long long)m0) - 1; m0 &= m0 - 1; }
+        else { s = 64 + __ffsll((unsigned long long)m1) - 1; m1 &= m1 - 1; }
+        r = s / k;
+        j = s % k;
+      }
+      rr[v] = (v == 0 || v < m) ? r : rr[0];
+      jj[v] = (v == 0 || v < m) ? j : jj[0];
     }
-    const uint32_t* xrow = xl + (uint64_t)r * (H / 2);
-    const float* csrow = cs + r * nch;
-    float out = gu_slice_dot<F, ACT16>(b.w, b.sc, xrow, csrow, wv, 0.f);
+    const int rl = pick4(lane & 3, rr[0], rr[1], rr[2], rr[3]);
+    const uint32_t* xr = xl + (uint64_t)rl * (H / 2);
+    const float *xs0 = cs + rr[0] * nch, *xs1 = cs + rr[1] * nch, *xs2 = cs + rr[2] * nch, *xs3 = cs + rr[3] * nch;
+    f4v out = {0.f, 0.f, 0.f, 0.f};
+    out = gu_slice_mfma<F, ACT16>(b.w, b.sc, xr, xs0, xs1, xs2, xs3, wv, out);
     for (int sl = wv + nw; sl < nsl; sl += nw) {     // hidden > 256 * waves: further slices in place
       SliceBuf c2;
       load_slice<F>(it.r, it.codes, it.scales, it.tl, sl, nch, nsl, lane, c2);
-      out = gu_slice_dot<F, ACT16>(c2.w, c2.sc, xrow, csrow, sl, out);
+      out = gu_slice_mfma<F, ACT16>(c2.w, c2.sc, xr, xs0, xs1, xs2, xs3, sl, out);
     }
-    float* rbuf = red + rb * (nw * 64);
-    rbuf[wv * 64 + lane] = out;
+    float* rbuf = red + rb * (4 * nw * 64);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (v < m) rbuf[(v * nw + wv) * 64 + lane] = out[v];
     __syncthreads();
-    if (wv == 0) gu_finish(a, rbuf, nw, r, j, it.t, lane);
+    for (int v = wv; v < m; v += nw)    // fewer waves than slots: waves take several
+      gu_finish(a, rbuf + v * nw * 64, nw, pick4(v, rr[0], rr[1], rr[2], rr[3]),
+                pick4(v, jj[0], jj[1], jj[2], jj[3]), it.t, lane);
     rb ^= 1;   // the other buffer next: its readers passed this barrier
   }
 }
@@ -253,7 +362,7 @@ __device__ __forceinline__ void gu_process(const DecodeArgs& a, const Picks& P, 
 // before the item's loads, so the compiler can count what is outstanding and
 // the wait for them leaves the item's loads in flight; XV == 0 (many rows)
 // copies them straight into LDS instead. LDS: activations [R][H] u16, chunk
-// sums [R][H/32] f32, two reduction buffers [nw][64] f32.
+// sums [R][H/32] f32, two reduction buffers [4][nw][64] f32.
 struct GuCtx {
   uint32_t* xl;
   float* cs;
@@ -592,7 +701,7 @@ __global__ __launch_bounds__(1024) void k_dec_down(DecodeArgs a) {
 constexpr int GU_GRID = 256;   // persistent gate/up workgroups (a multiple of 8)
 
 size_t decode_gu_smem(int R, int H) {
-  return (size_t)R * H * 2 + (size_t)R * (H / 32) * 4 + 2 * (size_t)std::min(8, H / KBLK) * 64 * 4;
+  return (size_t)R * H * 2 + (size_t)R * (H / 32) * 4 + 2 * 4 * (size_t)std::min(8, H / KBLK) * 64 * 4;
 }
 size_t decode_dn_smem(int k, int Imax) {
   (void)Imax;
