@@ -472,9 +472,10 @@ __device__ __forceinline__ void slice_dot(const uint32_t (&w)[8][Fmt<F>::WORDS],
   }
 }
 
-// The k best of up to 256 candidates held by one wave (lane l holds
-// candidates l + 64 i, i = 0..3, with their order keys; key 0 = absent),
-// ranked by (key desc, id asc). Every lane must be active. Steps:
+// The k best of up to 64 * NC candidates held by one wave (lane l holds
+// column i's candidate with its order key and id; key 0 = absent), ranked by
+// (key desc, id asc); ids must grow with (column, lane) so that lane order
+// settles ties. Every lane must be active. Steps:
 //  1. T = the k-th largest key, bit by bit from the top: a bit stays set when
 //     at least k keys are >= the prefix with it (one ballot per candidate
 //     column and bit);
@@ -484,25 +485,27 @@ __device__ __forceinline__ void slice_dot(const uint32_t (&w)[8][Fmt<F>::WORDS],
 //     picks' keys and ids.
 // On return lane j < k holds slot s_j (distinct, 0..k-1) with its id and
 // value; lanes >= k hold slot k.
-__device__ __forceinline__ void wave_topk(const uint32_t (&key)[4], const float (&val)[4], int lane, int k,
-                                          uint32_t* scratch /* wave-private LDS, 24 u32 */, int& slot,
-                                          int& id, float& v) {
+template <int NC>
+__device__ __forceinline__ void wave_topk_ids(const uint32_t (&key)[NC], const float (&val)[NC],
+                                              const int (&idv)[NC], int lane, int k,
+                                              uint32_t* scratch /* wave-private LDS, 24 u32 */, int& slot,
+                                              int& id, float& v) {
   uint32_t T = 0;
 #pragma unroll 4
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = T | (1u << b);
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    for (int i = 0; i < NC; ++i) cnt += __popcll(__ballot(key[i] >= c));
     T = cnt >= k ? c : T;
   }
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   int need = k, before = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) need -= __popcll(__ballot(key[i] > T));
-  bool sel[4];
+  for (int i = 0; i < NC; ++i) need -= __popcll(__ballot(key[i] > T));
+  bool sel[NC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NC; ++i) {
     const uint64_t eq = __ballot(key[i] == T);
     const int tie_rank = before + __popcll(eq & lt);
     sel[i] = key[i] > T || (key[i] == T && tie_rank < need);
@@ -510,12 +513,12 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[4], const float 
   }
   int pos = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NC; ++i) {
     const uint64_t sm = __ballot(sel[i]);
     if (sel[i]) {
       const int p = pos + __popcll(sm & lt);
       scratch[p] = key[i];
-      scratch[8 + p] = (uint32_t)(lane + 64 * i);
+      scratch[8 + p] = (uint32_t)idv[i];
       scratch[16 + p] = __float_as_uint(val[i]);
     }
     pos += __popcll(sm);
@@ -535,6 +538,12 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[4], const float 
     }
   }
   slot = lane < k ? s : k;
+}
+// 256 candidates, lane l holding ids l + 64 i
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[4], const float (&val)[4], int lane, int k,
+                                          uint32_t* scratch, int& slot, int& id, float& v) {
+  const int idv[4] = {lane, lane + 64, lane + 128, lane + 192};
+  wave_topk_ids<4>(key, val, idv, lane, k, scratch, slot, id, v);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

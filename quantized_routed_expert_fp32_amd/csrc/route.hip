@@ -10,9 +10,10 @@
 // (NaN above +inf above every finite logit), the keys above it plus the
 // lowest ids among its ties, slots by (key desc, id asc); then
 // exp(l - l_top) / sum in slot order and sigmoid of the gate logit.
-//  * decode batches (k_route): one launch; the logits go out with
-//    write-through stores, and the last of a row's tile workgroups to arrive
-//    (a per-row counter in the workspace, reset by that workgroup) picks.
+//  * decode batches (k_route): one launch; each tile workgroup picks its
+//    own k best, sends them out with write-through stores, and the last of
+//    a row's tile workgroups to arrive (a per-row counter in the workspace,
+//    reset by that workgroup) picks from the tiles' picks.
 //  * prompt chunks: logits of 32 rows x 64 experts per workgroup on MFMA
 //    (k_route_mfma, 4-bit router codes) or 8 rows per workgroup on the
 //    vector units (k_route_logits), then one wave per row picks in a second
@@ -145,15 +146,17 @@ __global__ __launch_bounds__(512) void k_route_logits(RouteArgs a, const uint16_
   }
 }
 
-// Top k of one row from its keys and values (lane l: experts l + 64 i),
-// then weights exp(l_j - l_top) / sum over the k picks in slot order, and
-// sigmoid of the gate logit c. One wave.
-__device__ __forceinline__ void pick_and_store(const RouteArgs& a, int row, const uint32_t (&key)[4],
-                                               const float (&v)[4], float c, int lane, uint32_t* scr) {
+// Top k of one row from its candidates (keys, values, expert ids; see
+// wave_topk_ids), then weights exp(l_j - l_top) / sum over the k picks in
+// slot order, and sigmoid of the gate logit c. One wave.
+template <int NC>
+__device__ __forceinline__ void pick_and_store_n(const RouteArgs& a, int row, const uint32_t (&key)[NC],
+                                                 const float (&v)[NC], const int (&idv)[NC], float c, int lane,
+                                                 uint32_t* scr) {
   const int k = a.k;
   int slot, id;
   float val;
-  wave_topk(key, v, lane, k, scr, slot, id, val);
+  wave_topk_ids<NC>(key, v, idv, lane, k, scr, slot, id, val);
   // into slot order
   if (lane < k) {
     scr[slot] = (uint32_t)id;
@@ -174,13 +177,22 @@ __device__ __forceinline__ void pick_and_store(const RouteArgs& a, int row, cons
   }
   if (lane == 0) a.sg[row] = 1.0f / (1.0f + expf(-c));
 }
+// all E <= 256 experts of a row, lane l holding experts l + 64 i
+__device__ __forceinline__ void pick_and_store(const RouteArgs& a, int row, const uint32_t (&key)[4],
+                                               const float (&v)[4], float c, int lane, uint32_t* scr) {
+  const int idv[4] = {lane, lane + 64, lane + 128, lane + 192};
+  pick_and_store_n<4>(a, row, key, v, idv, c, lane, scr);
+}
 
-// Decode batches: logits of one (tile of 64 experts, row) workgroup go to
-// the workspace with write-through stores (visible device-wide once the
-// store has completed); each wave waits for its stores, then one thread
-// counts the row's arrivals; the last tile workgroup reads the row back
-// (loads that bypass this XCD's L2) and picks. Tile 0's last wave also
-// forms the gate-row logit.
+// Decode batches: one workgroup per (tile of 64 experts, row) forms the
+// tile's logits and picks the tile's own k best (the k best of a row are
+// among the union of its tiles' k best under the same order); those k
+// (value, id) entries go to the workspace with write-through stores
+// (visible device-wide once the store has completed); each wave waits for
+// its stores, then one thread counts the row's arrivals; the last tile
+// workgroup reads the row's E/64 * k entries back (loads that bypass this
+// XCD's L2) and picks from them. Tile 0's last wave also forms the
+// gate-row logit.
 template <int FR, int FG, int ACT16>
 __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __restrict__ x) {
   __shared__ float red[8][64];
@@ -216,11 +228,24 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
     if (lane == 0) __hip_atomic_store(&a.gl_ws[row], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  const int k = a.k;
+  float* cand = a.lg_ws + (uint64_t)row * E;    // per tile: k values, then k ids (16 words)
   if (w == 0) {
     float l = 0.f;
     for (int q = 0; q < nw; ++q) l += red[q][lane];
-    __hip_atomic_store(&a.lg_ws[(uint64_t)row * E + 64 * t + lane], l, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    const int e = 64 * t + lane;
+    const float v1[1] = {a.bias ? l + a.bias[e] : l};
+    if (a.logits) a.logits[(uint64_t)row * (E + 1) + e] = v1[0];
+    const uint32_t k1[1] = {pick_key(v1[0])};
+    const int i1[1] = {e};
+    int slot, id;
+    float val;
+    wave_topk_ids<1>(k1, v1, i1, lane, k, scr, slot, id, val);   // lane j < k: the tile's j-th pick by id
+    if (lane < k) {
+      __hip_atomic_store(&cand[16 * t + lane], val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(reinterpret_cast<int*>(cand) + 16 * t + 8 + lane, id, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's stores have completed
   __syncthreads();
@@ -231,24 +256,18 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
   }
   __syncthreads();
   if (!s_last || w != 0) return;
-  float v[4];
-  uint32_t key[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    const int ec = min(e, E - 1);
-    const float l = __hip_atomic_load(&a.lg_ws[(uint64_t)row * E + ec], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    v[i] = a.bias ? l + a.bias[ec] : l;
-    key[i] = e < E ? pick_key(v[i]) : 0u;
-  }
+  // lane j < ntile * k: entry j % k of tile j / k (ids grow with the lane)
+  const int nc = ntile * k;
+  const int jt = min(lane, nc - 1) / k, ji = min(lane, nc - 1) % k;
+  const float cv = __hip_atomic_load(&cand[16 * jt + ji], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int ci = __hip_atomic_load(reinterpret_cast<const int*>(cand) + 16 * jt + 8 + ji, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
   const float c = __hip_atomic_load(&a.gl_ws[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (a.logits) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) a.logits[(uint64_t)row * (E + 1) + lane + 64 * i] = v[i];
-    if (lane == 0) a.logits[(uint64_t)row * (E + 1) + E] = c;
-  }
-  pick_and_store(a, row, key, v, c, lane, scr);
+  if (a.logits && lane == 0) a.logits[(uint64_t)row * (E + 1) + E] = c;
+  const float v1[1] = {cv};
+  const uint32_t k1[1] = {lane < nc ? pick_key(cv) : 0u};
+  const int i1[1] = {ci};
+  pick_and_store_n<1>(a, row, k1, v1, i1, c, lane, scr);
 }
 
 // Prompt chunks: logits of 32 rows x 64 experts per workgroup on 16-bit
