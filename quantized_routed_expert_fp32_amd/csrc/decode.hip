@@ -107,25 +107,50 @@ struct GuItem {
   int e;        // expert (routed) or the row (shared)
 };
 
-__device__ __forceinline__ GuItem gu_item(const DecodeArgs& a, const Picks& P, int item, int Tmax) {
+// What an item needs of its expert class, read once from the arguments and
+// held in registers (opaque to the compiler, which would otherwise reload
+// the argument block with a wait for each item's address).
+struct GuCls {
+  uint64_t base_off, stride;
+  uint32_t codes, scales, blk_bytes;
+  int tlast;   // last gate/up tile of the class
+};
+__device__ __forceinline__ GuCls gu_cls(const ExpertClass& c) {
+  GuCls g;
+  g.base_off = c.base_off;
+  g.stride = c.stride;
+  g.codes = (uint32_t)c.gu_codes;
+  g.scales = (uint32_t)c.gu_scales;
+  g.blk_bytes = c.blk_bytes;
+  g.tlast = 2 * c.inter / 64 - 1;
+  asm volatile("" : "+s"(g.base_off), "+s"(g.stride), "+s"(g.codes), "+s"(g.scales), "+s"(g.blk_bytes),
+               "+s"(g.tlast));
+  return g;
+}
+
+__device__ __forceinline__ GuItem gu_item(const uint8_t* base, const GuCls& rc, const GuCls& sc, const Picks& P,
+                                          int item, int Tmax) {
   GuItem it;
   const int u = item / Tmax;
   it.t = item % Tmax;
   it.shared = u >= P.nrt;
-  const ExpertClass& ec = it.shared ? a.sh : a.rt;
   it.e = it.shared ? u - P.nrt : unit_expert(P, u);
-  const uint8_t* blk = a.base + ec.base_off + (it.shared ? 0 : (uint64_t)it.e * ec.stride);
-  it.r = make_rsrc(blk, ec.blk_bytes);
-  it.codes = (uint32_t)ec.gu_codes;
-  it.scales = (uint32_t)ec.gu_scales;
-  it.tl = min(it.t, 2 * ec.inter / 64 - 1);
+  const uint64_t off = it.shared ? sc.base_off : rc.base_off + (uint64_t)it.e * rc.stride;
+  it.r = make_rsrc(base + off, it.shared ? sc.blk_bytes : rc.blk_bytes);
+  it.codes = it.shared ? sc.codes : rc.codes;
+  it.scales = it.shared ? sc.scales : rc.scales;
+  it.tl = min(it.t, it.shared ? sc.tlast : rc.tlast);
   return it;
 }
 
 template <int FR, int FS>
 __device__ __forceinline__ void gu_issue(const GuItem& it, int wv, int nch, int nkb, int lane, SliceBuf& b) {
-  if (it.shared) load_slice<FS>(it.r, it.codes, it.scales, it.tl, wv, nch, nkb, lane, b);
-  else load_slice<FR>(it.r, it.codes, it.scales, it.tl, wv, nch, nkb, lane, b);
+  if constexpr (FR == FS) {
+    load_slice<FR>(it.r, it.codes, it.scales, it.tl, wv, nch, nkb, lane, b);
+  } else {
+    if (it.shared) load_slice<FS>(it.r, it.codes, it.scales, it.tl, wv, nch, nkb, lane, b);
+    else load_slice<FR>(it.r, it.codes, it.scales, it.tl, wv, nch, nkb, lane, b);
+  }
 }
 
 // Up to 4 rows of an item against the wave's K slice on the matrix cores.
@@ -349,8 +374,12 @@ __device__ __forceinline__ void gu_process(const DecodeArgs& a, const Picks& P, 
                                            const SliceBuf& b, const uint32_t* xl, const float* cs,
                                            float* red, int& rb, int wv, int nw, int lane) {
   if (it.t != it.tl) return;      // tile beyond this class (intermediates differ)
-  if (it.shared) gu_process_t<FS, ACT16>(a, P, it, b, xl, cs, red, rb, wv, nw, lane);
-  else gu_process_t<FR, ACT16>(a, P, it, b, xl, cs, red, rb, wv, nw, lane);
+  if constexpr (FR == FS) {        // one copy of the code when both classes share a format
+    gu_process_t<FR, ACT16>(a, P, it, b, xl, cs, red, rb, wv, nw, lane);
+  } else {
+    if (it.shared) gu_process_t<FS, ACT16>(a, P, it, b, xl, cs, red, rb, wv, nw, lane);
+    else gu_process_t<FR, ACT16>(a, P, it, b, xl, cs, red, rb, wv, nw, lane);
+  }
 }
 
 
@@ -411,7 +440,9 @@ __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
   if (it_i >= c.n_items) return;
   const int G = gridDim.x;
   SliceBuf A, B;
-  GuItem ia = gu_item(a, P, it_i, c.Tmax);
+  const GuCls rcl = gu_cls(a.rt), scl = gu_cls(a.sh);
+  const uint8_t* const base = a.base;
+  GuItem ia = gu_item(base, rcl, scl, P, it_i, c.Tmax);
   gu_issue<FR, FS>(ia, c.wv, c.nch, c.nsl, c.lane, A);
   if constexpr (XV > 0) {
     // surplus threads rewrite a piece with the same bytes
@@ -442,13 +473,13 @@ __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
     // the next item's loads go out before this item's arithmetic; past the
     // end, the current item is re-issued (its lines are in L2)
     int nx1 = it_i + G;
-    GuItem ib = nx1 < c.n_items ? gu_item(a, P, nx1, c.Tmax) : ia;
+    GuItem ib = nx1 < c.n_items ? gu_item(base, rcl, scl, P, nx1, c.Tmax) : ia;
     gu_issue<FR, FS>(ib, c.wv, c.nch, c.nsl, c.lane, B);
     gu_process<FR, FS, ACT16>(a, P, ia, A, c.xl, c.cs, c.red, rb, c.wv, c.nw, c.lane);
     if (nx1 >= c.n_items) break;
     it_i = nx1;
     int nx2 = it_i + G;
-    ia = nx2 < c.n_items ? gu_item(a, P, nx2, c.Tmax) : ib;
+    ia = nx2 < c.n_items ? gu_item(base, rcl, scl, P, nx2, c.Tmax) : ib;
     gu_issue<FR, FS>(ia, c.wv, c.nch, c.nsl, c.lane, A);
     gu_process<FR, FS, ACT16>(a, P, ib, B, c.xl, c.cs, c.red, rb, c.wv, c.nw, c.lane);
     if (nx2 >= c.n_items) break;
