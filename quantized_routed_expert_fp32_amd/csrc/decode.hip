@@ -490,36 +490,52 @@ __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
 // ------------------------------------------------------------------ down
 constexpr int DN_KS = 2;   // waves per routed slot (each 1/KS of the intermediate axis)
 
+// The dots of down on 4x4x4 MFMAs, as in gate/up: B = the lane's weight
+// row (one output column per lane), A = h with the fp16 high part in row
+// slot 0 and the low part in slot 1 (slots 2, 3 repeat them; unused), so
+// one pass gives both dots. Per group: out += ms*(dot_hi + dot_lo) + bm*X.
+// hh/hl: the fp16 pairs of the part in LDS, hc: its chunk sums.
+__device__ __forceinline__ const uint32_t* dn_slot_src(const uint32_t* hh, const uint32_t* hl) {
+  return (threadIdx.x & 1) ? hl : hh;     // lane l supplies slot l % 4
+}
+
+template <int F>
+__device__ __forceinline__ f4v dn_chunk(const uint32_t* wc, const PairMasks& pk, const uint32_t* src, f4v acc) {
+  uint32_t v[16], av[16];
+  unpack_pairs<F, 1>(wc, pk, v);
+  const uint4* q = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint4 t = q[u];
+    av[4 * u] = t.x; av[4 * u + 1] = t.y; av[4 * u + 2] = t.z; av[4 * u + 3] = t.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = mfma4<1>(av[2 * i], av[2 * i + 1], v[2 * i], v[2 * i + 1], acc);
+  return acc;
+}
+
 // Routed part: one 256-wide block (8 chunks) of one slot's h against the
-// lane's weight row. hh/hl: fp16 pairs of the block in LDS, hc: chunk sums.
+// lane's weight row.
 template <int F>
 __device__ __forceinline__ float dn_block(const uint32_t (&w)[8][Fmt<F>::WORDS], const uint32_t* sc,
                                           const uint32_t* hh, const uint32_t* hl, const float* hc,
                                           float out) {
   constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
+  const PairMasks pk = pair_masks<F, 1>();
+  const uint32_t* src = dn_slot_src(hh, hl);
 #pragma unroll
   for (int gi = 0; gi < GPS; ++gi) {
     float ms, bm;
     coef_reg<F>(sc, gi, ms, bm);
-    float acc = 0.f, X = 0.f;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    float X = 0.f;
 #pragma unroll
     for (int cc = 0; cc < CPG; ++cc) {
       const int c = gi * CPG + cc;
-      uint32_t v[16], ph[16], pl[16];
-      unpack_chunk<F>(w[c], v);
-      const uint4* qh = reinterpret_cast<const uint4*>(hh + 16 * c);
-      const uint4* ql = reinterpret_cast<const uint4*>(hl + 16 * c);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint4 th = qh[u], tl = ql[u];
-        ph[4 * u] = th.x; ph[4 * u + 1] = th.y; ph[4 * u + 2] = th.z; ph[4 * u + 3] = th.w;
-        pl[4 * u] = tl.x; pl[4 * u + 1] = tl.y; pl[4 * u + 2] = tl.z; pl[4 * u + 3] = tl.w;
-      }
-      acc = dot_chunk_h(v, ph, acc);
-      acc = dot_chunk_h(v, pl, acc);
+      acc = dn_chunk<F>(w[c], pk, src + 16 * c, acc);
       X += hc[c];
     }
-    out = fmaf(ms, acc, out);
+    out = fmaf(ms, acc[0] + acc[1], out);
     out = fmaf(bm, X, out);
   }
   return out;
@@ -534,24 +550,16 @@ __device__ __forceinline__ float dn_group(const uint32_t (*w)[Fmt<F>::WORDS], ui
   float ms, bm;
   // the word holds this group's entry: affine one u32, symmetric the u16 at gi % 2
   coef_reg<F>(sc, Fmt<F>::AFF ? 0 : (gi & 1), ms, bm);
-  float acc = 0.f, X = 0.f;
+  const PairMasks pk = pair_masks<F, 1>();
+  const uint32_t* src = dn_slot_src(hh, hl);
+  f4v acc = {0.f, 0.f, 0.f, 0.f};
+  float X = 0.f;
 #pragma unroll
   for (int cc = 0; cc < CPG; ++cc) {
-    uint32_t v[16], ph[16], pl[16];
-    unpack_chunk<F>(w[cc], v);
-    const uint4* qh = reinterpret_cast<const uint4*>(hh + 16 * cc);
-    const uint4* ql = reinterpret_cast<const uint4*>(hl + 16 * cc);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint4 th = qh[u], tl = ql[u];
-      ph[4 * u] = th.x; ph[4 * u + 1] = th.y; ph[4 * u + 2] = th.z; ph[4 * u + 3] = th.w;
-      pl[4 * u] = tl.x; pl[4 * u + 1] = tl.y; pl[4 * u + 2] = tl.z; pl[4 * u + 3] = tl.w;
-    }
-    acc = dot_chunk_h(v, ph, acc);
-    acc = dot_chunk_h(v, pl, acc);
+    acc = dn_chunk<F>(w[cc], pk, src + 16 * cc, acc);
     X += hc[cc];
   }
-  return fmaf(bm, X, fmaf(ms, acc, 0.f));
+  return fmaf(bm, X, fmaf(ms, acc[0] + acc[1], 0.f));
 }
 
 // Per-lane byte offset, inside its scale block, of the 4-byte word holding
