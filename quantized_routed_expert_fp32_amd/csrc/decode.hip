@@ -6,9 +6,10 @@
 // of the interleaved gate/up matrix). Workgroup b takes items b, b + G, ...;
 // wave w owns the 256-wide K slice w, one weight row per lane, and streams
 // the tile's packed codes once (coalesced 128-bit loads) for every row that
-// picked the expert (the dots on 4x4x4 MFMAs, up to four rows per pass), so rows sharing an expert share its reads ("Native
+// picked the expert, so rows sharing an expert share its reads ("Native
 // server: --backend xpu for Nemotron on Intel Arc", review comments: each
-// extra row costs more because more distinct experts are read). The codes
+// extra row costs more because more distinct experts are read). The dots
+// run on 4x4x4 MFMAs, up to four rows per pass. The codes
 // and scale words of the next item are in flight while the current one is
 // computed. The activations of all rows sit in LDS (loaded once per
 // workgroup) with their 32-wide chunk sums. Output: h = silu(g)*u split into
@@ -18,16 +19,19 @@
 // with KS waves per routed slot, each over 1/KS of the intermediate axis,
 // plus a share of the shared expert's groups. Each wave loads the part of
 // the row's h it reads ahead of its weights and stages it in its own LDS
-// area, so it computes as soon as its own loads have landed. The slot parts
-// are added in part order, the shared parts in wave order; wave 0 forms
-// y = sum_j p_j e_j + sigma e_shared in slot order. Blocks are mapped so the
-// rows of one tile run on one XCD and share expert tiles in its L2.
+// area, so it computes as soon as its own loads have landed; the dots run
+// on 4x4x4 MFMAs with the hi and lo parts as two rows of one pass. The slot
+// parts are added in part order, the shared parts in wave order; wave 0
+// forms y = sum_j p_j e_j + sigma e_shared in slot order. Blocks are mapped
+// so the rows of one tile run on one XCD and share expert tiles in its L2.
 //
 // Every row's arithmetic is fixed (K slices owned by fixed waves, chunks and
 // groups in K order, slices reduced in slice order, slots combined in pick
-// order, shared last) and independent of the other rows, so a row's y is
-// bit-identical alone or in a batch ("Sage-A1.5 ... #1329", Limits to agree
-// on: the per-row kernels keep one stream's sum order).
+// order, shared last; an MFMA output element is formed from its own row slot
+// and column alone, whichever slot holds the row) and independent of the
+// other rows, so a row's y is bit-identical alone or in a batch ("Sage-A1.5
+// ... #1329", Limits to agree on: the per-row kernels keep one stream's sum
+// order).
 #include "moe_kernels.h"
 #include "moe_launch.h"
 #include "moe_dispatch.h"
