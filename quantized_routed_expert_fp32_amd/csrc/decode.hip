@@ -2,8 +2,9 @@
 //
 // gate/up (k_dec_gateup): a persistent grid. A unit is an expert picked by
 // some row, found from the picks as the first slot (row r, pick j) that
-// holds it, or the shared expert for one row; an item is (unit, 64-row tile
-// of the interleaved gate/up matrix). Workgroup b takes items b, b + G, ...;
+// holds it, or the shared expert for up to four rows (one pass of the
+// matrix-core dots serves four rows at the cost of one); an item is (unit,
+// 64-row tile of the interleaved gate/up matrix). Workgroup b takes items b, b + G, ...;
 // wave w owns the 256-wide K slice w, one weight row per lane, and streams
 // the tile's packed codes once (coalesced 128-bit loads) for every row that
 // picked the expert, so rows sharing an expert share its reads ("Native
@@ -102,13 +103,15 @@ __device__ __forceinline__ int unit_expert(const Picks& P, int u) {
   return __builtin_amdgcn_readlane(P.id1, __ffsll((unsigned long long)s1) - 1);
 }
 
+constexpr int GU_SHARED_ROWS = 4;   // rows per shared-expert unit (one pass)
+
 struct GuItem {
   rsrc_t r;     // the expert block
   uint32_t codes, scales;   // gate/up codes and scale words inside it
   int t;        // layout tile (64 rows: 32 gate + 32 up)
   int tl;       // tile actually loaded (t clamped into the class)
   int shared;
-  int e;        // expert (routed) or the row (shared)
+  int e;        // expert (routed) or the shared unit (rows 4e .. 4e + 3)
 };
 
 // What an item needs of its expert class, read once from the arguments and
@@ -329,7 +332,7 @@ __device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P
                                              float* red, int& rb, int wv, int nw, int lane) {
   const int H = a.H, nch = H / 32, nsl = H / KBLK, k = a.k;
   uint64_t m0 = 0, m1 = 0;
-  int n = 1;
+  int n = min(GU_SHARED_ROWS, a.R - GU_SHARED_ROWS * it.e);   // shared: rows 4e .. 4e + n - 1
   if (!it.shared) {
     m0 = __ballot(P.id0 == it.e);
     m1 = __ballot(P.id1 == it.e);
@@ -340,7 +343,7 @@ __device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P
     int rr[4], jj[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      int r = it.e, j = k;
+      int r = GU_SHARED_ROWS * it.e + v, j = k;
       if (!it.shared && v < m) {
         int s;
         if (m0) { s = __ffsll((unsigned long long)m0) - 1; m0 &= m0 - 1; }
@@ -408,7 +411,7 @@ struct GuCtx {
 // i = (unit i / Tmax, tile i % Tmax); workgroup b takes items b, b + G, ...
 // and the next item's loads are in flight during the current one's
 // arithmetic. With Tmax and G multiples of 8, every item of tile t runs on
-// XCD t % 8, so the per-row shared units re-read the shared expert's tiles
+// XCD t % 8, so the shared units re-read the shared expert's tiles
 // from that L2.
 template <int FR, int FS, int ACT16, int XV>
 __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
   }
   Picks P = find_units(c.lane < nslot ? i0 : -1, c.lane + 64 < nslot ? i1 : -1, a.E, c.lane);
   c.Tmax = 2 * a.Imax / 64;
-  c.n_items = (P.nrt + R) * c.Tmax;
+  c.n_items = (P.nrt + (R + GU_SHARED_ROWS - 1) / GU_SHARED_ROWS) * c.Tmax;
   int it_i = blockIdx.x;
   if (it_i >= c.n_items) return;
   const int G = gridDim.x;
