@@ -191,10 +191,10 @@ __device__ __forceinline__ void pick_and_store(const RouteArgs& a, int row, cons
 // (visible device-wide once the store has completed); each wave waits for
 // its stores, then one thread counts the row's arrivals; the last tile
 // workgroup reads the row's E/64 * k entries back (loads that bypass this
-// XCD's L2) and picks from them. Tile 0's last wave also forms the
-// gate-row logit.
+// XCD's L2) and picks from them. One wave past the slice waves forms the
+// gate-row logit in tile 0, beside the slices.
 template <int FR, int FG, int ACT16>
-__global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __restrict__ x) {
+__global__ __launch_bounds__(576) void k_route(RouteArgs a, const uint16_t* __restrict__ x) {
   __shared__ float red[8][64];
   __shared__ __align__(16) uint32_t lxs[8][128];
   __shared__ uint32_t scr[24];
@@ -202,12 +202,12 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
   const int H = a.H, E = a.E, nsl = H / KBLK, nch = H / 32, ntile = E / 64;
   const int t = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nw = blockDim.x >> 6;
+  const int nw = (blockDim.x >> 6) - 1;          // slice waves; the last wave forms the gate logit
   const uint16_t* xr = x + (uint64_t)row * H;
   const uint8_t* rc = a.base + a.r_off;
   const uint8_t* rs = a.base + a.r_soff;
   float out = 0.f;
-  for (int sl = w; sl < nsl; sl += nw) {
+  for (int sl = w; w < nw && sl < nsl; sl += nw) {
     uint2 xv[1];
     xv[0] = *reinterpret_cast<const uint2*>(xr + sl * KBLK + 4 * lane);
     uint32_t wc[8][Fmt<FR>::WORDS], sc[4];
@@ -218,8 +218,8 @@ __global__ __launch_bounds__(512) void k_route(RouteArgs a, const uint16_t* __re
     slice_dot<FR, 1, ACT16>(wc, sc, lane, xv, 1, lxs[w], part);
     out += part[0];
   }
-  red[w][lane] = out;
-  if (t == 0 && w == nw - 1) {
+  if (w < nw) red[w][lane] = out;
+  if (t == 0 && w == nw) {
     const float s16 = sum16(gate_row_part<FG, ACT16>(a, xr, lane));
     float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 0));
     c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 16));
@@ -479,7 +479,7 @@ template <int FR, int FG, int ACT16>
 static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
   const int nw = min(8, a.H / KBLK);
   if (a.R <= ROUTE_FUSED_MAX_ROWS) {
-    launch_k(k_route<FR, FG, ACT16>, dim3(a.E / 64, a.R), dim3(64 * nw), 0, s, ev, 0, a, a.x);
+    launch_k(k_route<FR, FG, ACT16>, dim3(a.E / 64, a.R), dim3(64 * (nw + 1)), 0, s, ev, 0, a, a.x);
     return hipGetLastError();
   }
   hipEvent_t e0[2] = {ev ? ev[0] : nullptr, nullptr}, e1[2] = {nullptr, ev ? ev[1] : nullptr};
