@@ -169,7 +169,7 @@ int moe_route(const moe_layer* layer, const void* x, int rows, const float* logi
   uint8_t* wb = static_cast<uint8_t*>(ws);
   a.lg_ws = reinterpret_cast<float*>(wb + rw.lg_off);
   a.gl_ws = reinterpret_cast<float*>(wb + rw.gl_off);
-  a.cnt = reinterpret_cast<unsigned*>(wb + rw.cnt_off);
+  a.cand = reinterpret_cast<uint64_t*>(wb + rw.cand_off);
   hipError_t e = launch_route(fr.kid, fg.kid, a, static_cast<hipStream_t>(stream), taps_events(taps));
   if (e != hipSuccess) return hip_fail("moe_route: launch", e);
   return MOE_OK;

@@ -41,7 +41,7 @@ uint64_t align256(uint64_t x);
 // Route scratch at the start of every workspace: per-row arrival counters
 // (zero between calls), gate-row logits, then [rows, E] fp32 logits.
 struct RouteWs {
-  uint64_t cnt_off, gl_off, lg_off, total;
+  uint64_t cand_off, gl_off, lg_off, total;
 };
 RouteWs route_ws_layout(const moe_layer_desc* d, int rows);
 uint64_t route_ws_bytes(const moe_layer_desc* d, int rows);

@@ -17,7 +17,7 @@ struct RouteArgs {
   float* logits;   // tap [R, E+1] or null
   float* lg_ws;    // [R, E] scratch: logits before the bias
   float* gl_ws;    // [R] scratch: gate-row logits
-  unsigned* cnt;   // [R] per-row arrival counters; zero between calls
+  uint64_t* cand;  // [R, 32] tile picks (id + 1) << 32 | value bits; zero between calls
 };
 
 // Offsets of one expert class (routed or shared) inside the packed layer.

@@ -11,9 +11,8 @@
 // lowest ids among its ties, slots by (key desc, id asc); then
 // exp(l - l_top) / sum in slot order and sigmoid of the gate logit.
 //  * decode batches (k_route): one launch; each tile workgroup picks its
-//    own k best, sends them out with write-through stores, and the last of
-//    a row's tile workgroups to arrive (a per-row counter in the workspace,
-//    reset by that workgroup) picks from the tiles' picks.
+//    own k best, sends them out with write-through stores, and tile 0's
+//    workgroup waits for them and picks from the tiles' picks.
 //  * prompt chunks: logits of 32 rows x 64 experts per workgroup on MFMA
 //    (k_route_mfma, 4-bit router codes) or 8 rows per workgroup on the
 //    vector units (k_route_logits), then one wave per row picks in a second
@@ -186,19 +185,20 @@ __device__ __forceinline__ void pick_and_store(const RouteArgs& a, int row, cons
 
 // Decode batches: one workgroup per (tile of 64 experts, row) forms the
 // tile's logits and picks the tile's own k best (the k best of a row are
-// among the union of its tiles' k best under the same order); those k
-// (value, id) entries go to the workspace with write-through stores
-// (visible device-wide once the store has completed); each wave waits for
-// its stores, then one thread counts the row's arrivals; the last tile
-// workgroup reads the row's E/64 * k entries back (loads that bypass this
-// XCD's L2) and picks from them. One wave past the slice waves forms the
-// gate-row logit in tile 0, beside the slices.
+// among the union of its tiles' k best under the same order). Tiles 1.. send
+// their k entries, each one 64-bit word (id + 1) << 32 | value bits, with
+// write-through stores; tile 0's workgroup polls those words (loads that
+// bypass its XCD's L2) until none is zero, clears them for the next call and
+// picks from its own entries and theirs. Every workgroup of the launch is
+// resident at once (E/64 * rows <= 128 workgroups), so the wait ends; it is
+// bounded all the same. One wave past the slice waves forms the gate-row
+// logit in tile 0, beside the slices.
 template <int FR, int FG, int ACT16>
 __global__ __launch_bounds__(576) void k_route(RouteArgs a, const uint16_t* __restrict__ x) {
   __shared__ float red[8][64];
   __shared__ __align__(16) uint32_t lxs[8][128];
   __shared__ uint32_t scr[24];
-  __shared__ int s_last;
+  __shared__ float s_gate;
   const int H = a.H, E = a.E, nsl = H / KBLK, nch = H / 32, ntile = E / 64;
   const int t = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -225,49 +225,48 @@ __global__ __launch_bounds__(576) void k_route(RouteArgs a, const uint16_t* __re
     c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 16));
     c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 32));
     c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s16), 48));
-    if (lane == 0) __hip_atomic_store(&a.gl_ws[row], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) s_gate = c;
   }
   __syncthreads();
+  if (w != 0) return;
   const int k = a.k;
-  float* cand = a.lg_ws + (uint64_t)row * E;    // per tile: k values, then k ids (16 words)
-  if (w == 0) {
-    float l = 0.f;
-    for (int q = 0; q < nw; ++q) l += red[q][lane];
-    const int e = 64 * t + lane;
-    const float v1[1] = {a.bias ? l + a.bias[e] : l};
-    if (a.logits) a.logits[(uint64_t)row * (E + 1) + e] = v1[0];
-    const uint32_t k1[1] = {pick_key(v1[0])};
-    const int i1[1] = {e};
-    int slot, id;
-    float val;
-    wave_topk_ids<1>(k1, v1, i1, lane, k, scr, slot, id, val);   // lane j < k: the tile's j-th pick by id
-    if (lane < k) {
-      __hip_atomic_store(&cand[16 * t + lane], val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(reinterpret_cast<int*>(cand) + 16 * t + 8 + lane, id, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
+  uint64_t* cand = a.cand + (uint64_t)row * 32;    // tile u's entries at 8 u .. 8 u + k - 1
+  float l = 0.f;
+  for (int q = 0; q < nw; ++q) l += red[q][lane];
+  const int e = 64 * t + lane;
+  const float v1[1] = {a.bias ? l + a.bias[e] : l};
+  if (a.logits) a.logits[(uint64_t)row * (E + 1) + e] = v1[0];
+  const uint32_t k1[1] = {pick_key(v1[0])};
+  const int i1[1] = {e};
+  int slot, id;
+  float val;
+  wave_topk_ids<1>(k1, v1, i1, lane, k, scr, slot, id, val);   // lane j < k: the tile's j-th pick by id
+  if (t != 0) {
+    if (lane < k)
+      __hip_atomic_store(&cand[8 * t + lane], ((uint64_t)(uint32_t)(id + 1) << 32) | __float_as_uint(val),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this wave's stores have completed
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = __hip_atomic_fetch_add(&a.cnt[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = old == (unsigned)(ntile - 1);
-    if (s_last) __hip_atomic_store(&a.cnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!s_last || w != 0) return;
-  // lane j < ntile * k: entry j % k of tile j / k (ids grow with the lane)
+  // tile 0: lane j < k holds its own entry j; lane j in [k, ntile * k) waits
+  // for entry j % k of tile j / k
   const int nc = ntile * k;
-  const int jt = min(lane, nc - 1) / k, ji = min(lane, nc - 1) % k;
-  const float cv = __hip_atomic_load(&cand[16 * jt + ji], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int ci = __hip_atomic_load(reinterpret_cast<const int*>(cand) + 16 * jt + 8 + ji, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-  const float c = __hip_atomic_load(&a.gl_ws[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool remote = lane >= k && lane < nc;
+  uint64_t* src = &cand[8 * (lane / k) + lane % k];
+  uint64_t word = 0;
+  for (int spin = 0; spin < (1 << 22); ++spin) {
+    if (remote) word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__ballot(remote && word == 0) == 0) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (remote) __hip_atomic_store(src, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // empty for the next call
+  const float cv = remote ? __uint_as_float((uint32_t)word) : val;
+  const int ci = remote ? (int)(word >> 32) - 1 : id;
+  const float c = s_gate;
   if (a.logits && lane == 0) a.logits[(uint64_t)row * (E + 1) + E] = c;
-  const float v1[1] = {cv};
-  const uint32_t k1[1] = {lane < nc ? pick_key(cv) : 0u};
-  const int i1[1] = {ci};
-  pick_and_store_n<1>(a, row, k1, v1, i1, c, lane, scr);
+  const float vv[1] = {cv};
+  const uint32_t kk[1] = {(lane < k || remote) ? pick_key(cv) : 0u};
+  const int ii[1] = {ci};
+  pick_and_store_n<1>(a, row, kk, vv, ii, c, lane, scr);
 }
 
 // Prompt chunks: logits of 32 rows x 64 experts per workgroup on 16-bit

@@ -130,3 +130,27 @@ def test_nan_and_zero_rows():
     assert list(g["ids"][2]) == list(range(k)) and np.all(g["p"][2] == 1.0 / k)
     assert g["sg"][2] == 0.5 and np.all(g["y"][2] == 0.0)
     check_parity(Lh, xb, g, dense, name="decode-small-nan-zero")
+
+
+def test_workspace_reused_across_row_counts_bit_for_bit():
+    """One workspace, zero-filled once, serves calls of different row counts
+    and both forms in turn (the decode router's hand-off words must be empty
+    at the start of every call); each call gives the bytes a fresh workspace
+    gives."""
+    from gpu_common import binding, to_dev_x, torch_mod
+    B = binding()
+    torch = torch_mod()
+    spec = synth.CONFIGS[1]
+    Lh, dev, _ = layer_of(spec, 0)
+    ws = B.new_workspace(dev, 64, True)      # sized for the largest call below
+    calls = [(8, False), (1, False), (16, False), (64, True), (3, False), (32, True), (8, False), (1, False)]
+    for i, (rows, grouped) in enumerate(calls):
+        log(f"case workspace reuse call {i} rows={rows} grouped={grouped}")
+        x = to_dev_x(synth.make_x(spec, 0, rows, rep=20 + i))
+        ids, p, sg = B.route(dev, x, ws=ws)
+        y = B.experts(dev, x, ids, p, sg, grouped, ws=ws)
+        ids2, p2, sg2 = B.route(dev, x)
+        y2 = B.experts(dev, x, ids2, p2, sg2, grouped)
+        torch.cuda.synchronize()
+        for name, u, v in (("ids", ids, ids2), ("p", p, p2), ("sg", sg, sg2), ("y", y, y2)):
+            assert torch.equal(u.view(torch.int32), v.view(torch.int32)), f"call {i} rows {rows}: {name}"
