@@ -224,6 +224,43 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n}), flush=True)
 
 
+def measured_ceilings(torch, dev, stream):
+    """Practical ceilings beside the published peaks: a plain 1 GiB device
+    copy (read + write bytes over its time) and a square fp16 GEMM of 8192
+    through torch's BLAS, each timed with events on the bench stream after
+    warm-up. Context for the roofline fractions, not their denominators."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    m = 8192
+    A = torch.randn(m, m, dtype=torch.float16, device=dev)
+    Bm = torch.randn(m, m, dtype=torch.float16, device=dev)
+    C = torch.empty(m, m, dtype=torch.float16, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    with torch.cuda.stream(stream):
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        e0.record(stream)
+        for _ in range(10):
+            b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["copy_1GiB_gbs"] = 2 * n * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+        for _ in range(3):
+            torch.mm(A, Bm, out=C)
+        e0.record(stream)
+        for _ in range(10):
+            torch.mm(A, Bm, out=C)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["gemm_fp16_8192_tflops"] = 2 * m ** 3 * 10 / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del a, b, A, Bm, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel, commands):
     """Markdown summary of the HBM byte counters of `kernel`: mean FETCH_SIZE
     and WRITE_SIZE (KiB per dispatch) scaled by what the same counters read
@@ -415,6 +452,10 @@ def main():
     log(f"[bench] route {kus[0]:.2f} us, gate/up {kus[1]:.2f} us ({achieved:.0f} GB/s), "
         f"down+combine {kus[2]:.2f} us")
 
+    ceilings = measured_ceilings(torch, dev, stream)
+    log(f"[bench] measured ceilings: copy {ceilings['copy_1GiB_gbs']:.0f} GB/s, "
+        f"fp16 GEMM {ceilings['gemm_fp16_8192_tflops']:.0f} TFLOP/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
@@ -450,6 +491,7 @@ def main():
                                    "decode_down_combine": kus[2]},
                      "mean_unique_experts": float(uniq.mean())},
         "prefill": prefill,
+        "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
