@@ -154,3 +154,23 @@ def test_workspace_reused_across_row_counts_bit_for_bit():
         torch.cuda.synchronize()
         for name, u, v in (("ids", ids, ids2), ("p", p, p2), ("sg", sg, sg2), ("y", y, y2)):
             assert torch.equal(u.view(torch.int32), v.view(torch.int32)), f"call {i} rows {rows}: {name}"
+
+
+def test_decode_16_row_window_at_full_size():
+    """16 decode rows (the widest window) through a full-size layer: parity,
+    and every row bit-identical to its one-row step. At this size the
+    activations go to LDS by direct loads rather than through registers."""
+    spec = synth.CONFIGS[1]
+    Lh, dev, dense = layer_of(spec, 0)
+    rows = 16
+    log(f"case decode window rows={rows} full size")
+    xb = synth.make_x(spec, 0, rows, rep=31)
+    batch = run_gpu(dev, Lh, xb)
+    check_parity(Lh, xb, batch, dense, name="decode-c1-r16", strict_y=1e-4)
+    for r in (0, 7, 15):
+        solo = run_gpu(dev, Lh, xb[r:r + 1], taps=False)
+        for key in ("ids", "p", "sg", "y"):
+            a_, b_ = solo[key][0], batch[key][r]
+            if a_.dtype == np.float32:
+                a_, b_ = a_.view(np.uint32), b_.view(np.uint32)
+            assert np.array_equal(a_, b_), f"row {r} {key} differs"
