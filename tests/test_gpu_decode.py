@@ -174,3 +174,27 @@ def test_decode_16_row_window_at_full_size():
             if a_.dtype == np.float32:
                 a_, b_ = a_.view(np.uint32), b_.view(np.uint32)
             assert np.array_equal(a_, b_), f"row {r} {key} differs"
+
+
+def test_router_hand_off_repeated_calls():
+    """Many back-to-back router calls on one workspace, two inputs in turn
+    (no host sync between calls): every call's picks, weights and gates equal
+    the first call's for the same input, bit for bit (a stale or torn
+    hand-off word between tile workgroups would show as a changed pick)."""
+    from gpu_common import binding, to_dev_x, torch_mod
+    B = binding()
+    torch = torch_mod()
+    spec = synth.CONFIGS[1]
+    Lh, dev, _ = layer_of(spec, 0)
+    ws = B.new_workspace(dev, 8, False)
+    xs = [to_dev_x(synth.make_x(spec, 0, 8, rep=40 + i)) for i in range(2)]
+    ref = [B.route(dev, x, ws=ws) for x in xs]
+    torch.cuda.synchronize()
+    ref = [tuple(t.clone() for t in r) for r in ref]
+    outs = []
+    for it in range(200):
+        outs.append(B.route(dev, xs[it % 2], ws=ws))
+    torch.cuda.synchronize()
+    for it, o in enumerate(outs):
+        for name, u, v in zip(("ids", "p", "sg"), o, ref[it % 2]):
+            assert torch.equal(u.view(torch.int32), v.view(torch.int32)), f"call {it}: {name}"
