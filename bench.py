@@ -316,18 +316,19 @@ def main():
         copy_calibration()
         return
     if args.counter_summary:
-        cmds = [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcF -o f -- "
-            "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-prefill --no-graph",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcW -o w -- "
-            "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-prefill --no-graph",
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/cpF -o f -- "
-            "python3 bench.py --copy-calib",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/cpW -o w -- "
-            "python3 bench.py --copy-calib",
-            "python3 bench.py --counter-summary gpurun_out/pmcF/f_counter_collection.csv "
-            "gpurun_out/pmcW/w_counter_collection.csv gpurun_out/cpF/f_counter_collection.csv "
-            "gpurun_out/cpW/w_counter_collection.csv"]
+        # the commands that wrote the four CSVs: each pass's output folder and
+        # file prefix are read back from the CSV path it was given
+        def run_of(path):
+            folder = os.path.dirname(path)
+            return folder, os.path.basename(path).split("_counter_collection")[0]
+        dec = "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-prefill --no-graph"
+        passes = [("FETCH_SIZE", dec), ("WRITE_SIZE", dec), ("FETCH_SIZE", "python3 bench.py --copy-calib"),
+                  ("WRITE_SIZE", "python3 bench.py --copy-calib")]
+        cmds = []
+        for (counter, prog), path in zip(passes, args.counter_summary):
+            folder, prefix = run_of(path)
+            cmds.append(f"rocprofv3 --pmc {counter} --output-format csv -d {folder} -o {prefix} -- {prog}")
+        cmds.append("python3 bench.py --counter-summary " + " ".join(args.counter_summary))
         sys.stdout.write(counter_summary(*args.counter_summary, "k_dec_gateup", cmds))
         return
     if args.gpus != 1:
