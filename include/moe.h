@@ -174,9 +174,11 @@ int moe_pack_layer(const moe_layer_desc* d, const moe_layer_src* src,
  * size serves both calls of a layer (calls on one stream run in order).
  * A workspace must be zero-filled before its first use: it holds hand-off
  * words that workgroups of one call use to pass work to each other, and
- * every call leaves them at zero again. A workspace sized for `rows` also
- * serves calls with fewer rows, in either form. Calls that overlap on one
- * workspace (e.g. on two streams) race; give each stream its own workspace. */
+ * every call leaves them at zero again. Any call may use a workspace larger
+ * than it needs (say one sized for the most rows of the grouped form); each
+ * call checks ws_bytes against its own need (MOE_ENOSPACE). Calls that
+ * overlap on one workspace (e.g. on two streams) race; give each stream its
+ * own workspace. */
 int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t* bytes);
 
 /* ------------------------------------------------------------- hot path */
