@@ -178,9 +178,22 @@ def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream):
         "rows_per_expert": {"max": int(cnt.max()), "mean": float(cnt.mean()),
                             "empty": int((cnt == 0).sum())},
     }
+    # the same chunk through the decode step's arithmetic in 16-row windows
+    # (moe_forward_windows: same bits however the prompt is cut), eager
+    wws = B.new_workspace(layer, 16, False, dev)
+    with torch.cuda.stream(stream):
+        B.forward_windows(layer, x, bias, ws=wws, out=(ids, p, sg), y=y, stream=stream)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(3):
+            B.forward_windows(layer, x, bias, ws=wws, out=(ids, p, sg), y=y, stream=stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+    res["windows_us_per_chunk"] = t0.elapsed_time(t1) / 3 * 1e3
     log(f"[bench] prefill {spec.name}: {us:.1f} us/chunk, {res['tokens_per_s']:.0f} tokens/s, "
         f"{res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma_peak']:.1f}% of f16 MFMA); "
-        + ", ".join(f"{k_} {v:.1f}" for k_, v in res["phase_us"].items()))
+        + ", ".join(f"{k_} {v:.1f}" for k_, v in res["phase_us"].items())
+        + f"; 16-row windows {res['windows_us_per_chunk']:.1f} us/chunk")
     return res
 
 

@@ -218,6 +218,26 @@ int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const in
                        const float* p, const float* shared_gate, float* y, void* ws,
                        uint64_t ws_bytes, const moe_taps* taps, void* stream);
 
+/* Route and experts of any number of rows through the decode step's
+ * arithmetic, in consecutive windows of up to 16 rows on `stream`: every
+ * row's ids, p, shared_gate and y are bit-identical to its one-row
+ * moe_route + moe_experts_decode step, however the rows are cut into calls
+ * ("Native server: --backend xpu for Nemotron on Intel Arc", description:
+ * windows and prompt rows take the decode step's arithmetic and a prompt
+ * gives the same bits however it is cut; "Sage-A1.5 ... #1329", Limits to
+ * agree on: the grouped MoE's sum order differs from one stream alone).
+ * Slower than moe_experts_grouped for wide prompts: each window reads the
+ * experts its rows picked.
+ *   x, logit_bias, ids, p, shared_gate, y: as moe_route / moe_experts_decode,
+ *   for `rows` rows (1..65536)
+ *   ws: >= moe_workspace_size(rows = min(rows, 16), grouped = 0) bytes,
+ *       zero-filled before its first use
+ * Errors: as the two calls; all checks happen before any window is
+ * enqueued. Preconditions as moe_experts_decode. */
+int moe_forward_windows(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+                        int32_t* ids, float* p, float* shared_gate, float* y, void* ws,
+                        uint64_t ws_bytes, void* stream);
+
 /* The same layer for prompt chunks (the prefill form): rows are sorted by
  * expert (histogram, prefix scan, stable scatter), then grouped GEMMs on
  * 16-bit MFMA compute gate/up + SwiGLU and down, then a fixed-order combine.

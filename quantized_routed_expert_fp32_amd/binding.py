@@ -65,7 +65,7 @@ class TapsC(C.Structure):
 
 EXPORTS = ["moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
            "moe_workspace_size", "moe_route", "moe_experts_decode", "moe_experts_grouped",
-           "moe_status_string", "moe_last_error", "moe_version"]
+           "moe_forward_windows", "moe_status_string", "moe_last_error", "moe_version"]
 
 _lib = None
 
@@ -92,8 +92,10 @@ def lib() -> C.CDLL:
     L.moe_experts_decode.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, u64,
                                      C.POINTER(TapsC), vp]
     L.moe_experts_grouped.argtypes = L.moe_experts_decode.argtypes
+    L.moe_forward_windows.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, vp, u64, vp]
     for f in ("moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
-              "moe_workspace_size", "moe_route", "moe_experts_decode", "moe_experts_grouped"):
+              "moe_workspace_size", "moe_route", "moe_experts_decode", "moe_experts_grouped",
+              "moe_forward_windows"):
         getattr(L, f).restype = C.c_int
     L.moe_status_string.argtypes = [C.c_int]
     L.moe_status_string.restype = C.c_char_p
@@ -258,6 +260,28 @@ def experts(layer: Layer, x, ids, p, sg, grouped: bool, ws=None, taps=None, y=No
               ws.numel() * ws.element_size(), _taps(taps), _stream_ptr(stream)),
            "moe_experts_grouped" if grouped else "moe_experts_decode")
     return y
+
+
+def forward_windows(layer: Layer, x, logit_bias=None, ws=None, out=None, y=None, stream=None):
+    """moe_forward_windows: route + decode experts in windows of 16 rows;
+    returns (ids, p, shared_gate, y), each row bit-identical to its one-row step."""
+    import torch
+    R = x.shape[0]
+    k = layer.desc.top_k
+    if out is None:
+        ids = torch.empty((R, k), dtype=torch.int32, device=x.device)
+        p = torch.empty((R, k), dtype=torch.float32, device=x.device)
+        sg = torch.empty((R,), dtype=torch.float32, device=x.device)
+    else:
+        ids, p, sg = out
+    if y is None:
+        y = torch.empty((R, layer.desc.hidden), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = new_workspace(layer, min(R, 16), False, x.device)
+    _check(lib().moe_forward_windows(C.byref(layer.c), _ptr(x), R, _ptr(logit_bias), _ptr(ids), _ptr(p),
+                                     _ptr(sg), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream_ptr(stream)), "moe_forward_windows")
+    return ids, p, sg, y
 
 
 def experts_decode(layer, x, ids, p, sg, **kw):

@@ -130,6 +130,8 @@ int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t*
   return MOE_OK;
 }
 
+static constexpr int kWindowRows = 16;   // decode rows per window of moe_forward_windows
+
 int moe_route(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
               int32_t* ids, float* p, float* shared_gate, void* ws, uint64_t ws_bytes,
               const moe_taps* taps, void* stream) {
@@ -230,6 +232,41 @@ int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const in
   a.tap_e = taps ? taps->e : nullptr;
   hipError_t e = launch_decode(fe.kid, fs.kid, a, static_cast<hipStream_t>(stream), taps_events(taps));
   if (e != hipSuccess) return hip_fail("moe_experts_decode: launch", e);
+  return MOE_OK;
+}
+
+int moe_forward_windows(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+                        int32_t* ids, float* p, float* shared_gate, float* y, void* ws, uint64_t ws_bytes,
+                        void* stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if (!x || !ids || !p || !shared_gate || !y || !ws) {
+    set_error("moe_forward_windows: NULL x/ids/p/shared_gate/y/ws");
+    return MOE_EINVAL;
+  }
+  if (rows < 1 || rows > 65536) { set_error("moe_forward_windows: rows outside 1..65536"); return MOE_EINVAL; }
+  // every window needs at most a 16-row decode workspace; checked before
+  // anything is enqueued
+  const int wmax = std::min(rows, kWindowRows);
+  const uint64_t need = decode_ws_layout(&layer->d, wmax).total;
+  if (ws_bytes < need) {
+    set_error("moe_forward_windows: workspace of " + std::to_string(ws_bytes) + " bytes, needs " +
+              std::to_string(need));
+    return MOE_ENOSPACE;
+  }
+  const int H = layer->d.hidden, k = layer->d.top_k;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  for (int r0 = 0; r0 < rows; r0 += kWindowRows) {
+    const int n = std::min(kWindowRows, rows - r0);
+    const void* xw = xb + (uint64_t)r0 * H * 2;
+    int32_t* iw = ids + (uint64_t)r0 * k;
+    float* pw = p + (uint64_t)r0 * k;
+    float* sw = shared_gate + r0;
+    st = moe_route(layer, xw, n, logit_bias, iw, pw, sw, ws, ws_bytes, nullptr, stream);
+    if (st) return st;
+    st = moe_experts_decode(layer, xw, n, iw, pw, sw, y + (uint64_t)r0 * H, ws, ws_bytes, nullptr, stream);
+    if (st) return st;
+  }
   return MOE_OK;
 }
 

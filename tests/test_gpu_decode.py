@@ -198,3 +198,34 @@ def test_router_hand_off_repeated_calls():
     for it, o in enumerate(outs):
         for name, u, v in zip(("ids", "p", "sg"), o, ref[it % 2]):
             assert torch.equal(u.view(torch.int32), v.view(torch.int32)), f"call {it}: {name}"
+
+
+def test_forward_windows_same_bits_however_cut():
+    """moe_forward_windows over 40 prompt rows: one call (windows 16 + 16 + 8)
+    and another cut (7 rows, then 33) give the same bits, each row equals its
+    one-row decode step, and the rows pass parity against the oracle."""
+    from gpu_common import binding, to_dev_x, torch_mod
+    B = binding()
+    torch = torch_mod()
+    spec = synth.CONFIGS[1]
+    Lh, dev, dense = layer_of(spec, 0)
+    rows = 40
+    log(f"case forward_windows rows={rows}")
+    xb = synth.make_x(spec, 0, rows, rep=50)
+    x = to_dev_x(xb)
+    a = B.forward_windows(dev, x)
+    b1 = B.forward_windows(dev, x[:7].contiguous())
+    b2 = B.forward_windows(dev, x[7:].contiguous())
+    torch.cuda.synchronize()
+    g = {name: t.cpu().numpy() for name, t in zip(("ids", "p", "sg", "y"), a)}
+    for i, name in enumerate(("ids", "p", "sg", "y")):
+        cut = torch.cat([b1[i], b2[i]])
+        assert torch.equal(a[i].view(torch.int32), cut.view(torch.int32)), f"{name} depends on the cut"
+    for r in (0, 6, 7, 15, 16, 39):
+        solo = run_gpu(dev, Lh, xb[r:r + 1], taps=False)
+        for key in ("ids", "p", "sg", "y"):
+            u, v = solo[key][0], g[key][r]
+            if u.dtype == np.float32:
+                u, v = u.view(np.uint32), v.view(np.uint32)
+            assert np.array_equal(u, v), f"row {r} {key} differs from its one-row step"
+    check_parity(Lh, xb, g, dense, name="forward-windows-c1-r40", strict_y=1e-4)
