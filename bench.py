@@ -106,7 +106,7 @@ def cpu_baseline(spec, Lh, rows, budget_s=15.0):
                        f"layer, per-row fp64 form, experts dequantised on first use, {dt:.1f} s")
 
 
-def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream):
+def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream, windows=False):
     """One prompt chunk through one layer: route + grouped experts, timed as a
     HIP graph; per-phase times from events inside the library's launches."""
     spec = synth.CONFIGS[cfg_id]
@@ -178,22 +178,25 @@ def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream):
         "rows_per_expert": {"max": int(cnt.max()), "mean": float(cnt.mean()),
                             "empty": int((cnt == 0).sum())},
     }
-    # the same chunk through the decode step's arithmetic in 16-row windows
-    # (moe_forward_windows: same bits however the prompt is cut), eager
-    wws = B.new_workspace(layer, 16, False, dev)
-    with torch.cuda.stream(stream):
-        B.forward_windows(layer, x, bias, ws=wws, out=(ids, p, sg), y=y, stream=stream)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for _ in range(3):
+    if windows:
+        # the same chunk through the decode step's arithmetic in 16-row windows
+        # (moe_forward_windows: same bits however the prompt is cut), eager;
+        # off by default so that the decode kernels' traced averages stay the
+        # 8-row workload's
+        wws = B.new_workspace(layer, 16, False, dev)
+        with torch.cuda.stream(stream):
             B.forward_windows(layer, x, bias, ws=wws, out=(ids, p, sg), y=y, stream=stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-    res["windows_us_per_chunk"] = t0.elapsed_time(t1) / 3 * 1e3
+            torch.cuda.synchronize()
+            t0.record(stream)
+            for _ in range(3):
+                B.forward_windows(layer, x, bias, ws=wws, out=(ids, p, sg), y=y, stream=stream)
+            t1.record(stream)
+            torch.cuda.synchronize()
+        res["windows_us_per_chunk"] = t0.elapsed_time(t1) / 3 * 1e3
     log(f"[bench] prefill {spec.name}: {us:.1f} us/chunk, {res['tokens_per_s']:.0f} tokens/s, "
         f"{res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma_peak']:.1f}% of f16 MFMA); "
         + ", ".join(f"{k_} {v:.1f}" for k_, v in res["phase_us"].items())
-        + f"; 16-row windows {res['windows_us_per_chunk']:.1f} us/chunk")
+        + (f"; 16-row windows {res['windows_us_per_chunk']:.1f} us/chunk" if windows else ""))
     return res
 
 
@@ -319,6 +322,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="only the prompt-chunk lines (debug)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--windows", action="store_true",
+                    help="also time each prompt chunk through moe_forward_windows (16-row decode windows)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB copy (scales the HBM byte counters)")
     ap.add_argument("--counter-summary", nargs=4, metavar="CSV",
@@ -361,7 +366,7 @@ def main():
     stream = torch.cuda.Stream()
     prefill = None
     if not args.no_prefill:
-        prefill = [bench_prefill(c, 20, 3, B, to_abi, synth, torch, dev, stream) for c in (3, 4)]
+        prefill = [bench_prefill(c, 20, 3, B, to_abi, synth, torch, dev, stream, args.windows) for c in (3, 4)]
         if args.prefill_only:
             print(json.dumps({"prefill": prefill}), flush=True)
             return
