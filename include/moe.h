@@ -56,7 +56,8 @@ enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1 };
  *       ("Sage-A1.5 ... on the XPU backend #1329", Proposal: affine 4/64 export)
  *   {3, 64, MOE_AFFINE, MOE_BF16}     MLX affine 3-bit, group 64 (routed/shared only)
  *       ("qwen3_5_moe on native CUDA with 3-bit routed experts #803", What I want to run)
- *   {8, 64, MOE_AFFINE, MOE_BF16}     MLX affine 8-bit, group 64 (router/gate row only)
+ *   {8, 64, MOE_AFFINE, MOE_BF16}     MLX affine 8-bit, group 64 (router, gate row; experts
+ *                                     on the decode path only: moe_experts_grouped refuses them)
  *       (same page and section: routers and the shared-expert gate at 8 bits)
  *   {4, 128, MOE_SYMMETRIC, MOE_FP16} int4 symmetric, group 128, fp16 scales (W4A16)
  *       ("Sage-1.5-W4A16" model card, Model details)

@@ -41,17 +41,18 @@
 
 namespace moe {
 
-// Codes (8 chunks of one K slice) and scale words of one lane.
+// Codes (8 chunks of one K slice, W words each) and scale words of one lane.
+template <int W>
 struct SliceBuf {
-  uint32_t w[8][4];
+  uint32_t w[8][W];
   uint32_t sc[4];
 };
 
 // Codes and scale words of K slice sl of tile t of a matrix in the range
 // behind r (codes / scales: byte offsets of the matrix's parts in it).
-template <int F>
+template <int F, typename SB>
 __device__ __forceinline__ void load_slice(rsrc_t r, uint32_t codes, uint32_t scales, int t, int sl, int nch,
-                                           int nkb, int lane, SliceBuf& b) {
+                                           int nkb, int lane, SB& b) {
   const uint32_t vc = chunk_voff<F>(lane), vs = scale_voff<F>(lane);
   // scale words first: group 0's arithmetic then waits only for its chunks
   load_scales_rs<F>(r, vs, scales + (uint32_t)sblk_off<F>(t, sl, nkb), b.sc);
@@ -150,8 +151,8 @@ __device__ __forceinline__ GuItem gu_item(const uint8_t* base, const GuCls& rc, 
   return it;
 }
 
-template <int FR, int FS>
-__device__ __forceinline__ void gu_issue(const GuItem& it, int wv, int nch, int nkb, int lane, SliceBuf& b) {
+template <int FR, int FS, typename SB>
+__device__ __forceinline__ void gu_issue(const GuItem& it, int wv, int nch, int nkb, int lane, SB& b) {
   if constexpr (FR == FS) {
     load_slice<FR>(it.r, it.codes, it.scales, it.tl, wv, nch, nkb, lane, b);
   } else {
@@ -199,7 +200,10 @@ struct PairMasks {
 template <int F, int ACT16>
 __device__ __forceinline__ PairMasks pair_masks() {
   PairMasks k;
-  if constexpr (F == F_Q3) {
+  if constexpr (F == F_Q8) {
+    k.m = ACT16 ? 0x03FC03FCu : 0x00780078u;   // fp16: the byte; bf16: a nibble
+    k.q0 = k.q1 = k.q2 = 0u;
+  } else if constexpr (F == F_Q3) {
     k.m = ACT16 ? 0x01C001C0u : 0x00380038u;
     k.q0 = ACT16 ? 0x00400040u : 0x00080008u;
     k.q1 = ACT16 ? 0x00800080u : 0x00100010u;
@@ -212,9 +216,26 @@ __device__ __forceinline__ PairMasks pair_masks() {
   asm volatile("" : "+s"(k.m), "+s"(k.q0), "+s"(k.q1), "+s"(k.q2), "+v"(k.c));
   return k;
 }
+// 8-bit codes: with fp16 activations 16 pairs 1 + q/256; with bf16 ones
+// (7 mantissa bits) the low nibbles' 16 pairs in o[0..15] and the high
+// nibbles' in o[16..31], each 1 + n/16.
 template <int F, int ACT16>
 __device__ __forceinline__ void unpack_pairs(const uint32_t* w, const PairMasks& k, uint32_t* o) {
-  if constexpr (F == F_Q3) {
+  if constexpr (F == F_Q8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t v = w[i];
+      if constexpr (ACT16) {
+        o[2 * i] = ((v << 2) & k.m) | k.c;
+        o[2 * i + 1] = ((v >> 6) & k.m) | k.c;
+      } else {
+        o[2 * i] = ((v << 3) & k.m) | k.c;
+        o[2 * i + 1] = ((v >> 5) & k.m) | k.c;
+        o[16 + 2 * i] = ((v >> 1) & k.m) | k.c;
+        o[16 + 2 * i + 1] = ((v >> 9) & k.m) | k.c;
+      }
+    }
+  } else if constexpr (F == F_Q3) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const uint32_t v = w[i];
@@ -239,22 +260,23 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t* w, const PairMasks&
   }
 }
 
-template <int F, int ACT16>
-__device__ __forceinline__ f4v gu_slice_mfma(const uint32_t (*w)[4], const uint32_t* sc, const uint32_t* xr,
+template <int F, int ACT16, int W>
+__device__ __forceinline__ f4v gu_slice_mfma(const uint32_t (*w)[W], const uint32_t* sc, const uint32_t* xr,
                                              const float* xs0, const float* xs1, const float* xs2,
                                              const float* xs3, int sl, f4v out) {
   constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
+  constexpr bool NIB = F == F_Q8 && !ACT16;   // two nibble sets, two sums
   const PairMasks pk = pair_masks<F, ACT16>();
 #pragma unroll
   for (int gi = 0; gi < GPS; ++gi) {
     float ms, bm;
     coef_reg<F>(sc, gi, ms, bm);
-    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    f4v acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
     float X0 = 0.f, X1 = 0.f, X2 = 0.f, X3 = 0.f;
 #pragma unroll
     for (int cc = 0; cc < CPG; ++cc) {
       const int c = gi * CPG + cc;
-      uint32_t v[16], av[16], wc[Fmt<F>::WORDS];
+      uint32_t v[NIB ? 32 : 16], av[16], wc[Fmt<F>::WORDS];
 #pragma unroll
       for (int q = 0; q < Fmt<F>::WORDS; ++q) {
         wc[q] = w[c][q];
@@ -271,15 +293,29 @@ __device__ __forceinline__ f4v gu_slice_mfma(const uint32_t (*w)[4], const uint3
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc = mfma4<ACT16>(av[2 * i], av[2 * i + 1], v[2 * i], v[2 * i + 1], acc);
+      if constexpr (NIB) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          acc2 = mfma4<ACT16>(av[2 * i], av[2 * i + 1], v[16 + 2 * i], v[16 + 2 * i + 1], acc2);
+      }
       X0 += xs0[sl * 8 + c];
       X1 += xs1[sl * 8 + c];
       X2 += xs2[sl * 8 + c];
       X3 += xs3[sl * 8 + c];
     }
-    out[0] = fmaf(bm, X0, fmaf(ms, acc[0], out[0]));
-    out[1] = fmaf(bm, X1, fmaf(ms, acc[1], out[1]));
-    out[2] = fmaf(bm, X2, fmaf(ms, acc[2], out[2]));
-    out[3] = fmaf(bm, X3, fmaf(ms, acc[3], out[3]));
+    if constexpr (NIB) {
+      // q = lo + 16 hi: s q + b = (ms/16)(1 + lo/16) + ms (1 + hi/16) + (bm - ms/16)
+      const float m16 = ms * (1.0f / 16.0f), b16 = bm - m16;
+      out[0] = fmaf(b16, X0, fmaf(ms, acc2[0], fmaf(m16, acc[0], out[0])));
+      out[1] = fmaf(b16, X1, fmaf(ms, acc2[1], fmaf(m16, acc[1], out[1])));
+      out[2] = fmaf(b16, X2, fmaf(ms, acc2[2], fmaf(m16, acc[2], out[2])));
+      out[3] = fmaf(b16, X3, fmaf(ms, acc2[3], fmaf(m16, acc[3], out[3])));
+    } else {
+      out[0] = fmaf(bm, X0, fmaf(ms, acc[0], out[0]));
+      out[1] = fmaf(bm, X1, fmaf(ms, acc[1], out[1]));
+      out[2] = fmaf(bm, X2, fmaf(ms, acc[2], out[2]));
+      out[3] = fmaf(bm, X3, fmaf(ms, acc[3], out[3]));
+    }
   }
   return out;
 }
@@ -326,9 +362,9 @@ __device__ __forceinline__ int pick4(int v, int a0, int a1, int a2, int a3) {
 // wave v finishes the pass's slot v. Slots past the pass's rows repeat its
 // first row; their results are not used. With fewer waves than slots a
 // wave finishes several.
-template <int F, int ACT16>
+template <int F, int ACT16, typename SB>
 __device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P, const GuItem& it,
-                                             const SliceBuf& b, const uint32_t* xl, const float* cs,
+                                             const SB& b, const uint32_t* xl, const float* cs,
                                              float* red, int& rb, int wv, int nw, int lane) {
   const int H = a.H, nch = H / 32, nsl = H / KBLK, k = a.k;
   uint64_t m0 = 0, m1 = 0;
@@ -360,7 +396,7 @@ __device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P
     f4v out = {0.f, 0.f, 0.f, 0.f};
     out = gu_slice_mfma<F, ACT16>(b.w, b.sc, xr, xs0, xs1, xs2, xs3, wv, out);
     for (int sl = wv + nw; sl < nsl; sl += nw) {     // hidden > 256 * waves: further slices in place
-      SliceBuf c2;
+      SB c2;
       load_slice<F>(it.r, it.codes, it.scales, it.tl, sl, nch, nsl, lane, c2);
       out = gu_slice_mfma<F, ACT16>(c2.w, c2.sc, xr, xs0, xs1, xs2, xs3, sl, out);
     }
@@ -376,9 +412,9 @@ __device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P
   }
 }
 
-template <int FR, int FS, int ACT16>
+template <int FR, int FS, int ACT16, typename SB>
 __device__ __forceinline__ void gu_process(const DecodeArgs& a, const Picks& P, const GuItem& it,
-                                           const SliceBuf& b, const uint32_t* xl, const float* cs,
+                                           const SB& b, const uint32_t* xl, const float* cs,
                                            float* red, int& rb, int wv, int nw, int lane) {
   if (it.t != it.tl) return;      // tile beyond this class (intermediates differ)
   if constexpr (FR == FS) {        // one copy of the code when both classes share a format
@@ -446,7 +482,8 @@ __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
   int it_i = blockIdx.x;
   if (it_i >= c.n_items) return;
   const int G = gridDim.x;
-  SliceBuf A, B;
+  constexpr int SW = Fmt<FR>::WORDS > Fmt<FS>::WORDS ? Fmt<FR>::WORDS : Fmt<FS>::WORDS;
+  SliceBuf<SW> A, B;
   const GuCls rcl = gu_cls(a.rt), scl = gu_cls(a.sh);
   const uint8_t* const base = a.base;
   GuItem ia = gu_item(base, rcl, scl, P, it_i, c.Tmax);
@@ -792,6 +829,7 @@ static hipError_t launch_decode_s(int fs, const DecodeArgs& a, hipStream_t s, hi
     case F_Q4: return launch_decode_t<FR, F_Q4>(a, s, ev);
     case F_Q3: return launch_decode_t<FR, F_Q3>(a, s, ev);
     case F_S4: return launch_decode_t<FR, F_S4>(a, s, ev);
+    case F_Q8: return launch_decode_t<FR, F_Q8>(a, s, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -801,6 +839,7 @@ hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s, hip
     case F_Q4: return launch_decode_s<F_Q4>(fs, a, s, ev);
     case F_Q3: return launch_decode_s<F_Q3>(fs, a, s, ev);
     case F_S4: return launch_decode_s<F_S4>(fs, a, s, ev);
+    case F_Q8: return launch_decode_s<F_Q8>(fs, a, s, ev);
   }
   return hipErrorInvalidValue;
 }

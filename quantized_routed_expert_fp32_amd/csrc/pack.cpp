@@ -48,11 +48,11 @@ bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* o) {
   bool ok = false;
   if (q4) { *o = {KF_Q4, 4, 64, 16, 4, true}; ok = true; }
   else if (q3 && expert) { *o = {KF_Q3, 3, 64, 12, 4, true}; ok = true; }
-  else if (q8 && !expert) { *o = {KF_Q8, 8, 64, 32, 4, true}; ok = true; }
+  else if (q8) { *o = {KF_Q8, 8, 64, 32, 4, true}; ok = true; }
   else if (s4) { *o = {KF_S4, 4, 128, 16, 2, false}; ok = true; }
   else if (dn && tc == TC_GATE_ROW) { *o = {KF_DENSE, 16, 0, 0, 0, false}; ok = true; }
   if (!ok) {
-    std::string acc = expert ? "{4,64,affine,bf16}, {3,64,affine,bf16}, {4,128,symmetric,fp16}"
+    std::string acc = expert ? "{4,64,affine,bf16}, {3,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}"
                      : tc == TC_ROUTER ? "{4,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}"
                      : "{4,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}, {16,0,dense,bf16}";
     set_error(std::string(class_name(tc)) + " format " + fmt_name(f) +

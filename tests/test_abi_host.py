@@ -54,7 +54,7 @@ def test_pack_size_matches_layout_arithmetic():
 
 
 @pytest.mark.parametrize("cls,fmt", [
-    ("routed", (5, 64, 0, 0)), ("routed", (8, 64, 0, 0)), ("router", (3, 64, 0, 0)),
+    ("routed", (5, 64, 0, 0)), ("routed", (2, 64, 0, 0)), ("router", (3, 64, 0, 0)),
     ("shared", (4, 32, 0, 0)), ("routed", (4, 128, 1, 0)), ("gate_row", (16, 0, 2, 1)),
 ])
 def test_unsupported_formats_refused_by_name(cls, fmt):
