@@ -47,6 +47,16 @@ def expert_bytes(spec, fmt, inter):
     return gu, dn
 
 
+def fmt_name(f):
+    """Short text name of a weight format, e.g. 'affine 4-bit g64 bf16 scale/bias'."""
+    dt = "bf16" if f.scale_dtype == 0 else "fp16"
+    if f.mode == 2:
+        return f"dense {dt}"
+    if f.mode == 1:
+        return f"symmetric {f.bits}-bit g{f.group} {dt} scale"
+    return f"affine {f.bits}-bit g{f.group} {dt} scale/bias"
+
+
 def router_bytes(spec):
     f, g = spec.router, spec.gate_row
     scb = 4 if f.mode == 0 else 2
@@ -322,6 +332,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="only the prompt-chunk lines (debug)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--decode-config", type=int, default=1, choices=(0, 1, 2),
+                    help="decode workload (default 1, the 8-row 40-layer 4-bit one; 2 is the mixed "
+                         "3-bit one, 0 the one-row one)")
+    ap.add_argument("--rows", type=int, default=None, help="decode rows (default: the workload's)")
     ap.add_argument("--windows", action="store_true",
                     help="also time each prompt chunk through moe_forward_windows (16-row decode windows)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -371,10 +385,12 @@ def main():
             print(json.dumps({"prefill": prefill}), flush=True)
             return
 
-    spec = synth.CONFIGS[1]
+    spec = synth.CONFIGS[args.decode_config]
     L = args.layers or spec.layers
-    R, k, H = spec.rows[0], spec.top_k, spec.hidden
+    R, k, H = args.rows or spec.rows[-1], spec.top_k, spec.hidden
     NX = 4
+    # the stored counter summary covers the default decode workload only
+    default_workload = args.decode_config == 1 and R == spec.rows[-1] and L == spec.layers
     log(f"[bench] workload {spec.name}: rows={R} layers={L}")
     layers, host = build_layers(spec, L, B, to_abi, synth, keep_host=1)
     xs = [[torch.from_numpy(synth.make_x(spec, l, R, rep=s).view(np.int16)).to(dev)
@@ -496,11 +512,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "rows": R, "layers": L, "hidden": H,
                    "experts": spec.n_experts, "top_k": k, "inter": spec.inter,
-                   "shared_inter": spec.shared_inter, "weights": "affine 4-bit g64 bf16 scale/bias",
+                   "shared_inter": spec.shared_inter, "weights": fmt_name(spec.routed),
+                   "shared_weights": fmt_name(spec.shared), "router_weights": fmt_name(spec.router),
                    "timing": "hip graph replay" if graphs else "eager"},
         "roofline": {"bound": "hbm", "kernel": "k_dec_gateup", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("k_dec_gateup"), "mean_us": gu_ms * 1e3,
+                     "traffic": stored_traffic("k_dec_gateup") if default_workload else None, "mean_us": gu_ms * 1e3,
                      "bytes_per_launch": gu_bytes},
         "step_hbm": {"algorithmic_bytes": mean_step_bytes,
                      "gbs": mean_step_bytes / ms_step / 1e6,
