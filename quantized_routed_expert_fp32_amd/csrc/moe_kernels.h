@@ -476,9 +476,10 @@ __device__ __forceinline__ void slice_dot(const uint32_t (&w)[8][Fmt<F>::WORDS],
 // column i's candidate with its order key and id; key 0 = absent), ranked by
 // (key desc, id asc); ids must grow with (column, lane) so that lane order
 // settles ties. Every lane must be active. Steps:
-//  1. T = the k-th largest key, bit by bit from the top: a bit stays set when
-//     at least k keys are >= the prefix with it (one ballot per candidate
-//     column and bit);
+//  1. T = the k-th largest key, two bits at a time from the top: of the four
+//     digits the largest is kept for which at least k keys are >= the prefix
+//     with it (three ballots per candidate column and step, all issued before
+//     the counts are read);
 //  2. the picks are every key > T plus the lowest ids among the keys == T;
 //  3. they are compacted in id order into the wave's LDS scratch (8 entries)
 //     and lane j < k reads entry j, then takes its slot from the other
@@ -490,14 +491,30 @@ __device__ __forceinline__ void wave_topk_ids(const uint32_t (&key)[NC], const f
                                               const int (&idv)[NC], int lane, int k,
                                               uint32_t* scratch /* wave-private LDS, 24 u32 */, int& slot,
                                               int& id, float& v) {
+  // T = the largest key with at least k keys >= T (the k-th largest key),
+  // two bits per step: the counts for the three candidate digits of a step
+  // are independent, and they do not increase with the digit
   uint32_t T = 0;
-#pragma unroll 4
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = T | (1u << b);
-    int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < NC; ++i) cnt += __popcll(__ballot(key[i] >= c));
-    T = cnt >= k ? c : T;
+  for (int b = 30; b >= 0; b -= 2) {
+    const uint32_t c1 = T | (1u << b), c2 = T | (2u << b), c3 = T | (3u << b);
+    // all compares of the step issue before the first count reads one
+    uint64_t m[NC][3];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      m[i][0] = __ballot(key[i] >= c1);
+      m[i][1] = __ballot(key[i] >= c2);
+      m[i][2] = __ballot(key[i] >= c3);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      n1 += __popcll(m[i][0]);
+      n2 += __popcll(m[i][1]);
+      n3 += __popcll(m[i][2]);
+    }
+    T = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : T;
   }
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   int need = k, before = 0;

@@ -6,7 +6,7 @@
 // Logits: one workgroup per (tile of 64 experts, group of NR rows); lanes
 // own router rows exactly as the expert kernels own weight rows, wave w sums
 // the K slices w, w + nw, ... and the waves are added in wave order.
-// Pick (wave_topk): a bit-by-bit search for the k-th largest order key
+// Pick (wave_topk): a two-bits-a-step search for the k-th largest order key
 // (NaN above +inf above every finite logit), the keys above it plus the
 // lowest ids among its ties, slots by (key desc, id asc); then
 // exp(l - l_top) / sum in slot order and sigmoid of the gate logit.
