@@ -229,3 +229,69 @@ def test_forward_windows_same_bits_however_cut():
                 u, v = u.view(np.uint32), v.view(np.uint32)
             assert np.array_equal(u, v), f"row {r} {key} differs from its one-row step"
     check_parity(Lh, xb, g, dense, name="forward-windows-c1-r40", strict_y=1e-4)
+
+
+def _pick_biases(E, k, seed=7):
+    """Logit-bias vectors that drive the top-k search through its hard cases;
+    with x = 0 every logit equals its bias exactly."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    out = {}
+    b = np.zeros(E, f32)                       # ties at the k-th place, across tiles
+    b[[200, 17, 90, E - 1, 1]] = 3.0
+    b[[250, 66, 130, 5, 199, 64]] = 2.0
+    out["boundary-ties"] = b
+    one = f32(1.0)                             # keys one unit in the last place apart
+    steps = rng.integers(0, 12, E)
+    b = np.array([np.nextafter(one, f32(2.0)) if s == 0 else one for s in steps], f32)
+    for e in range(E):
+        for _ in range(int(steps[e])):
+            b[e] = np.nextafter(b[e], f32(2.0))
+    out["last-bit"] = b
+    b = -rng.uniform(1.0, 10.0, E).astype(f32) # negatives with both zeros on top
+    b[[3, 100, 180]] = -0.0
+    b[[40, 222]] = 0.0
+    b[[9, 150]] = -np.float32(1e-38)           # denormal-sized just below zero
+    out["signed-zeros"] = b
+    b = rng.standard_normal(E).astype(f32)     # NaN above +inf above finite
+    b[[130, 7]] = np.nan
+    b[64] = np.inf
+    b[rng.choice(E, 40, replace=False)] = -np.inf
+    b[[130, 7]] = np.nan
+    b[64] = np.inf
+    out["nan-inf"] = b
+    b = np.full(E, -np.inf, f32)               # fewer finite values than k
+    b[[33, 190, 77]] = [0.5, -2.0, 0.5]
+    out["mostly-minus-inf"] = b
+    b = np.full(E, 0.5, f32)                   # one above a flat rest
+    b[201] = 0.75
+    out["flat-but-one"] = b
+    out["normal"] = rng.standard_normal(E).astype(f32)
+    return out
+
+
+@pytest.mark.parametrize("cfg,rows", [(1, 3), (1, 40), (2, 3), (2, 40)])
+def test_pick_order_from_crafted_logits(cfg, rows):
+    """x = 0 makes every logit its logit bias, so crafted biases test the
+    pick itself: ids equal the oracle's (value desc, id asc, NaN first,
+    -0 == +0) bit for bit, p agrees within 1e-6 (NaN where the oracle's is),
+    and the gate is sigmoid(0) = 1/2. 3 rows take the one-launch decode
+    router, 40 rows the prompt-chunk logits kernel and the per-row pick."""
+    from gpu_common import binding, to_dev_x, torch_mod
+    B = binding()
+    torch = torch_mod()
+    spec = synth.CONFIGS[cfg]
+    Lh, dev, _ = layer_of(spec, 0)
+    E, k, H = spec.n_experts, spec.top_k, spec.hidden
+    x = to_dev_x(np.zeros((rows, H), np.uint16))
+    for name, bias in _pick_biases(E, k).items():
+        log(f"[pick] cfg {cfg} rows {rows} {name}")
+        ids, p, sg = B.route(dev, x, logit_bias=torch.from_numpy(bias).cuda())
+        torch.cuda.synchronize()
+        ids, p, sg = ids.cpu().numpy(), p.cpu().numpy(), sg.cpu().numpy()
+        ref = O.route(np.zeros((rows, H)), np.zeros((E, H)), np.zeros(H), k, logit_bias=bias)
+        assert (ids == ref.ids).all(), f"{name}: ids {ids[0]} vs {ref.ids[0]}"
+        nan = np.isnan(ref.p)
+        assert (np.isnan(p) == nan).all(), f"{name}: NaN pattern of p"
+        assert np.allclose(p[~nan], ref.p[~nan], rtol=1e-6, atol=1e-7), f"{name}: p {p[0]} vs {ref.p[0]}"
+        assert (sg == 0.5).all(), f"{name}: gate"
