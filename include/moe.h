@@ -12,7 +12,7 @@
  *     g = Wg x, u = Wu x, h = silu(g) * u, e_j = Wd h
  *   y[r,:]       = sum_j p[r,j] e_j + sigma[r] e_shared      (fp32, slots in pick order)
  * with every weight matrix stored quantised: affine w = s*q + b per group of
- * 64 (MLX-style, 3/4/8-bit), or symmetric w = s*(u-8) per group of 128 (W4A16).
+ * 64 (MLX-style, 2/3/4/8-bit), or symmetric w = s*(u-8) per group of 128 (W4A16).
  *
  * Conventions for every call:
  *   - Pointers named dev_* or documented as device memory must point to
@@ -59,6 +59,11 @@ enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1 };
  *   {8, 64, MOE_AFFINE, MOE_BF16}     MLX affine 8-bit, group 64 (router, gate row; experts
  *                                     on the decode path only: moe_experts_grouped refuses them)
  *       (same page and section: routers and the shared-expert gate at 8 bits)
+ *   {2, 64, MOE_AFFINE, MOE_BF16}     MLX affine 2-bit, group 64 (routed/shared only, on the
+ *                                     decode path only: moe_experts_grouped refuses them)
+ *       ("qwen3_5_moe on native CUDA with 3-bit routed experts #803", What exists on
+ *       native: the loader reads MLX affine at 2 to 8 bits; Proposal and questions:
+ *       affine experts at other widths)
  *   {4, 128, MOE_SYMMETRIC, MOE_FP16} int4 symmetric, group 128, fp16 scales (W4A16)
  *       ("Sage-1.5-W4A16" model card, Model details)
  *   {16, 0, MOE_DENSE, MOE_BF16}      bf16 values (gate row only; the W4A16 export

@@ -275,8 +275,9 @@ int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const i
                         uint64_t ws_bytes, const moe_taps* taps, void* stream) {
   int st = experts_common("moe_experts_grouped", layer, x, rows, ids, p, shared_gate, y, ws, 65536);
   if (st) return st;
-  if (layer->d.routed.bits == 8 || layer->d.shared.bits == 8) {
-    set_error("moe_experts_grouped: 8-bit experts are read by the decode kernels only "
+  if (layer->d.routed.bits == 8 || layer->d.shared.bits == 8 || layer->d.routed.bits == 2 ||
+      layer->d.shared.bits == 2) {
+    set_error("moe_experts_grouped: 8-bit experts and 2-bit experts are read by the decode kernels only "
               "(moe_experts_decode, moe_forward_windows), not by the grouped GEMMs");
     return MOE_EUNSUPPORTED;
   }

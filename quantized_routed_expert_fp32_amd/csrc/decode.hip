@@ -203,6 +203,9 @@ __device__ __forceinline__ PairMasks pair_masks() {
   if constexpr (F == F_Q8) {
     k.m = ACT16 ? 0x03FC03FCu : 0x00780078u;   // fp16: the byte; bf16: a nibble
     k.q0 = k.q1 = k.q2 = 0u;
+  } else if constexpr (F == F_Q2) {
+    k.m = ACT16 ? 0x00C000C0u : 0x00180018u;
+    k.q0 = k.q1 = k.q2 = 0u;
   } else if constexpr (F == F_Q3) {
     k.m = ACT16 ? 0x01C001C0u : 0x00380038u;
     k.q0 = ACT16 ? 0x00400040u : 0x00080008u;
@@ -233,6 +236,18 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t* w, const PairMasks&
         o[2 * i + 1] = ((v >> 5) & k.m) | k.c;
         o[16 + 2 * i] = ((v >> 1) & k.m) | k.c;
         o[16 + 2 * i + 1] = ((v >> 9) & k.m) | k.c;
+      }
+    }
+  } else if constexpr (F == F_Q2) {
+    // pair j of word i at bits 2j: moved to mantissa bit 6 (fp16) or 3 (bf16)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t v = w[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        constexpr int T = ACT16 ? 6 : 3;
+        const uint32_t sv = 2 * j <= T ? v << (T - 2 * j) : v >> (2 * j - T);
+        o[8 * i + j] = (sv & k.m) | k.c;
       }
     }
   } else if constexpr (F == F_Q3) {
@@ -830,6 +845,7 @@ static hipError_t launch_decode_s(int fs, const DecodeArgs& a, hipStream_t s, hi
     case F_Q3: return launch_decode_t<FR, F_Q3>(a, s, ev);
     case F_S4: return launch_decode_t<FR, F_S4>(a, s, ev);
     case F_Q8: return launch_decode_t<FR, F_Q8>(a, s, ev);
+    case F_Q2: return launch_decode_t<FR, F_Q2>(a, s, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -840,6 +856,7 @@ hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s, hip
     case F_Q3: return launch_decode_s<F_Q3>(fs, a, s, ev);
     case F_S4: return launch_decode_s<F_S4>(fs, a, s, ev);
     case F_Q8: return launch_decode_s<F_Q8>(fs, a, s, ev);
+    case F_Q2: return launch_decode_s<F_Q2>(fs, a, s, ev);
   }
   return hipErrorInvalidValue;
 }

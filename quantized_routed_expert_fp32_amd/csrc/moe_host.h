@@ -9,7 +9,7 @@
 namespace moe {
 
 // kernel-side format ids (match moe_kernels.h)
-enum { KF_Q4 = 0, KF_Q3 = 1, KF_Q8 = 2, KF_S4 = 3, KF_DENSE = 4 };
+enum { KF_Q4 = 0, KF_Q3 = 1, KF_Q8 = 2, KF_S4 = 3, KF_DENSE = 4, KF_Q2 = 5 };
 
 struct FmtInfo {
   int kid;      // kernel format id
@@ -38,8 +38,9 @@ std::string fmt_name(const moe_qformat& f);
 
 uint64_t align256(uint64_t x);
 
-// Route scratch at the start of every workspace: per-row arrival counters
-// (zero between calls), gate-row logits, then [rows, E] fp32 logits.
+// Route scratch at the start of every workspace: the decode router's
+// hand-off words (a fixed area, zero between calls), gate-row logits, then
+// [rows, E] fp32 logits.
 struct RouteWs {
   uint64_t cand_off, gl_off, lg_off, total;
 };

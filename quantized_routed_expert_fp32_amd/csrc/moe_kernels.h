@@ -14,6 +14,7 @@
 //     8-bit) that v_dot2_f32_f16 takes directly:
 //       4-bit: word w holds pairs 4w..4w+3 at bits 4j (and 16+4j);
 //       8-bit: word w holds pairs 2w, 2w+1 at bits 8j (and 16+8j);
+//       2-bit: word w (0..1) holds pairs 8w..8w+7 at bits 2j (and 16+2j);
 //       3-bit: word w (0..2) holds pairs 5w..5w+4 at bits 3j (and 16+3j);
 //              pair 15 keeps bit b of its codes in bit 15 / bit 31 of word b.
 //   * scales: per tile, per 256-k block, per lane: 256/G entries of
@@ -36,7 +37,7 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 // kernel-side format ids
-enum { F_Q4 = 0, F_Q3 = 1, F_Q8 = 2, F_S4 = 3, F_DENSE = 4 };
+enum { F_Q4 = 0, F_Q3 = 1, F_Q8 = 2, F_S4 = 3, F_DENSE = 4, F_Q2 = 5 };
 
 template <int F> struct Fmt;
 template <> struct Fmt<F_Q4> {
@@ -51,6 +52,11 @@ template <> struct Fmt<F_Q3> {
 };
 template <> struct Fmt<F_Q8> {
   static constexpr int BITS = 8, G = 64, M = 256, CB = 32, WORDS = 8, SCB = 4;
+  static constexpr bool AFF = true;
+};
+template <> struct Fmt<F_Q2> {
+  // 2-bit codes also use the pair value 1 + q/16 (read by the decode kernels)
+  static constexpr int BITS = 2, G = 64, M = 16, CB = 8, WORDS = 2, SCB = 4;
   static constexpr bool AFF = true;
 };
 template <> struct Fmt<F_S4> {
@@ -153,6 +159,7 @@ template <> __device__ __forceinline__ void load_chunk<F_Q8>(const uint8_t* blk,
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // GFX9 raw buffer: stride 0, num_records in bytes, 32-bit data format word
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -164,6 +171,9 @@ template <int F> __device__ __forceinline__ void load_chunk_rs(rsrc_t r, uint32_
   if constexpr (F == F_Q3) {
     const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)voff, (int)soff, 0);
     w[0] = v.x; w[1] = v.y; w[2] = v.z;
+  } else if constexpr (F == F_Q2) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    w[0] = v.x; w[1] = v.y;
   } else if constexpr (F == F_Q8) {
     const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff / 2), (int)soff, 0);
     const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff / 2), (int)(soff + 64 * 16), 0);

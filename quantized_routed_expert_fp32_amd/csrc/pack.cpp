@@ -42,6 +42,7 @@ bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* o) {
   const bool q4 = f.bits == 4 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
   const bool q3 = f.bits == 3 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
   const bool q8 = f.bits == 8 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
+  const bool q2 = f.bits == 2 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
   const bool s4 = f.bits == 4 && f.group == 128 && f.mode == MOE_SYMMETRIC && f.scale_dtype == MOE_FP16;
   const bool dn = f.bits == 16 && f.mode == MOE_DENSE && f.scale_dtype == MOE_BF16;
   const bool expert = tc == TC_ROUTED || tc == TC_SHARED;
@@ -49,10 +50,12 @@ bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* o) {
   if (q4) { *o = {KF_Q4, 4, 64, 16, 4, true}; ok = true; }
   else if (q3 && expert) { *o = {KF_Q3, 3, 64, 12, 4, true}; ok = true; }
   else if (q8) { *o = {KF_Q8, 8, 64, 32, 4, true}; ok = true; }
+  else if (q2 && expert) { *o = {KF_Q2, 2, 64, 8, 4, true}; ok = true; }
   else if (s4) { *o = {KF_S4, 4, 128, 16, 2, false}; ok = true; }
   else if (dn && tc == TC_GATE_ROW) { *o = {KF_DENSE, 16, 0, 0, 0, false}; ok = true; }
   if (!ok) {
-    std::string acc = expert ? "{4,64,affine,bf16}, {3,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}"
+    std::string acc = expert ? "{4,64,affine,bf16}, {3,64,affine,bf16}, {8,64,affine,bf16}, {2,64,affine,bf16}, "
+                               "{4,128,symmetric,fp16}"
                      : tc == TC_ROUTER ? "{4,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}"
                      : "{4,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}, {16,0,dense,bf16}";
     set_error(std::string(class_name(tc)) + " format " + fmt_name(f) +
@@ -158,6 +161,16 @@ static inline uint32_t q8_word(uint32_t v) {
   const uint32_t b0 = v & 0xFF, b1 = (v >> 8) & 0xFF, b2 = (v >> 16) & 0xFF, b3 = v >> 24;
   return b0 | (b2 << 8) | (b1 << 16) | (b3 << 24);
 }
+// 2-bit: the 16 codes of a canonical word (k = 16w + i), even k in the low
+// half and odd k in the high half, pair j at bits 2j and 16 + 2j
+static inline uint32_t q2_word(uint32_t v) {
+  uint32_t even = 0, odd = 0;
+  for (int j = 0; j < 8; ++j) {
+    even |= ((v >> (4 * j)) & 3u) << (2 * j);
+    odd |= ((v >> (4 * j + 2)) & 3u) << (2 * j);
+  }
+  return even | (odd << 16);
+}
 static inline void q3_chunk(const uint32_t* c, uint32_t* o) {
   const unsigned __int128 s = (unsigned __int128)c[0] | ((unsigned __int128)c[1] << 32) |
                               ((unsigned __int128)c[2] << 64);
@@ -182,6 +195,9 @@ static inline void pack_chunk(int kid, const uint32_t* canon, uint32_t* o) {
       break;
     case KF_Q3:
       q3_chunk(canon, o);
+      break;
+    case KF_Q2:
+      for (int w = 0; w < 2; ++w) o[w] = q2_word(canon[w]);
       break;
   }
 }

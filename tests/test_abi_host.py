@@ -14,6 +14,8 @@ import pytest
 import oracle.moe_oracle as O
 import synth
 from synth import to_abi
+from synth.gen import Q2G64
+from dataclasses import replace
 
 qr = pytest.importorskip("quantized_routed_expert_fp32_amd")
 B = qr.binding
@@ -54,7 +56,8 @@ def test_pack_size_matches_layout_arithmetic():
 
 
 @pytest.mark.parametrize("cls,fmt", [
-    ("routed", (5, 64, 0, 0)), ("routed", (2, 64, 0, 0)), ("router", (3, 64, 0, 0)),
+    ("routed", (5, 64, 0, 0)), ("routed", (6, 64, 0, 0)), ("router", (3, 64, 0, 0)),
+    ("router", (2, 64, 0, 0)), ("gate_row", (2, 64, 0, 0)),
     ("shared", (4, 32, 0, 0)), ("routed", (4, 128, 1, 0)), ("gate_row", (16, 0, 2, 1)),
 ])
 def test_unsupported_formats_refused_by_name(cls, fmt):
@@ -101,6 +104,8 @@ def _read_chunk_codes(lane_words, bits):
             i = 2 * p + hi
             if bits == 4:
                 q[i] = (w[p // 4] >> (16 * hi + 4 * (p % 4))) & 0xF
+            elif bits == 2:
+                q[i] = (w[p // 8] >> (16 * hi + 2 * (p % 8))) & 3
             elif bits == 8:
                 q[i] = (w[p // 2] >> (16 * hi + 8 * (p % 2))) & 0xFF
             else:
@@ -142,10 +147,15 @@ def _read_matrix(buf, codes_off, scales_off, bits, group, affine, O_rows, K, row
     return q, s, b
 
 
-@pytest.mark.parametrize("base", [0, 2, 4])
+@pytest.mark.parametrize("base", [0, 2, 4, "q2"])
 def test_packed_layout_decodes_to_canonical(base):
     _lib()
-    spec = synth.make_tiny_config(synth.CONFIGS[base], cfg_id=200 + base, hidden=512,
+    if base == "q2":     # 2-bit routed and shared experts
+        src = replace(synth.CONFIGS[0], routed=Q2G64, shared=Q2G64)
+        cfg_id = 210
+    else:
+        src, cfg_id = synth.CONFIGS[base], 200 + base
+    spec = synth.make_tiny_config(src, cfg_id=cfg_id, hidden=512,
                                   n_experts=64, top_k=4, inter=256, shared_inter=256)
     Lh = synth.make_layer(spec, 0)
     buf, lc = B.pack_layer_host(_desc(spec), to_abi.tensors(Lh))
