@@ -12,7 +12,7 @@
  *     g = Wg x, u = Wu x, h = silu(g) * u, e_j = Wd h
  *   y[r,:]       = sum_j p[r,j] e_j + sigma[r] e_shared      (fp32, slots in pick order)
  * with every weight matrix stored quantised: affine w = s*q + b per group of
- * 64 (MLX-style, 2/3/4/8-bit), or symmetric w = s*(u-8) per group of 128 (W4A16).
+ * 64 (MLX-style, 2/3/4/5/6/8-bit), or symmetric w = s*(u-8) per group of 128 (W4A16).
  *
  * Conventions for every call:
  *   - Pointers named dev_* or documented as device memory must point to
@@ -59,8 +59,13 @@ enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1 };
  *   {8, 64, MOE_AFFINE, MOE_BF16}     MLX affine 8-bit, group 64 (router, gate row; experts
  *                                     on the decode path only: moe_experts_grouped refuses them)
  *       (same page and section: routers and the shared-expert gate at 8 bits)
- *   {2, 64, MOE_AFFINE, MOE_BF16}     MLX affine 2-bit, group 64 (routed/shared only, on the
- *                                     decode path only: moe_experts_grouped refuses them)
+ *   {2, 64, MOE_AFFINE, MOE_BF16}     MLX affine 2-bit, group 64
+ *   {5, 64, MOE_AFFINE, MOE_BF16}     MLX affine 5-bit, group 64
+ *   {6, 64, MOE_AFFINE, MOE_BF16}     MLX affine 6-bit, group 64
+ *                                     (these three: routed/shared only, on the decode path
+ *                                     only: moe_experts_grouped refuses them; 5/6-bit experts
+ *                                     pair with a shared expert of the same width or 4-bit
+ *                                     affine, other pairings are MOE_EUNSUPPORTED)
  *       ("qwen3_5_moe on native CUDA with 3-bit routed experts #803", What exists on
  *       native: the loader reads MLX affine at 2 to 8 bits; Proposal and questions:
  *       affine experts at other widths)

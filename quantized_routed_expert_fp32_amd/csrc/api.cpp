@@ -275,11 +275,16 @@ int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const i
                         uint64_t ws_bytes, const moe_taps* taps, void* stream) {
   int st = experts_common("moe_experts_grouped", layer, x, rows, ids, p, shared_gate, y, ws, 65536);
   if (st) return st;
-  if (layer->d.routed.bits == 8 || layer->d.shared.bits == 8 || layer->d.routed.bits == 2 ||
-      layer->d.shared.bits == 2) {
-    set_error("moe_experts_grouped: 8-bit experts and 2-bit experts are read by the decode kernels only "
-              "(moe_experts_decode, moe_forward_windows), not by the grouped GEMMs");
-    return MOE_EUNSUPPORTED;
+  {
+    // the grouped GEMMs read 3- and 4-bit experts; the other widths are read
+    // by the decode kernels only
+    const int rb = layer->d.routed.bits, sb = layer->d.shared.bits;
+    const int wb = (rb != 3 && rb != 4) ? rb : (sb != 3 && sb != 4) ? sb : 0;
+    if (wb) {
+      set_error("moe_experts_grouped: " + std::to_string(wb) + "-bit experts are read by the decode kernels "
+                "only (moe_experts_decode, moe_forward_windows), not by the grouped GEMMs");
+      return MOE_EUNSUPPORTED;
+    }
   }
   const GroupedWs wl = grouped_ws_layout(&layer->d, rows);
   if (ws_bytes < wl.total) {

@@ -206,6 +206,14 @@ __device__ __forceinline__ PairMasks pair_masks() {
   } else if constexpr (F == F_Q2) {
     k.m = ACT16 ? 0x00C000C0u : 0x00180018u;
     k.q0 = k.q1 = k.q2 = 0u;
+  } else if constexpr (F == F_Q5) {
+    k.m = ACT16 ? 0x03E003E0u : 0x007C007Cu;
+    k.q0 = k.q1 = k.q2 = 0u;
+  } else if constexpr (F == F_Q6) {
+    k.m = ACT16 ? 0x03F003F0u : 0x007E007Eu;
+    k.q0 = ACT16 ? 0x00F000F0u : 0x001E001Eu;   // low 4 bits of pairs 12..15
+    k.q1 = ACT16 ? 0x03000300u : 0x00600060u;   // their high 2 bits
+    k.q2 = 0u;
   } else if constexpr (F == F_Q3) {
     k.m = ACT16 ? 0x01C001C0u : 0x00380038u;
     k.q0 = ACT16 ? 0x00400040u : 0x00080008u;
@@ -250,6 +258,32 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t* w, const PairMasks&
         o[8 * i + j] = (sv & k.m) | k.c;
       }
     }
+  } else if constexpr (F == F_Q5) {
+    // value 1 + q/32: code bit 0 to mantissa bit 5 (fp16) or 2 (bf16)
+    constexpr int T = ACT16 ? 5 : 2;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const uint32_t v = w[i];
+      o[3 * i + 0] = ((v << T) & k.m) | k.c;
+      o[3 * i + 1] = ((ACT16 ? v : v >> 3) & k.m) | k.c;
+      o[3 * i + 2] = ((v >> (10 - T)) & k.m) | k.c;
+    }
+    uint32_t t = k.c;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) t |= (w[b] >> (15 - T - b)) & (0x00010001u << (T + b));
+    o[15] = t;
+  } else if constexpr (F == F_Q6) {
+    // value 1 + q/64: code bit 0 to mantissa bit 4 (fp16) or 1 (bf16)
+    constexpr int T = ACT16 ? 4 : 1;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const uint32_t v = w[i];
+      o[2 * i + 0] = ((v << T) & k.m) | k.c;
+      o[2 * i + 1] = ((v >> (6 - T)) & k.m) | k.c;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      o[12 + m] = ((w[4 + m / 2] >> (8 + 2 * (m % 2) - T)) & k.q1) | (((w[m] >> (12 - T)) & k.q0) | k.c);
   } else if constexpr (F == F_Q3) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
@@ -840,12 +874,18 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t
 
 template <int FR>
 static hipError_t launch_decode_s(int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
-  switch (fs) {
-    case F_Q4: return launch_decode_t<FR, F_Q4>(a, s, ev);
-    case F_Q3: return launch_decode_t<FR, F_Q3>(a, s, ev);
-    case F_S4: return launch_decode_t<FR, F_S4>(a, s, ev);
-    case F_Q8: return launch_decode_t<FR, F_Q8>(a, s, ev);
-    case F_Q2: return launch_decode_t<FR, F_Q2>(a, s, ev);
+  if constexpr (FR == F_Q5 || FR == F_Q6) {
+    // 5/6-bit routed experts: shared of the same width or 4-bit affine
+    if (fs == FR) return launch_decode_t<FR, FR>(a, s, ev);
+    if (fs == F_Q4) return launch_decode_t<FR, F_Q4>(a, s, ev);
+  } else {
+    switch (fs) {
+      case F_Q4: return launch_decode_t<FR, F_Q4>(a, s, ev);
+      case F_Q3: return launch_decode_t<FR, F_Q3>(a, s, ev);
+      case F_S4: return launch_decode_t<FR, F_S4>(a, s, ev);
+      case F_Q8: return launch_decode_t<FR, F_Q8>(a, s, ev);
+      case F_Q2: return launch_decode_t<FR, F_Q2>(a, s, ev);
+    }
   }
   return hipErrorInvalidValue;
 }
@@ -857,6 +897,8 @@ hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s, hip
     case F_S4: return launch_decode_s<F_S4>(fs, a, s, ev);
     case F_Q8: return launch_decode_s<F_Q8>(fs, a, s, ev);
     case F_Q2: return launch_decode_s<F_Q2>(fs, a, s, ev);
+    case F_Q5: return launch_decode_s<F_Q5>(fs, a, s, ev);
+    case F_Q6: return launch_decode_s<F_Q6>(fs, a, s, ev);
   }
   return hipErrorInvalidValue;
 }

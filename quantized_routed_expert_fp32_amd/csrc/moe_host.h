@@ -9,7 +9,7 @@
 namespace moe {
 
 // kernel-side format ids (match moe_kernels.h)
-enum { KF_Q4 = 0, KF_Q3 = 1, KF_Q8 = 2, KF_S4 = 3, KF_DENSE = 4, KF_Q2 = 5 };
+enum { KF_Q4 = 0, KF_Q3 = 1, KF_Q8 = 2, KF_S4 = 3, KF_DENSE = 4, KF_Q2 = 5, KF_Q5 = 6, KF_Q6 = 7 };
 
 struct FmtInfo {
   int kid;      // kernel format id

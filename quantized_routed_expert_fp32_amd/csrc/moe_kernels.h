@@ -15,6 +15,12 @@
 //       4-bit: word w holds pairs 4w..4w+3 at bits 4j (and 16+4j);
 //       8-bit: word w holds pairs 2w, 2w+1 at bits 8j (and 16+8j);
 //       2-bit: word w (0..1) holds pairs 8w..8w+7 at bits 2j (and 16+2j);
+//       5-bit: word w (0..4) holds pairs 3w..3w+2 at bits 5j (and 16+5j);
+//              pair 15 keeps bit b of its codes in bit 15 / bit 31 of word b;
+//       6-bit: word w (0..5) holds pairs 2w, 2w+1 at bits 6j (and 16+6j);
+//              pair 12+m keeps its low 4 bits in bits 12..15 (28..31) of
+//              word m, its high 2 bits in bits 12+2(m%2) (28+2(m%2)) of
+//              word 4+m/2;
 //       3-bit: word w (0..2) holds pairs 5w..5w+4 at bits 3j (and 16+3j);
 //              pair 15 keeps bit b of its codes in bit 15 / bit 31 of word b.
 //   * scales: per tile, per 256-k block, per lane: 256/G entries of
@@ -37,7 +43,7 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 // kernel-side format ids
-enum { F_Q4 = 0, F_Q3 = 1, F_Q8 = 2, F_S4 = 3, F_DENSE = 4, F_Q2 = 5 };
+enum { F_Q4 = 0, F_Q3 = 1, F_Q8 = 2, F_S4 = 3, F_DENSE = 4, F_Q2 = 5, F_Q5 = 6, F_Q6 = 7 };
 
 template <int F> struct Fmt;
 template <> struct Fmt<F_Q4> {
@@ -57,6 +63,16 @@ template <> struct Fmt<F_Q8> {
 template <> struct Fmt<F_Q2> {
   // 2-bit codes also use the pair value 1 + q/16 (read by the decode kernels)
   static constexpr int BITS = 2, G = 64, M = 16, CB = 8, WORDS = 2, SCB = 4;
+  static constexpr bool AFF = true;
+};
+template <> struct Fmt<F_Q5> {
+  // pair value 1 + q/32 (read by the decode kernels)
+  static constexpr int BITS = 5, G = 64, M = 32, CB = 20, WORDS = 5, SCB = 4;
+  static constexpr bool AFF = true;
+};
+template <> struct Fmt<F_Q6> {
+  // pair value 1 + q/64 (read by the decode kernels)
+  static constexpr int BITS = 6, G = 64, M = 64, CB = 24, WORDS = 6, SCB = 4;
   static constexpr bool AFF = true;
 };
 template <> struct Fmt<F_S4> {
@@ -174,6 +190,14 @@ template <int F> __device__ __forceinline__ void load_chunk_rs(rsrc_t r, uint32_
   } else if constexpr (F == F_Q2) {
     const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
     w[0] = v.x; w[1] = v.y;
+  } else if constexpr (F == F_Q5) {
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 16), (int)soff, 0);
+  } else if constexpr (F == F_Q6) {
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(voff + 16), (int)soff, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y;
   } else if constexpr (F == F_Q8) {
     const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff / 2), (int)soff, 0);
     const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff / 2), (int)(soff + 64 * 16), 0);

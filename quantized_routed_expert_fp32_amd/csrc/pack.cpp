@@ -43,6 +43,8 @@ bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* o) {
   const bool q3 = f.bits == 3 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
   const bool q8 = f.bits == 8 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
   const bool q2 = f.bits == 2 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
+  const bool q5 = f.bits == 5 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
+  const bool q6 = f.bits == 6 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
   const bool s4 = f.bits == 4 && f.group == 128 && f.mode == MOE_SYMMETRIC && f.scale_dtype == MOE_FP16;
   const bool dn = f.bits == 16 && f.mode == MOE_DENSE && f.scale_dtype == MOE_BF16;
   const bool expert = tc == TC_ROUTED || tc == TC_SHARED;
@@ -51,11 +53,13 @@ bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* o) {
   else if (q3 && expert) { *o = {KF_Q3, 3, 64, 12, 4, true}; ok = true; }
   else if (q8) { *o = {KF_Q8, 8, 64, 32, 4, true}; ok = true; }
   else if (q2 && expert) { *o = {KF_Q2, 2, 64, 8, 4, true}; ok = true; }
+  else if (q5 && expert) { *o = {KF_Q5, 5, 64, 20, 4, true}; ok = true; }
+  else if (q6 && expert) { *o = {KF_Q6, 6, 64, 24, 4, true}; ok = true; }
   else if (s4) { *o = {KF_S4, 4, 128, 16, 2, false}; ok = true; }
   else if (dn && tc == TC_GATE_ROW) { *o = {KF_DENSE, 16, 0, 0, 0, false}; ok = true; }
   if (!ok) {
     std::string acc = expert ? "{4,64,affine,bf16}, {3,64,affine,bf16}, {8,64,affine,bf16}, {2,64,affine,bf16}, "
-                               "{4,128,symmetric,fp16}"
+                               "{5,64,affine,bf16}, {6,64,affine,bf16}, {4,128,symmetric,fp16}"
                      : tc == TC_ROUTER ? "{4,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}"
                      : "{4,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}, {16,0,dense,bf16}";
     set_error(std::string(class_name(tc)) + " format " + fmt_name(f) +
@@ -94,6 +98,16 @@ int validate_desc(const moe_layer_desc* d) {
   if (!format_info(d->gate_row, TC_GATE_ROW, &fi)) return MOE_EUNSUPPORTED;
   if (!format_info(d->routed, TC_ROUTED, &fi)) return MOE_EUNSUPPORTED;
   if (!format_info(d->shared, TC_SHARED, &fi)) return MOE_EUNSUPPORTED;
+  // 5- and 6-bit experts: routed and shared of the same width, or routed at
+  // 5/6 bits beside a 4-bit affine shared expert (the kernels built for them)
+  const int rb = d->routed.bits, sb = d->shared.bits;
+  const bool wide_r = rb == 5 || rb == 6, wide_s = sb == 5 || sb == 6;
+  const bool q4_s = sb == 4 && d->shared.mode == MOE_AFFINE;
+  if ((wide_r || wide_s) && !(rb == sb || (wide_r && q4_s))) {
+    snprintf(buf, sizeof buf, "routed %d-bit with shared %d-bit experts unsupported: 5- and 6-bit experts pair "
+             "with a shared expert of the same width or 4-bit affine", rb, sb);
+    set_error(buf); return MOE_EUNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -171,6 +185,44 @@ static inline uint32_t q2_word(uint32_t v) {
   }
   return even | (odd << 16);
 }
+// n bits of a chunk's canonical stream from bit pos (words: the chunk's)
+static inline uint32_t stream_bits(const uint32_t* c, int nwords, int pos, int n) {
+  const int w = pos / 32, b = pos % 32;
+  uint64_t v = c[w];
+  if (w + 1 < nwords) v |= (uint64_t)c[w + 1] << 32;
+  return (uint32_t)(v >> b) & ((1u << n) - 1u);
+}
+// 5-bit: pair p < 15 in word p/3 at bits 5 (p mod 3) (and 16 + that); pair 15
+// keeps bit b of its codes in bit 15 / bit 31 of word b
+static inline void q5_chunk(const uint32_t* c, uint32_t* o) {
+  for (int w = 0; w < 5; ++w) o[w] = 0;
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t q = stream_bits(c, 5, 5 * i, 5);
+    const int p = i >> 1, hi = i & 1;
+    if (p < 15) {
+      o[p / 3] |= q << ((hi ? 16 : 0) + 5 * (p % 3));
+    } else {
+      for (int b = 0; b < 5; ++b) o[b] |= ((q >> b) & 1u) << (hi ? 31 : 15);
+    }
+  }
+}
+// 6-bit: pair p < 12 in word p/2 at bits 6 (p mod 2) (and 16 + that); pair
+// 12 + m keeps its low 4 bits in bits 12..15 of word m and its high 2 bits in
+// bits 12 + 2 (m mod 2) of word 4 + m/2 (each also at 16 + that for the odd code)
+static inline void q6_chunk(const uint32_t* c, uint32_t* o) {
+  for (int w = 0; w < 6; ++w) o[w] = 0;
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t q = stream_bits(c, 6, 6 * i, 6);
+    const int p = i >> 1, h = (i & 1) ? 16 : 0;
+    if (p < 12) {
+      o[p / 2] |= q << (h + 6 * (p % 2));
+    } else {
+      const int m = p - 12;
+      o[m] |= (q & 15u) << (h + 12);
+      o[4 + m / 2] |= (q >> 4) << (h + 12 + 2 * (m % 2));
+    }
+  }
+}
 static inline void q3_chunk(const uint32_t* c, uint32_t* o) {
   const unsigned __int128 s = (unsigned __int128)c[0] | ((unsigned __int128)c[1] << 32) |
                               ((unsigned __int128)c[2] << 64);
@@ -198,6 +250,12 @@ static inline void pack_chunk(int kid, const uint32_t* canon, uint32_t* o) {
       break;
     case KF_Q2:
       for (int w = 0; w < 2; ++w) o[w] = q2_word(canon[w]);
+      break;
+    case KF_Q5:
+      q5_chunk(canon, o);
+      break;
+    case KF_Q6:
+      q6_chunk(canon, o);
       break;
   }
 }

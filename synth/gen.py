@@ -20,7 +20,7 @@ Distributions (per workload; see the recipe table in the design notes):
   * 4-bit affine: bias = -8*scale + N(0, 1e-3) (standard deviation 1e-3);
   * 3-bit affine: bias = -4*scale exactly;
   * 8-bit affine: bias = -128*scale + N(0, 1e-3);
-  * 2-bit affine: bias = -2*scale + N(0, 1e-3);
+  * 2-, 5- and 6-bit affine: bias = -c*scale + N(0, 1e-3), c = 2, 16, 32;
   * router and gate row: scale and noise multiplied by a closed-form factor
     so the fp32 logits of x ~ N(0,1) have unit variance
     (factor = 1/sqrt(H * E[w^2]), with E[w^2] = E[s^2]*E[(q-c)^2] + noise^2);
@@ -56,6 +56,8 @@ Q4G64 = QFormat(4, 64, AFFINE, BF16)
 Q3G64 = QFormat(3, 64, AFFINE, BF16)
 Q8G64 = QFormat(8, 64, AFFINE, BF16)
 Q2G64 = QFormat(2, 64, AFFINE, BF16)
+Q5G64 = QFormat(5, 64, AFFINE, BF16)
+Q6G64 = QFormat(6, 64, AFFINE, BF16)
 S4G128 = QFormat(4, 128, SYMMETRIC, FP16)
 DENSE_BF16 = QFormat(16, 0, DENSE, BF16)
 
@@ -167,7 +169,7 @@ _ES2 = (0.002 ** 2 + 0.002 * 0.02 + 0.02 ** 2) / 3.0   # E[s^2], s ~ U(0.002, 0.
 
 
 def _code_offset(fmt: QFormat) -> int:
-    return {2: 2, 3: 4, 4: 8, 8: 128}[fmt.bits]
+    return {2: 2, 3: 4, 4: 8, 5: 16, 6: 32, 8: 128}[fmt.bits]
 
 
 def _noise_std(fmt: QFormat) -> float:

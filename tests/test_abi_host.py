@@ -14,7 +14,7 @@ import pytest
 import oracle.moe_oracle as O
 import synth
 from synth import to_abi
-from synth.gen import Q2G64
+from synth.gen import Q2G64, Q3G64, Q4G64, Q5G64, Q6G64
 from dataclasses import replace
 
 qr = pytest.importorskip("quantized_routed_expert_fp32_amd")
@@ -56,7 +56,8 @@ def test_pack_size_matches_layout_arithmetic():
 
 
 @pytest.mark.parametrize("cls,fmt", [
-    ("routed", (5, 64, 0, 0)), ("routed", (6, 64, 0, 0)), ("router", (3, 64, 0, 0)),
+    ("routed", (7, 64, 0, 0)), ("routed", (5, 128, 0, 0)), ("router", (3, 64, 0, 0)),
+    ("router", (6, 64, 0, 0)),
     ("router", (2, 64, 0, 0)), ("gate_row", (2, 64, 0, 0)),
     ("shared", (4, 32, 0, 0)), ("routed", (4, 128, 1, 0)), ("gate_row", (16, 0, 2, 1)),
 ])
@@ -72,6 +73,22 @@ def test_unsupported_formats_refused_by_name(cls, fmt):
     assert "MOE_EUNSUPPORTED" in msg
     assert {"router": "router", "gate_row": "gate row", "routed": "routed experts",
             "shared": "shared expert"}[cls] in msg
+
+
+@pytest.mark.parametrize("routed,shared,ok", [(Q5G64, Q5G64, True), (Q6G64, Q4G64, True),
+                                               (Q5G64, Q3G64, False), (Q4G64, Q6G64, False),
+                                               (Q5G64, Q6G64, False)])
+def test_wide_expert_pairings(routed, shared, ok):
+    """5/6-bit experts pair with a shared expert of the same width or 4-bit
+    affine; other pairings are refused by name before anything is built."""
+    _lib()
+    spec = replace(synth.CONFIGS[0], routed=routed, shared=shared)
+    d = B.layer_desc(*to_abi.desc_args(spec))
+    if ok:
+        assert B.pack_size(d) > 0
+    else:
+        with pytest.raises(B.MoeError, match="MOE_EUNSUPPORTED.*5- and 6-bit experts pair"):
+            B.pack_size(d)
 
 
 @pytest.mark.parametrize("field,val", [("hidden", 300), ("n_experts", 100), ("top_k", 9),
@@ -106,6 +123,17 @@ def _read_chunk_codes(lane_words, bits):
                 q[i] = (w[p // 4] >> (16 * hi + 4 * (p % 4))) & 0xF
             elif bits == 2:
                 q[i] = (w[p // 8] >> (16 * hi + 2 * (p % 8))) & 3
+            elif bits == 5:
+                if p < 15:
+                    q[i] = (w[p // 3] >> (16 * hi + 5 * (p % 3))) & 31
+                else:
+                    q[i] = sum(((w[b] >> (31 if hi else 15)) & 1) << b for b in range(5))
+            elif bits == 6:
+                if p < 12:
+                    q[i] = (w[p // 2] >> (16 * hi + 6 * (p % 2))) & 63
+                else:
+                    m = p - 12
+                    q[i] = ((w[m] >> (16 * hi + 12)) & 15) | (((w[4 + m // 2] >> (16 * hi + 12 + 2 * (m % 2))) & 3) << 4)
             elif bits == 8:
                 q[i] = (w[p // 2] >> (16 * hi + 8 * (p % 2))) & 0xFF
             else:
@@ -147,12 +175,13 @@ def _read_matrix(buf, codes_off, scales_off, bits, group, affine, O_rows, K, row
     return q, s, b
 
 
-@pytest.mark.parametrize("base", [0, 2, 4, "q2"])
+@pytest.mark.parametrize("base", [0, 2, 4, "q2", "q5", "q6"])
 def test_packed_layout_decodes_to_canonical(base):
     _lib()
-    if base == "q2":     # 2-bit routed and shared experts
-        src = replace(synth.CONFIGS[0], routed=Q2G64, shared=Q2G64)
-        cfg_id = 210
+    if base in ("q2", "q5", "q6"):     # routed and shared experts of that width
+        f = {"q2": Q2G64, "q5": Q5G64, "q6": Q6G64}[base]
+        src = replace(synth.CONFIGS[0], routed=f, shared=f)
+        cfg_id = 210 + f.bits
     else:
         src, cfg_id = synth.CONFIGS[base], 200 + base
     spec = synth.make_tiny_config(src, cfg_id=cfg_id, hidden=512,

@@ -13,7 +13,7 @@ import pytest
 
 import oracle.moe_oracle as O
 import synth
-from synth.gen import Q2G64, Q3G64, Q4G64, Q8G64, S4G128, QFormat, QTensor
+from synth.gen import Q2G64, Q3G64, Q4G64, Q5G64, Q6G64, Q8G64, S4G128, QFormat, QTensor
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -75,7 +75,7 @@ def _py_unpack(words_row, bits, cols):
     return out
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 def test_unpack_matches_bit_by_bit_definition(bits):
     rng = np.random.default_rng(7 + bits)
     cols = 256
@@ -95,7 +95,7 @@ def test_bf16_fp16_exact_conversion():
 
 
 # ------------------------------------------------------------ exact integer case
-@pytest.mark.parametrize("fmt", [Q4G64, Q3G64, Q8G64, Q2G64, S4G128])
+@pytest.mark.parametrize("fmt", [Q4G64, Q3G64, Q8G64, Q2G64, Q5G64, Q6G64, S4G128])
 def test_integer_exact_projection(fmt):
     """s = 2^-k per group (k varies), b = -c*s: every projection is a dyadic rational."""
     rng = np.random.default_rng(11)
@@ -103,7 +103,7 @@ def test_integer_exact_projection(fmt):
     words = rng.integers(0, 1 << 32, size=(rows, cols * fmt.bits // 32), dtype=np.uint32)
     ng = cols // fmt.group
     kexp = rng.integers(3, 9, size=(rows, ng))
-    off = {2: 2, 3: 4, 4: 8, 8: 128}[fmt.bits]
+    off = {2: 2, 3: 4, 4: 8, 5: 16, 6: 32, 8: 128}[fmt.bits]
     # bf16 / fp16 bits of 2^-k and -off * 2^-k
     if fmt.scale_dtype == O.BF16:
         s_bits = ((127 - kexp) << 7).astype(np.uint16)
