@@ -295,3 +295,24 @@ def test_pick_order_from_crafted_logits(cfg, rows):
         assert (np.isnan(p) == nan).all(), f"{name}: NaN pattern of p"
         assert np.allclose(p[~nan], ref.p[~nan], rtol=1e-6, atol=1e-7), f"{name}: p {p[0]} vs {ref.p[0]}"
         assert (sg == 0.5).all(), f"{name}: gate"
+
+
+def test_tree_window_rows_equal_one_row_steps():
+    """A verify window shaped like a draft tree: 16 rows drawn from 6
+    distinct inputs, some repeated (sibling branches that carry the same
+    hidden state), so units serve up to several copies of a row in one pass.
+    Every row equals its one-row step bit for bit, and equal inputs give
+    equal bits."""
+    spec = synth.CONFIGS[1]
+    Lh, dev, _ = layer_of(spec, 3)
+    base = synth.make_x(spec, 3, 6, rep=61)
+    tree = [0, 1, 1, 2, 3, 3, 3, 4, 1, 5, 5, 0, 2, 4, 4, 3]
+    xb = base[tree]
+    g = run_gpu(dev, Lh, xb, taps=False)
+    for r, src in enumerate(tree):
+        solo = run_gpu(dev, Lh, base[src:src + 1], taps=False)
+        for key in ("ids", "p", "sg", "y"):
+            u, v = solo[key][0], g[key][r]
+            if u.dtype == np.float32:
+                u, v = u.view(np.uint32), v.view(np.uint32)
+            assert np.array_equal(u, v), f"row {r} (input {src}) {key} differs"
