@@ -149,6 +149,12 @@ typedef struct moe_taps {
    * phase of two launches takes the first one's start and the second one's
    * end). Events are used only outside stream capture. */
   void* kernel_events[8];
+  /* Test hook for the failure path of the decode router (up to 32 rows):
+   * 0 keeps the kernel's own bound on its wait for the tiles' hand-off; a
+   * negative value makes the wait end at once, so every row is reported as
+   * not handed off (ids -1, NaN p and shared_gate) and the workspace must be
+   * zero-filled before its next use. */
+  int32_t route_wait_limit;
 } moe_taps;
 
 /* ------------------------------------------------------------ pack loader */
@@ -208,7 +214,13 @@ int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t*
  *   ws         device workspace, >= moe_workspace_size bytes for `rows`,
  *              zero-filled before its first use (see moe_workspace_size)
  *   taps       NULL, or taps->logits / kernel_events (route: 1 kernel)
- * A row holding NaN gets the NaN-ordered picks 0..k-1 and NaN weights. */
+ * A row holding NaN gets the NaN-ordered picks 0..k-1 and NaN weights.
+ * Up to 32 rows run as one launch whose workgroups hand their tiles' picks to
+ * one another and must all be resident at once; if another kernel holds the
+ * GPU so long that a row's hand-off does not arrive within the kernel's
+ * bounded wait, that row gets ids -1 and NaN p and shared_gate (never a pick
+ * from missing entries), and the workspace must be zero-filled again before
+ * its next use. */
 int moe_route(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
               int32_t* ids, float* p, float* shared_gate, void* ws, uint64_t ws_bytes,
               const moe_taps* taps, void* stream);

@@ -60,7 +60,7 @@ class LayerC(C.Structure):
 
 class TapsC(C.Structure):
     _fields_ = [("logits", C.c_void_p), ("gu", C.c_void_p), ("h", C.c_void_p), ("e", C.c_void_p),
-                ("kernel_events", C.c_void_p * 8)]
+                ("kernel_events", C.c_void_p * 8), ("route_wait_limit", C.c_int32)]
 
 
 EXPORTS = ["moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
@@ -220,6 +220,7 @@ def _taps(taps: Optional[dict]):
         setattr(t, k, v.data_ptr() if v is not None else None)
     for i, ev in enumerate(taps.get("events") or []):
         t.kernel_events[i] = ev.cuda_event if ev is not None else None
+    t.route_wait_limit = int(taps.get("route_wait_limit", 0))
     return C.byref(t)
 
 

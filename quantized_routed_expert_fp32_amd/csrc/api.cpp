@@ -167,6 +167,7 @@ int moe_route(const moe_layer* layer, const void* x, int rows, const float* logi
   a.sg = shared_gate;
   a.R = rows;
   a.logits = taps ? taps->logits : nullptr;
+  a.wait_limit = (taps && taps->route_wait_limit < 0) ? 0 : (1 << 22);
   const RouteWs rw = route_ws_layout(&layer->d, rows);
   uint8_t* wb = static_cast<uint8_t*>(ws);
   a.lg_ws = reinterpret_cast<float*>(wb + rw.lg_off);

@@ -18,6 +18,7 @@ struct RouteArgs {
   float* lg_ws;    // [R, E] scratch: logits before the bias
   float* gl_ws;    // [R] scratch: gate-row logits
   uint64_t* cand;  // [R, 32] tile picks (id + 1) << 32 | value bits; zero between calls
+  int wait_limit;  // polls of the hand-off before a row is reported as not handed off
 };
 
 // Offsets of one expert class (routed or shared) inside the packed layer.

@@ -191,7 +191,9 @@ __device__ __forceinline__ void pick_and_store(const RouteArgs& a, int row, cons
 // bypass its XCD's L2) until none is zero, clears them for the next call and
 // picks from its own entries and theirs. Every workgroup of the launch is
 // resident at once (E/64 * rows <= 128 workgroups), so the wait ends; it is
-// bounded all the same. One wave past the slice waves forms the gate-row
+// bounded all the same, and a row whose entries do not arrive within the
+// bound gets ids -1 and NaN weights and gate. One wave past the slice waves
+// forms the gate-row
 // logit in tile 0, beside the slices.
 template <int FR, int FG, int ACT16>
 __global__ __launch_bounds__(576) void k_route(RouteArgs a, const uint16_t* __restrict__ x) {
@@ -253,12 +255,22 @@ __global__ __launch_bounds__(576) void k_route(RouteArgs a, const uint16_t* __re
   const bool remote = lane >= k && lane < nc;
   uint64_t* src = &cand[8 * (lane / k) + lane % k];
   uint64_t word = 0;
-  for (int spin = 0; spin < (1 << 22); ++spin) {
+  for (int spin = 0; spin < a.wait_limit; ++spin) {
     if (remote) word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (__ballot(remote && word == 0) == 0) break;
     __builtin_amdgcn_s_sleep(1);
   }
   if (remote) __hip_atomic_store(src, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // empty for the next call
+  if (__ballot(remote && word == 0) != 0) {
+    // the wait bound ran out (the tile workgroups were not all resident):
+    // the row is marked invalid rather than picked from missing entries
+    if (lane < k) {
+      a.ids[(uint64_t)row * k + lane] = -1;
+      a.p[(uint64_t)row * k + lane] = __uint_as_float(0x7FC00000u);
+    }
+    if (lane == 0) a.sg[row] = __uint_as_float(0x7FC00000u);
+    return;
+  }
   const float cv = remote ? __uint_as_float((uint32_t)word) : val;
   const int ci = remote ? (int)(word >> 32) - 1 : id;
   const float c = s_gate;

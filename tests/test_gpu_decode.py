@@ -316,3 +316,28 @@ def test_tree_window_rows_equal_one_row_steps():
             if u.dtype == np.float32:
                 u, v = u.view(np.uint32), v.view(np.uint32)
             assert np.array_equal(u, v), f"row {r} (input {src}) {key} differs"
+
+
+def test_router_wait_bound_reports_rows_not_handed_off():
+    """The decode router's failure path, forced from the host: with the
+    test hook ending the hand-off wait at once, every row is reported as not
+    handed off (ids -1, NaN weights and gate) instead of being picked from
+    missing entries; after the documented zero-fill of the workspace the
+    next call equals a call on a fresh workspace bit for bit."""
+    from gpu_common import binding, to_dev_x, torch_mod
+    B = binding()
+    torch = torch_mod()
+    spec = synth.CONFIGS[1]
+    Lh, dev, _ = layer_of(spec, 0)
+    x = to_dev_x(synth.make_x(spec, 0, 8, rep=71))
+    ref = B.route(dev, x, ws=B.new_workspace(dev, 8, False))
+    ws = B.new_workspace(dev, 8, False)
+    ids, p, sg = B.route(dev, x, ws=ws, taps={"route_wait_limit": -1})
+    torch.cuda.synchronize()
+    assert (ids.cpu() == -1).all()
+    assert torch.isnan(p.cpu()).all() and torch.isnan(sg.cpu()).all()
+    ws.zero_()
+    again = B.route(dev, x, ws=ws)
+    torch.cuda.synchronize()
+    for name, u, v in zip(("ids", "p", "sg"), again, ref):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32)), name
