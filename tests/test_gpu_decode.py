@@ -341,3 +341,29 @@ def test_router_wait_bound_reports_rows_not_handed_off():
     torch.cuda.synchronize()
     for name, u, v in zip(("ids", "p", "sg"), again, ref):
         assert torch.equal(u.view(torch.int32), v.view(torch.int32)), name
+
+
+@pytest.mark.parametrize("rows", [32, 33])
+def test_route_at_the_one_launch_limit(rows):
+    """32 rows are the most the one-launch decode router takes (128 tile
+    workgroups that hand picks to one another, all resident at once); 33 go
+    to the logits kernel and the per-row pick. At full size both give the
+    oracle's ids (except near-tie rows), weights within 1e-5 and the gate
+    within 1e-6."""
+    from gpu_common import binding, near_tie_rows, to_dev_x, torch_mod
+    B = binding()
+    torch = torch_mod()
+    spec = synth.CONFIGS[1]
+    Lh, dev, dense = layer_of(spec, 5)
+    xb = synth.make_x(spec, 5, rows, rep=81)
+    ids, p, sg = B.route(dev, to_dev_x(xb), ws=B.new_workspace(dev, rows, rows > 16))
+    torch.cuda.synchronize()
+    ids, p, sg = ids.cpu().numpy(), p.cpu().numpy(), sg.cpu().numpy()
+    Wr, wg = dense.router()
+    ref = O.route(O.act_to_f64(xb, spec.act), Wr, wg, spec.top_k)
+    near = near_tie_rows(ref, spec.top_k)
+    same = (ids == ref.ids).all(axis=1)
+    assert (same | near).all(), f"ids differ on rows {np.where(~same & ~near)[0]}"
+    assert np.allclose(p[same], ref.p[same], rtol=0, atol=1e-5)
+    assert np.allclose(sg, ref.sigma, rtol=0, atol=1e-6)
+    log(f"[route] rows {rows}: near-tie rows {int(near.sum())}, differing {int((~same).sum())}")
