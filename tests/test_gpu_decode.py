@@ -270,13 +270,15 @@ def _pick_biases(E, k, seed=7):
     return out
 
 
-@pytest.mark.parametrize("cfg,rows", [(1, 3), (1, 40), (2, 3), (2, 40)])
+@pytest.mark.parametrize("cfg,rows", [(1, 3), (1, 40), (2, 3), (2, 40), (4, 3), (4, 40)])
 def test_pick_order_from_crafted_logits(cfg, rows):
     """x = 0 makes every logit its logit bias, so crafted biases test the
     pick itself: ids equal the oracle's (value desc, id asc, NaN first,
     -0 == +0) bit for bit, p agrees within 1e-6 (NaN where the oracle's is),
     and the gate is sigmoid(0) = 1/2. 3 rows take the one-launch decode
-    router, 40 rows the prompt-chunk logits kernel and the per-row pick."""
+    router, 40 rows the prompt-chunk logits kernel and the per-row pick;
+    routers: 4-bit affine, 8-bit affine, int4-symmetric g128 with fp16
+    activations and a bf16 gate row."""
     from gpu_common import binding, to_dev_x, torch_mod
     B = binding()
     torch = torch_mod()
