@@ -150,8 +150,8 @@ typedef struct moe_taps {
    * end). Events are used only outside stream capture. */
   void* kernel_events[8];
   /* Test hook for the failure path of the decode router (up to 32 rows):
-   * 0 keeps the kernel's own bound on its wait for the tiles' hand-off; a
-   * negative value makes the wait end at once, so every row is reported as
+   * 0 (or any positive value) keeps the kernel's own bound on its wait for
+   * the tiles' hand-off; a negative value makes the wait end at once, so every row is reported as
    * not handed off (ids -1, NaN p and shared_gate) and the workspace must be
    * zero-filled before its next use. */
   int32_t route_wait_limit;
