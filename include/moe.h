@@ -151,9 +151,9 @@ typedef struct moe_taps {
   void* kernel_events[8];
   /* Test hook for the failure path of the decode router (up to 32 rows):
    * 0 (or any positive value) keeps the kernel's own bound on its wait for
-   * the tiles' hand-off; a negative value makes the wait end at once, so every row is reported as
-   * not handed off (ids -1, NaN p and shared_gate) and the workspace must be
-   * zero-filled before its next use. */
+   * the tiles' hand-off; a negative value makes the wait end at once, so
+   * every row is reported as not handed off (ids -1, NaN p and shared_gate)
+   * and the failure is recorded in the workspace (see moe_route_failures). */
   int32_t route_wait_limit;
 } moe_taps;
 
@@ -189,22 +189,27 @@ int moe_pack_layer(const moe_layer_desc* d, const moe_layer_src* src,
 /* Workspace bytes for moe_route plus moe_experts_decode (grouped = 0) or
  * plus moe_experts_grouped (grouped = 1) at `rows` rows. One buffer of this
  * size serves both calls of a layer (calls on one stream run in order).
- * A workspace must be zero-filled before its first use: it holds hand-off
- * words that workgroups of one call use to pass work to each other, and
- * every call leaves them at zero again. Any call may use a workspace larger
- * than it needs (say one sized for the most rows of the grouped form); each
- * call checks ws_bytes against its own need (MOE_ENOSPACE). Calls that
- * overlap on one workspace (e.g. on two streams) race; give each stream its
- * own workspace. */
+ * A workspace must be zero-filled once, before its first use: its first
+ * bytes hold the decode router's hand-off words, tagged with a call counter
+ * kept beside them, and a sticky failure count (moe_route_failures). Every
+ * call leaves them consistent for the next, so the workspace needs no
+ * clearing between calls, also when calls are captured and replayed. Any
+ * call may use a workspace larger than it needs (say one sized for the most
+ * rows of the grouped form); each call checks ws_bytes against its own need
+ * (MOE_ENOSPACE). Calls that overlap on one workspace (e.g. on two streams)
+ * race; give each stream its own workspace. */
 int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t* bytes);
 
 /* ------------------------------------------------------------- hot path */
 
-/* Router of the layer ("qwen3_5_moe on native CUDA with 3-bit routed experts
- * #803", Activity, comment "Progress on the 4-bit gate": fp32 logits over the
- * experts and the shared expert's gate row; top-k by logit with ties to the
- * lower id; weights exp(l - l_top) over the k; the shared expert as a slot
- * weighted by sigmoid of its gate). Weights are renormalised over the k picks.
+/* Router of the layer. Source: "qwen3_5_moe on native CUDA with 3-bit routed
+ * experts #803", Activity, the "Progress on the 4-bit gate" comment, which
+ * gives the routing arithmetic: fp32 logits for every expert and for the
+ * shared expert's gate row, the k largest logits picked with equal logits
+ * going to the smaller expert id, each pick weighted by the exponential of
+ * its logit minus the largest one, and the shared expert added as one more
+ * slot scaled by the sigmoid of its gate logit. Here the k weights are also
+ * divided by their sum (a reading of that comment).
  *   x          device, [rows, H] activations (act_dtype), row-major
  *   rows       >= 1
  *   logit_bias device, [E] fp32 added to the logits before the pick, or NULL
@@ -219,8 +224,11 @@ int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t*
  * one another and must all be resident at once; if another kernel holds the
  * GPU so long that a row's hand-off does not arrive within the kernel's
  * bounded wait, that row gets ids -1 and NaN p and shared_gate (never a pick
- * from missing entries), and the workspace must be zero-filled again before
- * its next use. */
+ * from missing or stale entries) and the failure is counted in the
+ * workspace. The count is sticky: until moe_route_failures clears it, every
+ * later call of this router on that workspace reports its rows the same way
+ * (so a sequence of calls, such as moe_forward_windows, stops producing
+ * results after the first failure instead of continuing silently). */
 int moe_route(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
               int32_t* ids, float* p, float* shared_gate, void* ws, uint64_t ws_bytes,
               const moe_taps* taps, void* stream);
@@ -244,13 +252,15 @@ int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const in
 /* Route and experts of any number of rows through the decode step's
  * arithmetic, in consecutive windows of up to 16 rows on `stream`: every
  * row's ids, p, shared_gate and y are bit-identical to its one-row
- * moe_route + moe_experts_decode step, however the rows are cut into calls
- * ("Native server: --backend xpu for Nemotron on Intel Arc", description:
- * windows and prompt rows take the decode step's arithmetic and a prompt
- * gives the same bits however it is cut; "Sage-A1.5 ... #1329", Limits to
- * agree on: the grouped MoE's sum order differs from one stream alone).
- * Slower than moe_experts_grouped for wide prompts: each window reads the
- * experts its rows picked.
+ * moe_route + moe_experts_decode step, however the rows are cut into calls.
+ * Sources: "Native server: --backend xpu for Nemotron on Intel Arc", the
+ * review thread (prompt rows and verify windows are to reproduce the one-row
+ * step exactly, whatever the cut of the prompt); "Sage-A1.5 ... #1329",
+ * Limits to agree on (the grouped form adds in another order than one
+ * stream alone). Slower than moe_experts_grouped for wide prompts: each
+ * window reads the experts its rows picked. A router failure in one window
+ * leaves that window's rows and every later one marked as failed (ids -1,
+ * NaN), see moe_route; moe_route_failures reports it.
  *   x, logit_bias, ids, p, shared_gate, y: as moe_route / moe_experts_decode,
  *   for `rows` rows (1..65536)
  *   ws: >= moe_workspace_size(rows = min(rows, 16), grouped = 0) bytes,
@@ -272,6 +282,18 @@ int moe_forward_windows(const moe_layer* layer, const void* x, int rows, const f
 int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const int32_t* ids,
                         const float* p, const float* shared_gate, float* y, void* ws,
                         uint64_t ws_bytes, const moe_taps* taps, void* stream);
+
+/* Router failures recorded in workspace ws (moe_workspace_size bytes, on
+ * the device): *count = the number of rows the decode router reported as
+ * failed (ids -1, NaN weights) since the count was last cleared: rows whose
+ * hand-off missed the wait bound, and every row of the later calls while the
+ * count was nonzero (0 when every call succeeded). With clear != 0 a nonzero count is reset to zero afterwards,
+ * which ends the sticky state described at moe_route. Copies 4 bytes to the
+ * host and synchronises `stream` (work enqueued before it has finished);
+ * not for use during stream capture.
+ * Errors: MOE_EINVAL (null), MOE_ENOSPACE (ws_bytes below the fixed router
+ * area), MOE_EHIP. */
+int moe_route_failures(void* ws, uint64_t ws_bytes, int clear, uint32_t* count, void* stream);
 
 /* ----------------------------------------------------------- diagnostics */
 const char* moe_status_string(int status);

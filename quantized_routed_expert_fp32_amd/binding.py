@@ -65,7 +65,8 @@ class TapsC(C.Structure):
 
 EXPORTS = ["moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
            "moe_workspace_size", "moe_route", "moe_experts_decode", "moe_experts_grouped",
-           "moe_forward_windows", "moe_status_string", "moe_last_error", "moe_version"]
+           "moe_forward_windows", "moe_route_failures", "moe_status_string", "moe_last_error",
+           "moe_version"]
 
 _lib = None
 
@@ -93,9 +94,10 @@ def lib() -> C.CDLL:
                                      C.POINTER(TapsC), vp]
     L.moe_experts_grouped.argtypes = L.moe_experts_decode.argtypes
     L.moe_forward_windows.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, vp, u64, vp]
+    L.moe_route_failures.argtypes = [vp, u64, i32, C.POINTER(C.c_uint32), vp]
     for f in ("moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
               "moe_workspace_size", "moe_route", "moe_experts_decode", "moe_experts_grouped",
-              "moe_forward_windows"):
+              "moe_forward_windows", "moe_route_failures"):
         getattr(L, f).restype = C.c_int
     L.moe_status_string.argtypes = [C.c_int]
     L.moe_status_string.restype = C.c_char_p
@@ -203,10 +205,37 @@ def workspace_size(desc: LayerDescC, rows: int, grouped: bool) -> int:
     return n.value
 
 
-def new_workspace(layer: "Layer", rows: int, grouped: bool, device="cuda"):
-    """A zero-filled workspace for `rows` rows (route + experts of one layer)."""
+def new_workspace(layer: "Layer", rows: int, grouped: bool, device="cuda", stream=None):
+    """A zero-filled workspace for `rows` rows (route + experts of one layer),
+    allocated and cleared on `stream` (default: the current stream), so that
+    calls enqueued on that stream find it cleared."""
     import torch
-    return torch.zeros(workspace_size(layer.desc, rows, grouped), dtype=torch.uint8, device=device)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    with torch.cuda.stream(s):
+        return torch.zeros(workspace_size(layer.desc, rows, grouped), dtype=torch.uint8, device=device)
+
+
+def route_failures(ws, clear=True, stream=None) -> int:
+    """moe_route_failures: rows whose decode-router hand-off missed the wait
+    bound since the count was last cleared (synchronises `stream`)."""
+    n = C.c_uint32()
+    _check(lib().moe_route_failures(_ptr(ws), ws.numel() * ws.element_size(), int(clear), C.byref(n),
+                                    _stream_ptr(stream)), "moe_route_failures")
+    return n.value
+
+
+def _on(stream):
+    """Context in which outputs of a call on `stream` are allocated."""
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else _nullctx()
+
+
+class _nullctx:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
 
 
 def _taps(taps: Optional[dict]):
@@ -233,14 +262,15 @@ def route(layer: Layer, x, logit_bias=None, taps=None, out=None, ws=None, stream
     import torch
     R = x.shape[0]
     k = layer.desc.top_k
-    if out is None:
-        ids = torch.empty((R, k), dtype=torch.int32, device=x.device)
-        p = torch.empty((R, k), dtype=torch.float32, device=x.device)
-        sg = torch.empty((R,), dtype=torch.float32, device=x.device)
-    else:
-        ids, p, sg = out
+    with _on(stream):
+        if out is None:
+            ids = torch.empty((R, k), dtype=torch.int32, device=x.device)
+            p = torch.empty((R, k), dtype=torch.float32, device=x.device)
+            sg = torch.empty((R,), dtype=torch.float32, device=x.device)
+        else:
+            ids, p, sg = out
     if ws is None:
-        ws = new_workspace(layer, R, R > 16, x.device)
+        ws = new_workspace(layer, R, R > 16, x.device, stream)
     _check(lib().moe_route(C.byref(layer.c), _ptr(x), R, _ptr(logit_bias), _ptr(ids), _ptr(p),
                            _ptr(sg), _ptr(ws), ws.numel() * ws.element_size(), _taps(taps),
                            _stream_ptr(stream)), "moe_route")
@@ -252,10 +282,11 @@ def experts(layer: Layer, x, ids, p, sg, grouped: bool, ws=None, taps=None, y=No
     """moe_experts_decode (grouped=False) or moe_experts_grouped: returns y fp32 [R,H]."""
     import torch
     R = x.shape[0]
-    if y is None:
-        y = torch.empty((R, layer.desc.hidden), dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((R, layer.desc.hidden), dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = new_workspace(layer, R, grouped, x.device)
+        ws = new_workspace(layer, R, grouped, x.device, stream)
     fn = lib().moe_experts_grouped if grouped else lib().moe_experts_decode
     _check(fn(C.byref(layer.c), _ptr(x), R, _ptr(ids), _ptr(p), _ptr(sg), _ptr(y), _ptr(ws),
               ws.numel() * ws.element_size(), _taps(taps), _stream_ptr(stream)),
@@ -269,16 +300,17 @@ def forward_windows(layer: Layer, x, logit_bias=None, ws=None, out=None, y=None,
     import torch
     R = x.shape[0]
     k = layer.desc.top_k
-    if out is None:
-        ids = torch.empty((R, k), dtype=torch.int32, device=x.device)
-        p = torch.empty((R, k), dtype=torch.float32, device=x.device)
-        sg = torch.empty((R,), dtype=torch.float32, device=x.device)
-    else:
-        ids, p, sg = out
-    if y is None:
-        y = torch.empty((R, layer.desc.hidden), dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if out is None:
+            ids = torch.empty((R, k), dtype=torch.int32, device=x.device)
+            p = torch.empty((R, k), dtype=torch.float32, device=x.device)
+            sg = torch.empty((R,), dtype=torch.float32, device=x.device)
+        else:
+            ids, p, sg = out
+        if y is None:
+            y = torch.empty((R, layer.desc.hidden), dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = new_workspace(layer, min(R, 16), False, x.device)
+        ws = new_workspace(layer, min(R, 16), False, x.device, stream)
     _check(lib().moe_forward_windows(C.byref(layer.c), _ptr(x), R, _ptr(logit_bias), _ptr(ids), _ptr(p),
                                      _ptr(sg), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream_ptr(stream)), "moe_forward_windows")

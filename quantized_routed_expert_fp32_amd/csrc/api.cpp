@@ -132,9 +132,12 @@ int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t*
 
 static constexpr int kWindowRows = 16;   // decode rows per window of moe_forward_windows
 
-int moe_route(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
-              int32_t* ids, float* p, float* shared_gate, void* ws, uint64_t ws_bytes,
-              const moe_taps* taps, void* stream) {
+// moe_route; sticky = 0 keeps an earlier failure recorded in the workspace
+// from marking this call's rows (the static-scratch entry point, whose
+// callers cannot clear the count).
+static int route_impl(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+                      int32_t* ids, float* p, float* shared_gate, void* ws, uint64_t ws_bytes,
+                      const moe_taps* taps, void* stream, int sticky) {
   int st = check_layer(layer);
   if (st) return st;
   if (!x || !ids || !p || !shared_gate || !ws) {
@@ -168,14 +171,22 @@ int moe_route(const moe_layer* layer, const void* x, int rows, const float* logi
   a.R = rows;
   a.logits = taps ? taps->logits : nullptr;
   a.wait_limit = (taps && taps->route_wait_limit < 0) ? 0 : (1 << 22);
+  a.sticky = sticky;
   const RouteWs rw = route_ws_layout(&layer->d, rows);
   uint8_t* wb = static_cast<uint8_t*>(ws);
   a.lg_ws = reinterpret_cast<float*>(wb + rw.lg_off);
   a.gl_ws = reinterpret_cast<float*>(wb + rw.gl_off);
   a.cand = reinterpret_cast<uint64_t*>(wb + rw.cand_off);
+  a.sync = reinterpret_cast<uint32_t*>(wb + rw.sync_off);
   hipError_t e = launch_route(fr.kid, fg.kid, a, static_cast<hipStream_t>(stream), taps_events(taps));
   if (e != hipSuccess) return hip_fail("moe_route: launch", e);
   return MOE_OK;
+}
+
+int moe_route(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+              int32_t* ids, float* p, float* shared_gate, void* ws, uint64_t ws_bytes,
+              const moe_taps* taps, void* stream) {
+  return route_impl(layer, x, rows, logit_bias, ids, p, shared_gate, ws, ws_bytes, taps, stream, 1);
 }
 
 static int experts_common(const char* name, const moe_layer* layer, const void* x, int rows,
@@ -236,9 +247,11 @@ int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const in
   return MOE_OK;
 }
 
-int moe_forward_windows(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
-                        int32_t* ids, float* p, float* shared_gate, float* y, void* ws, uint64_t ws_bytes,
-                        void* stream) {
+}  // extern "C"
+
+int moe::forward_windows_impl(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+                              int32_t* ids, float* p, float* shared_gate, float* y, void* ws,
+                              uint64_t ws_bytes, void* stream, int sticky) {
   int st = check_layer(layer);
   if (st) return st;
   if (!x || !ids || !p || !shared_gate || !y || !ws) {
@@ -263,12 +276,20 @@ int moe_forward_windows(const moe_layer* layer, const void* x, int rows, const f
     int32_t* iw = ids + (uint64_t)r0 * k;
     float* pw = p + (uint64_t)r0 * k;
     float* sw = shared_gate + r0;
-    st = moe_route(layer, xw, n, logit_bias, iw, pw, sw, ws, ws_bytes, nullptr, stream);
+    st = route_impl(layer, xw, n, logit_bias, iw, pw, sw, ws, ws_bytes, nullptr, stream, sticky);
     if (st) return st;
     st = moe_experts_decode(layer, xw, n, iw, pw, sw, y + (uint64_t)r0 * H, ws, ws_bytes, nullptr, stream);
     if (st) return st;
   }
   return MOE_OK;
+}
+
+extern "C" {
+
+int moe_forward_windows(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+                        int32_t* ids, float* p, float* shared_gate, float* y, void* ws, uint64_t ws_bytes,
+                        void* stream) {
+  return forward_windows_impl(layer, x, rows, logit_bias, ids, p, shared_gate, y, ws, ws_bytes, stream, 1);
 }
 
 int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const int32_t* ids,
@@ -324,6 +345,30 @@ int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const i
   a.tap_e = taps ? taps->e : nullptr;
   hipError_t e = launch_grouped(fe.kid, fs.kid, a, static_cast<hipStream_t>(stream), taps_events(taps));
   if (e != hipSuccess) return hip_fail("moe_experts_grouped: launch", e);
+  return MOE_OK;
+}
+
+int moe_route_failures(void* ws, uint64_t ws_bytes, int clear, uint32_t* count, void* stream) {
+  if (!ws || !count) { set_error("moe_route_failures: NULL ws/count"); return MOE_EINVAL; }
+  moe_layer_desc d{};
+  d.n_experts = 64;
+  const RouteWs rw = route_ws_layout(&d, 1);
+  if (ws_bytes < rw.sync_off + 16) {
+    set_error("moe_route_failures: workspace smaller than its fixed router area");
+    return MOE_ENOSPACE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* word = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + rw.sync_off) + 2;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, word, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail("moe_route_failures: read", e);
+  if (clear && v != 0) {
+    e = hipMemsetAsync(word, 0, 4, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail("moe_route_failures: clear", e);
+  }
+  *count = v;
   return MOE_OK;
 }
 

@@ -502,6 +502,10 @@ __global__ __launch_bounds__(256) void k_grp_combine(GroupedArgs a) {
   const float* e = a.e_ws + (uint64_t)r * (k + 1) * H + n;
   float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
+    // a slot whose id is outside [0, E) has no expert output (the sort
+    // skipped it): it adds nothing, as in the decode form
+    const int id = a.ids[r * k + j];
+    if (id < 0 || id >= a.E) continue;
     const float pj = a.p[r * k + j];
     const float4 v = *reinterpret_cast<const float4*>(e + (uint64_t)j * H);
     y.x = fmaf(pj, v.x, y.x);

@@ -39,10 +39,10 @@ std::string fmt_name(const moe_qformat& f);
 uint64_t align256(uint64_t x);
 
 // Route scratch at the start of every workspace: the decode router's
-// hand-off words (a fixed area, zero between calls), gate-row logits, then
-// [rows, E] fp32 logits.
+// hand-off words and their call-counter words (a fixed area, kept consistent
+// by every call), gate-row logits, then [rows, E] fp32 logits.
 struct RouteWs {
-  uint64_t cand_off, gl_off, lg_off, total;
+  uint64_t cand_off, sync_off, gl_off, lg_off, total;
 };
 RouteWs route_ws_layout(const moe_layer_desc* d, int rows);
 uint64_t route_ws_bytes(const moe_layer_desc* d, int rows);
@@ -64,5 +64,12 @@ struct GroupedWs {
   int max_tiles;
 };
 GroupedWs grouped_ws_layout(const moe_layer_desc* d, int rows);
+
+// moe_forward_windows with the router's sticky-failure rule switchable
+// (sticky = 0: a failure recorded in the workspace by an earlier call does
+// not mark this call's rows).
+int forward_windows_impl(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+                         int32_t* ids, float* p, float* shared_gate, float* y, void* ws,
+                         uint64_t ws_bytes, void* stream, int sticky);
 
 }  // namespace moe

@@ -17,8 +17,10 @@ struct RouteArgs {
   float* logits;   // tap [R, E+1] or null
   float* lg_ws;    // [R, E] scratch: logits before the bias
   float* gl_ws;    // [R] scratch: gate-row logits
-  uint64_t* cand;  // [R, 32] tile picks (id + 1) << 32 | value bits; zero between calls
+  uint64_t* cand;  // [R, 32] tile picks: epoch << 40 | id << 32 | value bits
+  uint32_t* sync;  // [0] epoch state, [1] completed workgroups, [2] failed rows (sticky)
   int wait_limit;  // polls of the hand-off before a row is reported as not handed off
+  int sticky;      // 1: a failure count already in sync[2] marks this call's rows failed
 };
 
 // Offsets of one expert class (routed or shared) inside the packed layer.

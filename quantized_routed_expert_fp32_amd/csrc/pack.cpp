@@ -417,10 +417,11 @@ int pack_layer_host(const moe_layer_desc* d, const moe_layer_src* src, void* hos
 RouteWs route_ws_layout(const moe_layer_desc* d, int rows) {
   RouteWs w;
   uint64_t o = 0;
-  // the decode router's hand-off words: one fixed area for its most rows
-  // (32 rows x 32 entries), first whatever the row count of the call, so no
-  // other part of any call's workspace overlaps it and it stays zero
+  // the decode router's hand-off words (32 rows x 32 entries) and its call
+  // counter words: one fixed area at the start whatever the row count of the
+  // call, so no other part of any call's workspace overlaps it
   w.cand_off = o; o = align256(o + 32 * 32 * 8);
+  w.sync_off = o; o = align256(o + 16);
   w.gl_off = o; o = align256(o + (uint64_t)rows * 4);
   w.lg_off = o; o = align256(o + (uint64_t)rows * d->n_experts * 4);
   w.total = o;

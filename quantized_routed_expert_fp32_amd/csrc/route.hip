@@ -186,15 +186,38 @@ __device__ __forceinline__ void pick_and_store(const RouteArgs& a, int row, cons
 // Decode batches: one workgroup per (tile of 64 experts, row) forms the
 // tile's logits and picks the tile's own k best (the k best of a row are
 // among the union of its tiles' k best under the same order). Tiles 1.. send
-// their k entries, each one 64-bit word (id + 1) << 32 | value bits, with
-// write-through stores; tile 0's workgroup polls those words (loads that
-// bypass its XCD's L2) until none is zero, clears them for the next call and
-// picks from its own entries and theirs. Every workgroup of the launch is
-// resident at once (E/64 * rows <= 128 workgroups), so the wait ends; it is
-// bounded all the same, and a row whose entries do not arrive within the
-// bound gets ids -1 and NaN weights and gate. One wave past the slice waves
-// forms the gate-row
-// logit in tile 0, beside the slices.
+// their k entries to tile 0's workgroup of the row, each entry one 64-bit
+// word (epoch << 40 | id << 32 | value bits) written through to memory;
+// tile 0 polls those words (loads that bypass its XCD's L2) until each
+// carries this call's epoch, then picks from its own entries and theirs.
+// The epoch is a call counter kept in the workspace: every workgroup reads
+// it at its start, and the last workgroup of the launch to finish (an
+// integer completion counter) advances it, so a word left by an earlier
+// call (or replay of a captured call) is never taken for this call's, and
+// the words need no clearing between calls. Every workgroup of the launch
+// is resident at once (E/64 * rows <= 128 workgroups), so the wait ends; it
+// is bounded all the same: a row whose entries do not arrive within the
+// bound gets ids -1 and NaN weights and gate, and the failure is counted in
+// a sticky word of the workspace (moe_route_failures), which also makes
+// every later call on that workspace report its rows the same way until the
+// count is cleared. One wave past the slice waves forms the gate-row logit
+// in tile 0, beside the slices.
+constexpr uint32_t EPOCH_MOD = 0xFFFFFFu;   // epochs 1 .. 2^24 - 1 (0 never matches)
+
+// Completion of one workgroup of k_route (wave 0, one lane): the last one
+// of the launch resets the counter and advances the epoch state.
+__device__ __forceinline__ void route_done(const RouteArgs& a, uint32_t state) {
+  const uint32_t total = gridDim.x * gridDim.y;
+  // every workgroup read the epoch state before it got here (its hand-off
+  // words or its wait used the value), so the last one may advance it; the
+  // next launch sees the new state after this kernel ends
+  const uint32_t old = __hip_atomic_fetch_add(&a.sync[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old == total - 1) {
+    __hip_atomic_store(&a.sync[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.sync[0], (state + 1) % EPOCH_MOD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <int FR, int FG, int ACT16>
 __global__ __launch_bounds__(576) void k_route(RouteArgs a, const uint16_t* __restrict__ x) {
   __shared__ float red[8][64];
@@ -208,6 +231,8 @@ __global__ __launch_bounds__(576) void k_route(RouteArgs a, const uint16_t* __re
   const uint16_t* xr = x + (uint64_t)row * H;
   const uint8_t* rc = a.base + a.r_off;
   const uint8_t* rs = a.base + a.r_soff;
+  // this call's epoch state (set by the previous launch's last workgroup)
+  const uint32_t state = w == 0 ? __hip_atomic_load(&a.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
   float out = 0.f;
   for (int sl = w; w < nw && sl < nsl; sl += nw) {
     uint2 xv[1];
@@ -243,42 +268,58 @@ __global__ __launch_bounds__(576) void k_route(RouteArgs a, const uint16_t* __re
   int slot, id;
   float val;
   wave_topk_ids<1>(k1, v1, i1, lane, k, scr, slot, id, val);   // lane j < k: the tile's j-th pick by id
+  const uint32_t ep = state % EPOCH_MOD + 1;
   if (t != 0) {
     if (lane < k)
-      __hip_atomic_store(&cand[8 * t + lane], ((uint64_t)(uint32_t)(id + 1) << 32) | __float_as_uint(val),
+      __hip_atomic_store(&cand[8 * t + lane],
+                         ((uint64_t)((ep << 8) | (uint32_t)id) << 32) | __float_as_uint(val),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) route_done(a, state);
     return;
   }
   // tile 0: lane j < k holds its own entry j; lane j in [k, ntile * k) waits
-  // for entry j % k of tile j / k
+  // for entry j % k of tile j / k (a word of this call's epoch)
   const int nc = ntile * k;
   const bool remote = lane >= k && lane < nc;
   uint64_t* src = &cand[8 * (lane / k) + lane % k];
   uint64_t word = 0;
-  for (int spin = 0; spin < a.wait_limit; ++spin) {
-    if (remote) word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__ballot(remote && word == 0) == 0) break;
+  bool have = !remote;
+  // a failure recorded earlier on this workspace keeps every later call's
+  // rows marked as failed until the caller clears it
+  const bool sticky =
+      a.sticky && __hip_atomic_load(&a.sync[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+  for (int spin = 0; spin < a.wait_limit && !sticky; ++spin) {
+    if (!have) {
+      word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      have = (uint32_t)(word >> 40) == ep;
+    }
+    if (__ballot(!have) == 0) break;
     __builtin_amdgcn_s_sleep(1);
   }
-  if (remote) __hip_atomic_store(src, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // empty for the next call
-  if (__ballot(remote && word == 0) != 0) {
-    // the wait bound ran out (the tile workgroups were not all resident):
-    // the row is marked invalid rather than picked from missing entries
+  if (sticky || __ballot(!have) != 0) {
+    // the wait bound ran out (the tile workgroups were not all resident) or
+    // an earlier call failed: the row is marked invalid rather than picked
+    // from missing entries
     if (lane < k) {
       a.ids[(uint64_t)row * k + lane] = -1;
       a.p[(uint64_t)row * k + lane] = __uint_as_float(0x7FC00000u);
     }
-    if (lane == 0) a.sg[row] = __uint_as_float(0x7FC00000u);
+    if (lane == 0) {
+      a.sg[row] = __uint_as_float(0x7FC00000u);
+      __hip_atomic_fetch_add(&a.sync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      route_done(a, state);
+    }
     return;
   }
   const float cv = remote ? __uint_as_float((uint32_t)word) : val;
-  const int ci = remote ? (int)(word >> 32) - 1 : id;
+  const int ci = remote ? (int)((word >> 32) & 0xFFu) : id;
   const float c = s_gate;
   if (a.logits && lane == 0) a.logits[(uint64_t)row * (E + 1) + E] = c;
   const float vv[1] = {cv};
   const uint32_t kk[1] = {(lane < k || remote) ? pick_key(cv) : 0u};
   const int ii[1] = {ci};
   pick_and_store_n<1>(a, row, kk, vv, ii, c, lane, scr);
+  if (lane == 0) route_done(a, state);
 }
 
 // Prompt chunks: logits of 32 rows x 64 experts per workgroup on 16-bit

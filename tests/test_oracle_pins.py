@@ -146,6 +146,8 @@ def test_hand_routing_example():
     assert list(rt.ids[0]) == [int(v) for v in c["ids"]]
     assert np.allclose(rt.p[0], [float(v) for v in c["p"]], rtol=0, atol=5e-9)
     assert rt.sigma[0] == float(c["sigma"][0])
+    # the near-tie measure: the k-th minus the (k+1)-th sorted logit
+    assert rt.gap[0] == float(c["gap"][0])
 
 
 def _cmp_key(v, e):
@@ -412,3 +414,65 @@ def test_logit_bias_is_added():
     rt = O.route(x, np.eye(E), np.zeros(E), k, bias)
     assert list(rt.ids[0]) == [5, 2]
     assert np.allclose(rt.p[0], [1 / (1 + math.exp(-7)), math.exp(-7) / (1 + math.exp(-7))])
+
+
+# ------------------------------------------------------------ parity metrics
+def _metric_blocks():
+    """[name] blocks of tests/golden/error_metrics_hand.txt; matrices as rows
+    separated by '|'."""
+    out = {}
+    for name, kv in _blocks("error_metrics_hand.txt").items():
+        d = {}
+        for key, v in kv.items():
+            if "|" in v:
+                rows, cur = [], []
+                for t in v:
+                    if t == "|":
+                        rows.append(cur)
+                        cur = []
+                    else:
+                        cur.append(float(t))
+                rows.append(cur)
+                d[key] = np.array(rows)
+            else:
+                d[key] = np.array([float(t) for t in v])
+        out[name] = d
+    return out
+
+
+def test_row_error_hand_worked():
+    """Each row is normalised by its own max|ref| (not the batch's)."""
+    c = _metric_blocks()["row_error"]
+    err = O.row_error(c["got"], c["ref"])
+    assert np.array_equal(err, c["err"])
+
+
+def test_class_errors_hand_worked():
+    """Worst column (per-column normalisation) and the Frobenius aggregate,
+    rows with a non-finite reference left out."""
+    c = _metric_blocks()["class_errors"]
+    rep = O.class_errors(c["got"], c["ref"])
+    assert rep["worst_col"] == float(c["worst_col"][0])
+    assert abs(rep["aggregate"] - float(c["aggregate"][0])) <= 1e-9
+    assert rep["max_abs"] == float(c["max_abs"][0])
+
+
+def test_dense_row_is_bf16():
+    """A DENSE row holds bf16 bit patterns (hand-worked values)."""
+    c = {}
+    for line in open(os.path.join(GOLDEN, "dense_row_hand.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, *v = line.split()
+            c[k] = v
+    bits = np.array([[int(b, 16) for b in c["bits"]]], np.uint16)
+    W = O.dequant(synth.gen.DENSE_BF16, bits, None, None, bits.shape[1])
+    assert list(W[0]) == [float(v) for v in c["values"]]
+
+
+def test_gap_is_kth_minus_next():
+    """gap = (k-th) - (k+1)-th sorted logit, for several k on one row."""
+    lg = np.array([[5.0, -1.0, 3.0, 3.0, 0.5, 2.0]])
+    for k, want in ((1, 2.0), (2, 0.0), (3, 1.0), (4, 1.5), (5, 1.5)):
+        rt = O.route(lg, np.eye(6), np.zeros(6), k)
+        assert rt.gap[0] == want, (k, rt.gap[0])
