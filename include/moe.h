@@ -17,8 +17,10 @@
  * Conventions for every call:
  *   - Pointers named dev_* or documented as device memory must point to
  *     device memory of the current HIP device; host_* pointers to host memory.
- *   - All device memory is owned by the caller. The library allocates no
- *     device memory and keeps no global state; calls are reentrant.
+ *   - All device memory is owned by the caller. The library makes no device
+ *     allocation and keeps no global state, except the fixed device array
+ *     of moe_forward_windows_noalloc (part of the loaded code object) and
+ *     its per-device address; the other calls are reentrant.
  *   - Arguments are validated before anything is enqueued; on an error code
  *     nothing has been enqueued. moe_last_error() (thread-local) then names
  *     the argument, tensor class or format that was refused.
@@ -270,6 +272,26 @@ int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const in
 int moe_forward_windows(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
                         int32_t* ids, float* p, float* shared_gate, float* y, void* ws,
                         uint64_t ws_bytes, void* stream);
+
+/* moe_forward_windows without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation). The workspace is a fixed device array
+ * inside the library, 512 KiB, one copy per GPU, held until the process
+ * ends; its address on each device is resolved once, on the first call with
+ * that device current. The call allocates nothing.
+ *   layer, x, rows, logit_bias, ids, p, shared_gate, y: as moe_forward_windows.
+ * Limit: layers whose 16-row decode workspace (moe_workspace_size with
+ * rows = min(rows, 16), grouped = 0) exceeds 512 KiB are refused with
+ * MOE_ENOSPACE before anything is enqueued (the qwen3_5-MoE 35B-A3B shapes
+ * need 329,216 bytes).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (two streams, two threads) race and must be serialised by the caller.
+ * A router failure (see moe_route) marks only the failing call's rows; it is
+ * not carried into later calls.
+ * Errors: as moe_forward_windows, plus MOE_ENOSPACE as above and MOE_EHIP if
+ * the array's device address cannot be resolved. */
+int moe_forward_windows_noalloc(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
+                                int32_t* ids, float* p, float* shared_gate, float* y, void* stream);
 
 /* The same layer for prompt chunks (the prefill form): rows are sorted by
  * expert (histogram, prefix scan, stable scatter), then grouped GEMMs on

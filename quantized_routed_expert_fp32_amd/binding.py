@@ -65,8 +65,8 @@ class TapsC(C.Structure):
 
 EXPORTS = ["moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
            "moe_workspace_size", "moe_route", "moe_experts_decode", "moe_experts_grouped",
-           "moe_forward_windows", "moe_route_failures", "moe_status_string", "moe_last_error",
-           "moe_version"]
+           "moe_forward_windows", "moe_forward_windows_noalloc", "moe_route_failures",
+           "moe_status_string", "moe_last_error", "moe_version"]
 
 _lib = None
 
@@ -95,9 +95,10 @@ def lib() -> C.CDLL:
     L.moe_experts_grouped.argtypes = L.moe_experts_decode.argtypes
     L.moe_forward_windows.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, vp, u64, vp]
     L.moe_route_failures.argtypes = [vp, u64, i32, C.POINTER(C.c_uint32), vp]
+    L.moe_forward_windows_noalloc.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, vp]
     for f in ("moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
               "moe_workspace_size", "moe_route", "moe_experts_decode", "moe_experts_grouped",
-              "moe_forward_windows", "moe_route_failures"):
+              "moe_forward_windows", "moe_forward_windows_noalloc", "moe_route_failures"):
         getattr(L, f).restype = C.c_int
     L.moe_status_string.argtypes = [C.c_int]
     L.moe_status_string.restype = C.c_char_p
@@ -314,6 +315,28 @@ def forward_windows(layer: Layer, x, logit_bias=None, ws=None, out=None, y=None,
     _check(lib().moe_forward_windows(C.byref(layer.c), _ptr(x), R, _ptr(logit_bias), _ptr(ids), _ptr(p),
                                      _ptr(sg), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream_ptr(stream)), "moe_forward_windows")
+    return ids, p, sg, y
+
+
+def forward_windows_noalloc(layer: Layer, x, logit_bias=None, out=None, y=None, stream=None):
+    """moe_forward_windows_noalloc: as forward_windows, with the library's
+    fixed device array as the workspace (the call allocates no device
+    memory); returns (ids, p, shared_gate, y)."""
+    import torch
+    R = x.shape[0]
+    k = layer.desc.top_k
+    with _on(stream):
+        if out is None:
+            ids = torch.empty((R, k), dtype=torch.int32, device=x.device)
+            p = torch.empty((R, k), dtype=torch.float32, device=x.device)
+            sg = torch.empty((R,), dtype=torch.float32, device=x.device)
+        else:
+            ids, p, sg = out
+        if y is None:
+            y = torch.empty((R, layer.desc.hidden), dtype=torch.float32, device=x.device)
+    _check(lib().moe_forward_windows_noalloc(C.byref(layer.c), _ptr(x), R, _ptr(logit_bias), _ptr(ids),
+                                             _ptr(p), _ptr(sg), _ptr(y), _stream_ptr(stream)),
+           "moe_forward_windows_noalloc")
     return ids, p, sg, y
 
 

@@ -14,7 +14,7 @@ OUT = os.path.join(PKG, "libmoe.so")
 BUILD = os.path.join(PKG, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["route.hip", "decode.hip", "grouped.hip"]
+HIP_SOURCES = ["route.hip", "decode.hip", "grouped.hip", "noalloc.hip"]
 CXX_SOURCES = ["pack.cpp", "api.cpp"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
                "-munsafe-fp-atomics", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
