@@ -338,7 +338,7 @@ int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const i
   a.e_ws = reinterpret_cast<float*>(w + wl.e_off);
   a.tiles = reinterpret_cast<int32_t*>(w + wl.tiles_off);
   a.max_tiles = wl.max_tiles;
-  a.gemm_nblk = 1;
+  a.x16 = a.act_fp16 ? a.x : reinterpret_cast<const uint16_t*>(w + wl.x16_off);
   a.y = y;
   a.tap_gu = taps ? taps->gu : nullptr;
   a.tap_h = taps ? taps->h : nullptr;

@@ -1,41 +1,49 @@
 // Grouped (prompt-chunk) path: the prefill form for chunks of many rows.
 //
-//  1. k_grp_sort (one workgroup): expert histogram of the picks, exclusive
-//     prefix scan, scatter of the slots (row r, pick j) into
-//     expert-major order; the shared expert follows as expert E with every
-//     row. Then the tile lists: experts with many rows get 128-row M-tiles,
-//     the rest 32-row M-tiles (the Zipf-skewed chunk has one hot expert
-//     with most rows and a long tail of small ones).
-//  2. k_grp_gemm<GU>: per (M-tile, 256-column block) a workgroup of 4 waves;
-//     wave w owns one 64-row layout tile of the gate/up matrix (32 gate rows
-//     + the 32 up rows of the same intermediate indices), so gate and up of
-//     an output land in the same lane and SwiGLU runs in registers. A (the
-//     activations of the tile's slots, gathered by the sort's permutation)
-//     is staged through LDS as fp16; B (the packed codes) goes from memory
-//     straight to registers and is dequantised there to fp16
-//     (affine: s*q + b; symmetric: s*(u - 8)); v_mfma_f32_32x32x16_f16
-//     accumulates in fp32. Output h in fp16, expert-major. The 128-row and
-//     32-row tile lists share one launch, so the few large tiles (the shared
-//     expert, hot experts) run beside the many small ones.
+//  1. k_grp_sort: one workgroup sorts the slots (row r, pick j) by expert:
+//     per-wave expert histograms, an exclusive scan, and a scatter into
+//     expert-major order (the shared expert follows as expert E with every
+//     row). Lanes of a wave that hold the same expert are grouped by ballots,
+//     so one LDS atomic serves the group (the hot experts of a skewed chunk
+//     would otherwise serialise the wave). Then the work list: each expert's
+//     run is cut into M-tiles of 128 rows, the last one 32, 64, 96 or 128
+//     rows tall; the list holds every 128-row tile first, then the 96-, 64-
+//     and 32-row ones, so the longest work starts first and the short tiles
+//     fill the end. Extra workgroups of the same launch convert bf16
+//     activations to fp16 for the GEMMs.
+//  2. k_grp_gemm<GU>: a persistent grid (two workgroups per CU) takes
+//     (M-tile, 256-column block) items from a device queue. Wave w owns one
+//     64-row layout tile of the gate/up matrix (32 gate rows and the 32 up
+//     rows of the same intermediate indices), so gate and up of an output
+//     land in the same lane and SwiGLU runs in registers. Both operands go
+//     from memory straight into a three-stage LDS ring (global_load_lds, one
+//     64-k step ahead): A, the tile's activation rows gathered by the sort's
+//     permutation (XOR-swizzled 16-byte segments), and per wave B, the packed
+//     codes and scale words of its layout tile. B is dequantised to fp16
+//     right before use (affine: s*q + b; symmetric: s*(u - 8));
+//     v_mfma_f32_32x32x16_f16 accumulates in fp32. Output h in fp16,
+//     expert-major.
 //  3. k_grp_gemm<DN>: the same on h and the down matrices; output e in fp32
-//     in slot order.
+//     per slot.
 //  4. k_grp_combine: y = sum_j p_j e_j + sigma e_shared, slots in pick order.
-// ("Sage-A1.5 ... #1329", Proposal: grouped MoE and XMX prompt chunks;
-//  Limits to agree on: the grouped form has a different sum order than the
-//  per-row form, so it is judged by tolerance, not bits.)
+// ("Sage-A1.5 ... #1329", Proposal: grouped MoE and prompt chunks on the
+//  matrix engines; Limits to agree on: the grouped form adds in another
+//  order than the per-row form, so it is judged by tolerance, not bits.)
 #include "moe_kernels.h"
 #include "moe_launch.h"
 #include "moe_dispatch.h"
+
+#include <algorithm>
 
 namespace moe {
 
 typedef f16 half8v_t __attribute__((ext_vector_type(8)));
 typedef float f16v_t __attribute__((ext_vector_type(16)));
 
-constexpr int BIG_MIN_ROWS = 96;   // experts with at least this many rows take 128-row tiles
-
-// meta layout (int32): [0] n_big, [1] n_small, [2 .. E+3) offsets (E+2 entries)
+// meta layout (int32): [0] M-tiles in the work list, [1] gate/up queue
+// counter, [2] down queue counter, [8 .. E+10) expert offsets (E+2 entries)
 constexpr int META_OFF = 8;
+constexpr int GEMM_WG_PER_CU = 2;
 
 // ------------------------------------------------------------------ sort
 // Exclusive prefix sum of n <= 320 LDS counters by one wave (lane l owns
@@ -64,33 +72,65 @@ __device__ __forceinline__ int wave_exclusive_scan(const int* in, int* out, int 
   return __shfl(inc, 63);
 }
 
-// One workgroup of 1024 threads (16 waves). Wave w owns the contiguous slot
-// range [w S, (w+1) S), S = ceil(R k / 16), read 1024 slots at a time:
-//  1. per-wave expert histograms (LDS atomics on the wave's own row);
+// The lanes of the wave whose expert id equals this lane's (ids < 512; only
+// valid lanes are counted; an invalid lane gets 0): one ballot per id bit.
+__device__ __forceinline__ uint64_t same_id_lanes(int e, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(valid && bit);
+    m &= bit ? bb : ~bb;
+  }
+  return valid ? m : 0ull;
+}
+
+// Workgroup 0: the sort and the work list (1024 threads, 16 waves; wave w
+// owns the contiguous slot range [w S, (w+1) S), S = ceil(R k / 16)):
+//  1. per-wave expert histograms (one LDS atomic per group of lanes with the
+//     same expert);
 //  2. exclusive scan over the experts (shared expert E with every row), then
 //     each wave's base per expert: the offset plus the earlier waves' counts;
-//  3. the same walk again scatters each slot (row r, pick j) to the position
-//     its atomic increment of the wave's counter returns. Rows of one expert
-//     stay within the wave's range in slot order only up to the order the
-//     hardware serves one instruction's lanes; a row's output does not depend
-//     on its position in a tile, so results are the same either way;
-//  4. the tile lists: experts with many rows get 128-row M-tiles, the rest
-//     32-row M-tiles (the Zipf-skewed chunk has one hot expert with most rows
-//     and a long tail of small ones), each list laid out by a scan over the
-//     experts' tile counts.
+//  3. the same walk again scatters each slot to its position (the group's
+//     base plus the lane's rank in it), so positions are deterministic;
+//  4. the work list of M-tiles (expert, first position, rows), 128-row tiles
+//     first, then 96-, 64- and 32-row ones, each class laid out by a scan
+//     over the experts; the queue counters of the two GEMMs are reset.
+// Workgroups 1.. (bf16 activations only): x -> fp16 copy for the gate/up GEMM.
 __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
   __shared__ int cnt[320];
   __shared__ int off[320];
-  __shared__ int tb[320], ts[320];       // tiles per expert (big / small lists), then their offsets
+  __shared__ int nt[4][320];             // M-tiles per expert in each height class, then their offsets
   __shared__ int wh[16][258];            // per-wave counts, then per-wave running positions
-  __shared__ int s_tot[2];
+  __shared__ int s_tot[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (blockIdx.x > 0) {
+    // bf16 -> fp16 (exact for |x| >= 2^-17 and below 65504), 8 values a thread
+    const uint64_t n8 = (uint64_t)a.R * a.H / 8;
+    const uint4* src = reinterpret_cast<const uint4*>(a.x);
+    uint4* dst = reinterpret_cast<uint4*>(const_cast<uint16_t*>(a.x16));
+    for (uint64_t i = (uint64_t)(blockIdx.x - 1) * 1024 + tid; i < n8; i += (uint64_t)(gridDim.x - 1) * 1024) {
+      const uint4 v = src[i];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        half2v h;
+        h.x = (f16)bf16_to_f(u[q] & 0xFFFFu);
+        h.y = (f16)bf16_to_f(u[q] >> 16);
+        o[q] = as_u(h);
+      }
+      dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    return;
+  }
   const int E = a.E, k = a.k, R = a.R, nslot = R * k;
   const int S = (nslot + 15) / 16, s0 = w * S, s1 = min(nslot, s0 + S);
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   for (int q = tid; q < 16 * 258; q += 1024) (&wh[0][0])[q] = 0;
   __syncthreads();
-  // 1. histograms: the picks of 16 rounds are loaded at once (one latency
-  // per 1024 slots of a wave)
+  // 1. histograms (the ids of 16 rounds are loaded at once: one memory
+  // latency per 1024 slots of a wave)
   for (int bb = s0; bb < s1; bb += 1024) {
     int ev[16];
 #pragma unroll
@@ -101,7 +141,9 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int e = ev[q];
-      if (e >= 0 && e < E) atomicAdd(&wh[w][e], 1);
+      const bool valid = e >= 0 && e < E;
+      const uint64_t same = same_id_lanes(e, valid);
+      if (valid && (same & lt) == 0) atomicAdd(&wh[w][e], __popcll(same));
     }
   }
   __syncthreads();
@@ -130,9 +172,11 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
   for (int e = tid; e <= E + 1; e += 1024) a.meta[META_OFF + e] = off[e];
   for (int e = tid; e <= E; e += 1024) {
     const int c = cnt[e];
-    const bool big = c >= BIG_MIN_ROWS;
-    tb[e] = big ? (c + 127) / 128 : 0;
-    ts[e] = big ? 0 : (c + 31) / 32;
+    const int mtr = ((c & 127) + 31) >> 5;       // height of the last tile in 32-row units (0: none)
+    nt[0][e] = (c >> 7) + (mtr == 4);
+    nt[1][e] = mtr == 3;
+    nt[2][e] = mtr == 2;
+    nt[3][e] = mtr == 1;
   }
   __syncthreads();
   // 3. scatter (positions from the wave's own LDS row)
@@ -147,34 +191,43 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
     for (int q = 0; q < 16; ++q) {
       const int i = bb + 64 * q + lane;
       const int e = ev[q];
-      if (e >= 0 && e < E) a.perm[atomicAdd(&wh[w][e], 1)] = (i / k) * (k + 1) + i % k;
+      const bool valid = e >= 0 && e < E;
+      const uint64_t same = same_id_lanes(e, valid);
+      const int leader = valid ? __ffsll((unsigned long long)same) - 1 : lane;
+      int base = 0;
+      if (valid && leader == lane) base = atomicAdd(&wh[w][e], __popcll(same));
+      base = __shfl(base, leader);
+      if (valid) a.perm[base + __popcll(same & lt)] = (i / k) * (k + 1) + i % k;
     }
   }
   for (int r = tid; r < R; r += 1024) a.perm[off[E] + r] = r * (k + 1) + k;
-  // 4. tile lists: entry = (expert, first position, rows)
-  if (w == 0) {
-    const int nb = wave_exclusive_scan(tb, tb, E + 1, lane);
-    if (lane == 0) s_tot[0] = nb;
-  } else if (w == 1) {
-    const int ns = wave_exclusive_scan(ts, ts, E + 1, lane);
-    if (lane == 0) s_tot[1] = ns;
+  // 4. work list: one scan per height class (waves 0..3)
+  if (w < 4) {
+    const int tot = wave_exclusive_scan(nt[w], nt[w], E + 1, lane);
+    if (lane == 0) s_tot[w] = tot;
   }
   __syncthreads();
+  const int b1 = s_tot[0], b2 = b1 + s_tot[1], b3 = b2 + s_tot[2];
   for (int e = tid; e <= E; e += 1024) {
     const int c = cnt[e];
-    if (c == 0) continue;
-    const bool big = c >= BIG_MIN_ROWS;
-    const int bm = big ? 128 : 32;
-    int* t = big ? a.tiles + 3 * tb[e] : a.tiles + 3 * (a.max_tiles + ts[e]);
-    for (int m0 = 0; m0 < c; m0 += bm, t += 3) {
+    const int full = c >> 7, rem = c & 127, mtr = (rem + 31) >> 5;
+    int* t = a.tiles + 3 * nt[0][e];
+    for (int m = 0; m < full; ++m, t += 3) {
       t[0] = e;
-      t[1] = off[e] + m0;
-      t[2] = min(bm, c - m0);
+      t[1] = off[e] + 128 * m;
+      t[2] = 128;
+    }
+    if (mtr > 0) {
+      if (mtr != 4) t = a.tiles + 3 * (mtr == 3 ? b1 + nt[1][e] : mtr == 2 ? b2 + nt[2][e] : b3 + nt[3][e]);
+      t[0] = e;
+      t[1] = off[e] + 128 * full;
+      t[2] = rem;
     }
   }
   if (tid == 0) {
-    a.meta[0] = s_tot[0];
-    a.meta[1] = s_tot[1];
+    a.meta[0] = b3 + s_tot[3];
+    a.meta[1] = 0;
+    a.meta[2] = 0;
   }
 }
 
@@ -237,82 +290,199 @@ __device__ __forceinline__ void deq_chunk_half(const uint32_t* cw, int wsel, hal
 
 enum { GU = 0, DN = 1 };
 
-constexpr int AST = 72;    // LDS row stride of the A tile in halves (64 + 8 pad)
+// The LDS ring of the GEMMs: 3 stages, each the A tile of one 64-k step
+// (128 rows x 64 k fp16, 16 KiB) and, per wave, the B codes of its layout
+// tile for that step (two chunk blocks of 64 rows) and the rows' scale
+// words. Every load of a step goes straight from memory into its stage
+// (global_load_lds), so nothing of the pipeline sits in registers; loads run
+// one step ahead.
+constexpr int NST = 3;
+constexpr int A_STAGE = 128 * 64;        // halves of the A tile of one step
+constexpr int B_WAVE = 2 * 1024 + 256;   // bytes of one wave's B area (codes of 2 chunks, scale words)
+constexpr int STAGE_BYTES = 2 * A_STAGE + 4 * B_WAVE;
+constexpr int B_LOADS = 3;               // B loads per thread and step: 2 chunk blocks, 1 scale word
 
 // 4-bit codes: the lane of half hsel takes words 2 hsel, 2 hsel + 1 of each
 // chunk row (8 contiguous bytes), i.e. k = 16 hsel .. 16 hsel + 15 of the
 // chunk, and the A fragments follow the same k. The 3-bit rows hold a
-// chunk's codes across all 3 words, so their lanes load the full row.
+// chunk's codes across all 3 words, so their lanes take the full row.
 template <int F> struct BFrag {
   static constexpr bool HALF = F == F_Q4 || F == F_S4;
   static constexpr int W = HALF ? 2 : Fmt<F>::WORDS;   // words per chunk per lane
 };
 
-// One pipeline stage: the A segments a thread stages, the code words and
-// the scale word (per n-tile) of the wave's layout tile for one 64-k step.
-template <int F, int SPT>
-struct GrpStage {
-  uint4 av[SPT];
-  uint32_t bw[2][2][BFrag<F>::W];
+// Codes (per n-tile and chunk) and scale words (per n-tile) of the wave's
+// layout tile for one 64-k step, as the lane uses them.
+template <int F>
+struct BStage {
+  uint32_t w[2][2][BFrag<F>::W];
   uint32_t sr[2];
 };
 
-template <int F, int SPT>
-__device__ __forceinline__ void grp_issue(GrpStage<F, SPT>& st, const uint16_t* const (&arow)[SPT],
-                                          const int (&aseg)[SPT], const uint8_t* codes, const uint8_t* scales,
-                                          int T, int nch, int nkb, int col, int hsel, int kk0) {
-  constexpr int GPS = KBLK / Fmt<F>::G;
-#pragma unroll
-  for (int q = 0; q < SPT; ++q) st.av[q] = *reinterpret_cast<const uint4*>(arow[q] + kk0 + 8 * aseg[q]);
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint8_t* blk = codes + chunk_off<F>(T, kk0 / 32 + c, nch);
-      if constexpr (BFrag<F>::HALF) {
-        const uint2 v = *reinterpret_cast<const uint2*>(blk + (32 * nt + col) * Fmt<F>::CB + 8 * hsel);
-        st.bw[nt][c][0] = v.x;
-        st.bw[nt][c][1] = v.y;
-      } else {
-        load_chunk<F>(blk, 32 * nt + col, st.bw[nt][c]);
-      }
-    }
-  const int gi = (kk0 % KBLK) / Fmt<F>::G;
-  const uint8_t* sblk = scales + sblk_off<F>(T, kk0 / KBLK, nkb);
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    if constexpr (Fmt<F>::AFF) st.sr[nt] = reinterpret_cast<const uint32_t*>(sblk)[(32 * nt + col) * GPS + gi];
-    else st.sr[nt] = reinterpret_cast<const uint16_t*>(sblk)[(32 * nt + col) * GPS + gi];
-  }
+// At most N vector-memory operations of this wave still in flight (expcnt
+// and lgkmcnt not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// A segments of a stage into one LDS buffer (bf16 -> fp16 on the way: exact
-// for |x| in fp16's normal range)
-template <int MODE, int ACT16, int SPT>
-__device__ __forceinline__ void grp_store_a(const uint4 (&av)[SPT], uint16_t* buf, const int (&arr)[SPT],
-                                            const int (&aseg)[SPT]) {
+// LDS byte address of a __shared__ pointer
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// XOR swizzle of the A tile's 16-byte segments: row r's segment s sits at
+// position s ^ swz(r), so the 8 (32 banks) or 16 (64 banks) lanes served
+// together read distinct bank groups.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// The B loads of one step into the wave's area bw (exactly B_LOADS loads:
+// the wait counts rely on it): lane l copies row l of the layout tile's two
+// chunk blocks (CB bytes each) and row l's scale word: affine, the (s, b)
+// word of the step's group; symmetric, the word holding both fp16 scales of
+// the row's 256-wide block. Every load to LDS here moves whole dwords; a
+// 16- or 4-byte load puts lane l's data at l times its size, a 12-byte load
+// (3-bit rows) at 16 l, so a chunk block takes 1 KiB in LDS either way.
+template <int F>
+__device__ __forceinline__ void issue_b(uint8_t* bw, const uint8_t* blk, uint32_t codes, uint32_t scales, int T,
+                                       int nch, int nkb, int lane, int step) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int GPS = KBLK / Fmt<F>::G, CB = Fmt<F>::CB;
+  const int kk0 = 64 * step;
 #pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    uint4 v = av[q];
-    if constexpr (MODE == GU && !ACT16) {
-      uint32_t* u = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        half2v h;
-        h.x = (f16)bf16_to_f(u[i] & 0xFFFFu);
-        h.y = (f16)bf16_to_f(u[i] >> 16);
-        u[i] = as_u(h);
-      }
-    }
-    *reinterpret_cast<uint4*>(buf + arr[q] * AST + 8 * aseg[q]) = v;
+  for (int c = 0; c < 2; ++c)
+    __builtin_amdgcn_global_load_lds(blk + codes + chunk_off<F>(T, kk0 / 32 + c, nch) + lane * CB,
+                                     (__attribute__((address_space(3))) void*)(bw + 1024 * c), CB, 0, 0);
+  const uint8_t* sb = blk + scales + sblk_off<F>(T, kk0 / KBLK, nkb);
+  if constexpr (Fmt<F>::AFF) {
+    const int gi = (kk0 % KBLK) / Fmt<F>::G;
+    __builtin_amdgcn_global_load_lds(sb + (lane * GPS + gi) * 4, (__attribute__((address_space(3))) void*)(bw + 2048),
+                                     4, 0, 0);
+  } else {
+    static_assert(GPS == 2, "two fp16 scales per row and block");
+    __builtin_amdgcn_global_load_lds(sb + lane * 4, (__attribute__((address_space(3))) void*)(bw + 2048), 4, 0, 0);
   }
+#endif
+}
+
+// The A loads of one step: MT loads of 16 bytes per thread straight into
+// the stage's A tile (wave w's instruction i fills the 1 KiB at segment
+// 256 i + 64 w; lane l's segment is row q / 8, position q % 8, holding the
+// row's source segment (q % 8) ^ swz(row)).
+template <int MT>
+__device__ __forceinline__ void issue_a(const uint16_t* const* asrc, uint16_t* buf, int w, int step) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+    __builtin_amdgcn_global_load_lds(asrc[i] + 64 * step,
+                                     (__attribute__((address_space(3))) void*)(buf + (256 * i + 64 * w) * 8), 16, 0,
+                                     0);
+#endif
+}
+
+// The reads below are inline asm, each block waiting for its own results:
+// the compiler would otherwise guard every LDS read against the loads into
+// LDS still in flight (the prefetched stage included) by waiting for all of
+// them. What they read has landed: the step's wait and barrier came first.
+// Every output is early-clobber ("=&v"): a block issues several reads before
+// its one wait, so an output register shared with an address input of the
+// same block can be overwritten while the block still reads through it (a
+// W4A16 instantiation whose scale outputs took the address registers read
+// wrong scales for whole k-steps).
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v3u __attribute__((ext_vector_type(3)));
+
+// The lane's B words of one step from the wave's area at byte address bw:
+// codes of rows col and 32 + col (half hsel for 4-bit codes, the whole row
+// for 3-bit ones) of both chunks, and the two rows' scale entries (a
+// symmetric row's word holds the scales of groups 0 and 1 of its block; the
+// step's group is step % 4 / 2).
+template <int F>
+__device__ __forceinline__ void read_b(BStage<F>& st, uint32_t bw, int col, int hsel, int step) {
+  uint32_t s0, s1;
+  if constexpr (BFrag<F>::HALF) {
+    const uint32_t ac = bw + col * 16 + 8 * hsel;
+    v2u c00, c10, c01, c11;
+    if constexpr (Fmt<F>::AFF) {
+      asm volatile("ds_read_b64 %0, %6\n\tds_read_b64 %1, %6 offset:512\n\tds_read_b64 %2, %6 offset:1024\n\t"
+                   "ds_read_b64 %3, %6 offset:1536\n\tds_read_b32 %4, %7\n\tds_read_b32 %5, %7 offset:128\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(c00), "=&v"(c10), "=&v"(c01), "=&v"(c11), "=&v"(s0), "=&v"(s1)
+                   : "v"(ac), "v"(bw + 2048 + col * 4));
+    } else {
+      asm volatile("ds_read_b64 %0, %6\n\tds_read_b64 %1, %6 offset:512\n\tds_read_b64 %2, %6 offset:1024\n\t"
+                   "ds_read_b64 %3, %6 offset:1536\n\tds_read_b32 %4, %7\n\tds_read_b32 %5, %7 offset:128\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(c00), "=&v"(c10), "=&v"(c01), "=&v"(c11), "=&v"(s0), "=&v"(s1)
+                   : "v"(ac), "v"(bw + 2048 + col * 4));
+      const int sh = 16 * ((step & 3) >> 1);
+      s0 >>= sh;
+      s1 >>= sh;
+    }
+    st.w[0][0][0] = c00.x; st.w[0][0][1] = c00.y;
+    st.w[1][0][0] = c10.x; st.w[1][0][1] = c10.y;
+    st.w[0][1][0] = c01.x; st.w[0][1][1] = c01.y;
+    st.w[1][1][0] = c11.x; st.w[1][1][1] = c11.y;
+  } else {
+    // 3-bit rows: 12 bytes at a 16-byte lane stride
+    static_assert(Fmt<F>::CB == 12, "row layout");
+    const uint32_t ac = bw + col * 16;
+    v3u r0, r1, r2, r3;
+    asm volatile("ds_read_b96 %0, %6\n\tds_read_b96 %1, %6 offset:512\n\tds_read_b96 %2, %6 offset:1024\n\t"
+                 "ds_read_b96 %3, %6 offset:1536\n\tds_read_b32 %4, %7\n\tds_read_b32 %5, %7 offset:128\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(s0), "=&v"(s1)
+                 : "v"(ac), "v"(bw + 2048 + col * 4));
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      st.w[0][0][q] = r0[q];
+      st.w[1][0][q] = r1[q];
+      st.w[0][1][q] = r2[q];
+      st.w[1][1][q] = r3[q];
+    }
+  }
+  st.sr[0] = s0;
+  st.sr[1] = s1;
+}
+
+template <int F>
+__device__ __forceinline__ int a_seg(int i, int hsel) {
+  const int c = i >> 1, j = i & 1;
+  return BFrag<F>::HALF ? 4 * c + 2 * hsel + j : 4 * c + 2 * j + hsel;
+}
+
+// The MT A fragments of k-step i (rows 32 mt + col) from the A tile at
+// byte address buf.
+template <int F, int MT>
+__device__ __forceinline__ void read_a(half8v_t (&ah)[MT], uint32_t buf, int i, int col, int hsel) {
+  const uint32_t ad = buf + col * 128 + 16 * (a_seg<F>(i, hsel) ^ swz(col));
+  v4u r0, r1, r2, r3;
+  if constexpr (MT == 4)
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:4096\n\tds_read_b128 %2, %4 offset:8192\n\t"
+                 "ds_read_b128 %3, %4 offset:12288\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3) : "v"(ad));
+  else if constexpr (MT == 3)
+    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:4096\n\tds_read_b128 %2, %3 offset:8192\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r0), "=&v"(r1), "=&v"(r2) : "v"(ad));
+  else if constexpr (MT == 2)
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:4096\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r0), "=&v"(r1) : "v"(ad));
+  else
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r0) : "v"(ad));
+  ah[0] = __builtin_bit_cast(half8v_t, r0);
+  if constexpr (MT > 1) ah[1] = __builtin_bit_cast(half8v_t, r1);
+  if constexpr (MT > 2) ah[2] = __builtin_bit_cast(half8v_t, r2);
+  if constexpr (MT > 3) ah[3] = __builtin_bit_cast(half8v_t, r3);
 }
 
 // The MFMAs of one 64-k step: 4 k-steps of 16 over the step's 2 chunks; the
-// A fragments of a k-step are read from LDS ahead of the dequantisation.
-template <int F, int MT, int SPT>
-__device__ __forceinline__ void grp_mma(f16v_t (&acc)[MT][2], const GrpStage<F, SPT>& st, const uint16_t* buf,
-                                        int col, int hsel) {
+// A fragments of k-step i + 1 are read while those of k-step i are in use.
+template <int F, int MT>
+__device__ __forceinline__ void step_mma(f16v_t (&acc)[MT][2], const BStage<F>& st, uint32_t abuf, int col,
+                                         int hsel) {
   half2v s16[2], b2[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -321,108 +491,111 @@ __device__ __forceinline__ void grp_mma(f16v_t (&acc)[MT][2], const GrpStage<F, 
       sc = bf16_to_f(st.sr[nt] & 0xFFFFu);
       bi = bf16_to_f(st.sr[nt] >> 16);
     } else {
-      sc = f16_bits_to_f(st.sr[nt]);
+      sc = f16_bits_to_f(st.sr[nt] & 0xFFFFu);
       bi = 0.f;
     }
     const f16 sh = (f16)(16.0f * sc), bh = (f16)bi;
     s16[nt] = {sh, sh};
     b2[nt] = {bh, bh};
   }
+  half8v_t ah[2][MT];
+  read_a<F, MT>(ah[0], abuf, 0, col, hsel);
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int i = 0; i < 4; ++i) {
+    const int c = i >> 1, j = i & 1;
+    if (i + 1 < 4) read_a<F, MT>(ah[(i + 1) & 1], abuf, i + 1, col, hsel);
+    half8v_t bf[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // k offset of this lane's 8 values inside the 64-k step
-      const int koff = BFrag<F>::HALF ? 32 * c + 16 * hsel + 8 * j : 32 * c + 16 * j + 8 * hsel;
-      half8v_t ah[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        ah[mt] = __builtin_bit_cast(half8v_t, *reinterpret_cast<const uint4*>(buf + (32 * mt + col) * AST + koff));
-      half8v_t bf[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        uint32_t d[4];
-        if constexpr (BFrag<F>::HALF) deq_word<F>(&st.bw[nt][c][j], s16[nt], b2[nt], d);
-        else deq_chunk_half<F>(st.bw[nt][c], 2 * j + hsel, s16[nt], b2[nt], d);
-        bf[nt] = __builtin_bit_cast(half8v_t, *reinterpret_cast<uint4*>(d));
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+    for (int nt = 0; nt < 2; ++nt) {
+      uint32_t d[4];
+      if constexpr (BFrag<F>::HALF) deq_word<F>(&st.w[nt][c][j], s16[nt], b2[nt], d);
+      else deq_chunk_half<F>(st.w[nt][c], 2 * j + hsel, s16[nt], b2[nt], d);
+      bf[nt] = __builtin_bit_cast(half8v_t, *reinterpret_cast<uint4*>(d));
     }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i & 1][mt], bf[nt], acc[mt][nt], 0, 0, 0);
+  }
 }
 
-// One workgroup: (tile, column block of 4 layout tiles); wave w = layout tile.
-// BM = 32 * MT rows. K walked in steps of 64 (two code chunks) through a ring
-// of NS register stages: the loads of step t + NS - 1 are issued before the
-// MFMAs of step t. The A tile alternates between two LDS buffers, so one
-// barrier per step orders both the buffer's writes before its reads and the
-// reads of step t - 1 before the writes of step t + 1.
-template <int F, int MODE, int MT, int ACT16, int NS>
-__device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* __restrict__ x,
-                                         int e, int m0, int mc, int nb, uint16_t* lds_a, int* slot_l) {
+// One item: rows [m0, m0 + mc) of expert e's run (mc <= 32 MT), column
+// block nb (wave w: layout tile 4 nb + w). K in steps of 64: at step t the
+// A and B loads of step t + 1 go out (past the last step, the last step's
+// loads again, unused), then the wave waits until its own loads of step t
+// have landed (at most the loads of step t + 1 in flight: the count is exact
+// because every load here is one known instruction), and a bare barrier
+// makes every wave's part of the stage visible and tells that every wave has
+// finished step t - 1 (so the stage of step t - 2, which the loads of step
+// t + 1 refill, is no longer read). __syncthreads would add a release fence,
+// which waits for every load to LDS in flight, the prefetched stage
+// included.
+template <int F, int MODE, int MT>
+__device__ __forceinline__ void gemm_item(const GroupedArgs& a, int e, int m0, int mc, int nb, uint8_t* const (&stg)[NST],
+                                          int* slot_l) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = a.k, H = a.H;
   const bool shared = e == a.E;
   const ExpertClass& ec = shared ? a.sh : a.rt;
-  const int I = ec.inter;
-  const int K = MODE == GU ? H : I;          // contraction length
+  const int K = MODE == GU ? H : ec.inter;   // contraction length
   const int T = nb * 4 + w;                  // this wave's layout tile
   const uint8_t* blk = a.base + ec.base_off + (shared ? 0 : (uint64_t)e * ec.stride);
-  const uint8_t* codes = blk + (MODE == GU ? ec.gu_codes : ec.dn_codes);
-  const uint8_t* scales = blk + (MODE == GU ? ec.gu_scales : ec.dn_scales);
+  const uint32_t codes = (uint32_t)(MODE == GU ? ec.gu_codes : ec.dn_codes);
+  const uint32_t scales = (uint32_t)(MODE == GU ? ec.gu_scales : ec.dn_scales);
   const int nch = K / 32, nkb = K / KBLK;
-  constexpr int BM = 32 * MT;
-  // ---- A rows this thread stages: BM rows x 64 halves per step, as
-  // (row, 8-half segment) pairs
-  constexpr int SEGS = BM * 8;               // 8 halves per segment
-  constexpr int SPT = SEGS / 256;            // segments per thread
-  const uint16_t* arow[SPT];
-  int aseg[SPT], arr[SPT];
+  const int col = lane & 31, hsel = lane >> 5;
+  // A rows staged by this thread (rows past mc repeat the last row; their
+  // results are not stored)
+  const uint16_t* asrc[MT];
 #pragma unroll
-  for (int q = 0; q < SPT; ++q) {
-    const int sidx = tid + 256 * q;
-    const int rr = sidx / 8, sg = sidx % 8;
+  for (int i = 0; i < MT; ++i) {
+    const int q = 256 * i + tid;
+    const int rr = q >> 3, pos = q & 7;
     const int rowc = min(rr, mc - 1);
     const int slot = a.perm[m0 + rowc];
-    if (sg == 0) slot_l[rr] = slot;       // the tile's slot indexes, for the epilogue
+    if (pos == 0) slot_l[rr] = slot;
     const uint16_t* src;
-    if constexpr (MODE == GU) src = x + (uint64_t)(slot / (k + 1)) * H;
+    if constexpr (MODE == GU) src = a.x16 + (uint64_t)(slot / (k + 1)) * H;
     else src = a.hbuf + (uint64_t)(m0 + rowc) * a.Imax;
-    arow[q] = src;
-    aseg[q] = sg;
-    arr[q] = rr;
+    asrc[i] = src + 8 * (pos ^ swz(rr));
   }
   f16v_t acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.f;
-  const int col = lane & 31, hsel = lane >> 5;
-  // K is a multiple of 256, so the step count is a multiple of NS (2 or 4);
-  // the prefetches past the last step re-read it (clamped, never used)
-  const int steps = K / 64;
-  GrpStage<F, SPT> st[NS];
+      for (int v = 0; v < 16; ++v) acc[mt][n][v] = 0.f;
+  const int steps = K / 64;   // a multiple of 4 (K is a multiple of 256)
+  uint8_t* bw[NST];
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    grp_issue<F, SPT>(st[s], arow, aseg, codes, scales, T, nch, nkb, col, hsel, 64 * min(s, steps - 1));
-  for (int base = 0; base < steps; base += NS) {
+  for (int q = 0; q < NST; ++q) bw[q] = stg[q] + 2 * A_STAGE + B_WAVE * w;
+  issue_a<MT>(asrc, reinterpret_cast<uint16_t*>(stg[0]), w, 0);
+  issue_b<F>(bw[0], blk, codes, scales, T, nch, nkb, lane, 0);
+  for (int base = 0; base < steps; base += NST) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int step = base + s;
-      uint16_t* buf = lds_a + (s & 1) * (BM * AST);
-      grp_store_a<MODE, ACT16, SPT>(st[s].av, buf, arr, aseg);
-      grp_issue<F, SPT>(st[(s + NS - 1) % NS], arow, aseg, codes, scales, T, nch, nkb, col, hsel,
-                        64 * min(step + NS - 1, steps - 1));
-      __syncthreads();
-      grp_mma<F, MT, SPT>(acc, st[s], buf, col, hsel);
+    for (int s = 0; s < NST; ++s) {
+      const int t = base + s;
+      if (t >= steps) break;
+      const int tn = min(t + 1, steps - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      issue_a<MT>(asrc, reinterpret_cast<uint16_t*>(stg[(s + 1) % NST]), w, tn);
+      issue_b<F>(bw[(s + 1) % NST], blk, codes, scales, T, nch, nkb, lane, tn);
+      asm volatile("" ::: "memory");
+      wait_vm<MT + B_LOADS>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      BStage<F> bs;
+      read_b<F>(bs, lds_addr(bw[s]), col, hsel, t);
+      step_mma<F, MT>(acc, bs, lds_addr(stg[s]), col, hsel);
     }
   }
+  wait_vm<0>();   // the repeated loads past the last step have landed before the stages are reused
   // ---- epilogue (slot indexes of the tile's rows from LDS; 32-bit offsets:
   // positions < R (k+1) <= 589824 and Imax, H <= 4096 keep them below 2^32)
 #pragma unroll
@@ -449,46 +622,60 @@ __device__ __forceinline__ void grp_tile(const GroupedArgs& a, const uint16_t* _
       } else {
         const uint32_t s = (uint32_t)slot_l[row];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const uint32_t n = 64 * T + 32 * nt + col;
-          a.e_ws[s * (uint32_t)H + n] = acc[mt][nt][v];
-          if (a.tap_e) a.tap_e[(uint64_t)s * H + n] = acc[mt][nt][v];
+        for (int n = 0; n < 2; ++n) {
+          const uint32_t c = 64 * T + 32 * n + col;
+          a.e_ws[s * (uint32_t)H + c] = acc[mt][n][v];
+          if (a.tap_e) a.tap_e[(uint64_t)s * H + c] = acc[mt][n][v];
         }
       }
     }
   }
 }
 
-// One launch for both tile lists, so the two run side by side: workgroups
-// [0, nbig) take the 128-row list (tile wg / nblk, column block wg % nblk),
-// the rest the 32-row list. Each list is sized for its worst case; the
-// workgroups past a list's tile count exit at once.
-template <int FR, int FS, int MODE, int MT, int ACT16>
-__device__ __forceinline__ void grp_list(const GroupedArgs& a, const uint16_t* __restrict__ x, int list, int wg,
-                                         uint16_t* lds_a, int* slot_l) {
-  constexpr int NS = MT == 1 ? 4 : 2;        // pipeline stages
-  const int nblk = a.gemm_nblk;
-  const int ti = wg / nblk, nb = wg % nblk;
-  const int ntiles = a.meta[list];
-  if (ti >= ntiles) return;
-  const int* t = a.tiles + 3 * (list ? a.max_tiles + ti : ti);
-  const int e = t[0], m0 = t[1], mc = t[2];
-  if (e < 0 || e > a.E || mc <= 0) return;
-  const bool shared = e == a.E;
-  const int I = shared ? a.sh.inter : a.rt.inter;
-  const int nlt = MODE == GU ? 2 * I / 64 : a.H / 64;   // layout tiles of this expert along N
-  if (nb * 4 >= nlt) return;
-  if (shared) grp_tile<FS, MODE, MT, ACT16, NS>(a, x, e, m0, mc, nb, lds_a, slot_l);
-  else grp_tile<FR, MODE, MT, ACT16, NS>(a, x, e, m0, mc, nb, lds_a, slot_l);
+template <int F, int MODE>
+__device__ __forceinline__ void gemm_item_mt(const GroupedArgs& a, int e, int m0, int mc, int nb,
+                                             uint8_t* const (&stg)[NST], int* slot_l) {
+  switch ((mc + 31) >> 5) {
+    case 4: gemm_item<F, MODE, 4>(a, e, m0, mc, nb, stg, slot_l); break;
+    case 3: gemm_item<F, MODE, 3>(a, e, m0, mc, nb, stg, slot_l); break;
+    case 2: gemm_item<F, MODE, 2>(a, e, m0, mc, nb, stg, slot_l); break;
+    default: gemm_item<F, MODE, 1>(a, e, m0, mc, nb, stg, slot_l); break;
+  }
 }
 
-template <int FR, int FS, int MODE, int ACT16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_grp_gemm(GroupedArgs a, const uint16_t* __restrict__ x, int nbig) {
-  __shared__ __align__(16) uint16_t lds_a[2 * 128 * AST];
+// Persistent workgroups: each takes items q = (M-tile q / nblk, column block
+// q % nblk) from the queue counter until the list is done. The work list is
+// ordered by tile height, so the long items start first.
+template <int FR, int FS, int MODE>
+__global__ __launch_bounds__(256, GEMM_WG_PER_CU) void k_grp_gemm(GroupedArgs a) {
+  __shared__ __align__(16) uint8_t stg0[STAGE_BYTES];
+  __shared__ __align__(16) uint8_t stg1[STAGE_BYTES];
+  __shared__ __align__(16) uint8_t stg2[STAGE_BYTES];
+  uint8_t* const stg[NST] = {stg0, stg1, stg2};
   __shared__ int slot_l[128];
-  const int wg = blockIdx.x;
-  if (wg < nbig) grp_list<FR, FS, MODE, 4, ACT16>(a, x, 0, wg, lds_a, slot_l);
-  else grp_list<FR, FS, MODE, 1, ACT16>(a, x, 1, wg - nbig, lds_a, slot_l);
+  __shared__ int s_item[2];
+  int* ctr = a.meta + (MODE == GU ? 1 : 2);
+  const int nlt_max = MODE == GU ? 2 * a.Imax / 64 : a.H / 64;   // layout tiles along N (widest class)
+  const int nblk = (nlt_max + 3) / 4;
+  const int n_items = a.meta[0] * nblk;
+  int par = 0;
+  for (;;) {
+    if (threadIdx.x == 0) s_item[par] = atomicAdd(ctr, 1);
+    __syncthreads();
+    const int q = s_item[par];
+    par ^= 1;
+    if (q >= n_items) break;
+    const int* t = a.tiles + 3 * (q / nblk);
+    const int nb = q % nblk;
+    const int e = t[0], m0 = t[1], mc = t[2];
+    if (e < 0 || e > a.E || mc <= 0) continue;
+    const bool shared = e == a.E;
+    const int I = shared ? a.sh.inter : a.rt.inter;
+    const int nlt = MODE == GU ? 2 * I / 64 : a.H / 64;
+    if (nb * 4 >= nlt) continue;
+    if (shared) gemm_item_mt<FS, MODE>(a, e, m0, mc, nb, stg, slot_l);
+    else gemm_item_mt<FR, MODE>(a, e, m0, mc, nb, stg, slot_l);
+  }
 }
 
 // ------------------------------------------------------------------ combine
@@ -523,46 +710,42 @@ __global__ __launch_bounds__(256) void k_grp_combine(GroupedArgs a) {
 }
 
 // ------------------------------------------------------------------ launch
-template <int FR, int FS, int MODE, int ACT16>
-static hipError_t launch_gemm(const GroupedArgs& a, hipStream_t s, int nblk, hipEvent_t* ev, int i) {
-  GroupedArgs b = a;
-  b.gemm_nblk = nblk;
-  // upper bounds of the two lists: every expert's rows split in tiles; an
-  // expert of c >= 96 rows takes ceil(c / 128) <= c / 128 + c / 96 tiles
-  const int slots = a.R * (a.k + 1);
-  const int max_big = slots / 128 + slots / BIG_MIN_ROWS + 1;
-  const int max_small = slots / 32 + a.E + 1;
-  const int nbig = max_big * nblk;
-  launch_k(k_grp_gemm<FR, FS, MODE, ACT16>, dim3(nbig + max_small * nblk), dim3(256), 0, s, ev, i, b, a.x, nbig);
-  return hipGetLastError();
+static int gemm_grid() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * GEMM_WG_PER_CU;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev] * GEMM_WG_PER_CU;
 }
 
-template <int FR, int FS, int ACT16>
+template <int FR, int FS>
 static hipError_t launch_grouped_t(const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
-  const int Imax = a.Imax;
-  launch_k(k_grp_sort, dim3(1), dim3(1024), 0, s, ev, 0, a);
+  // sort workgroup, plus conversion workgroups for bf16 activations
+  const uint64_t n8 = (uint64_t)a.R * a.H / 8;
+  const int nconv = a.act_fp16 ? 0 : (int)std::min<uint64_t>(256, (n8 + 1023) / 1024);
+  launch_k(k_grp_sort, dim3(1 + nconv), dim3(1024), 0, s, ev, 0, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_gemm<FR, FS, GU, ACT16>(a, s, (2 * Imax / 64 + 3) / 4, ev, 2);
-  if (err != hipSuccess) return err;
-  err = launch_gemm<FR, FS, DN, ACT16>(a, s, (a.H / 64 + 3) / 4, ev, 4);
-  if (err != hipSuccess) return err;
+  const int G = gemm_grid();
+  launch_k(k_grp_gemm<FR, FS, GU>, dim3(G), dim3(256), 0, s, ev, 2, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  launch_k(k_grp_gemm<FR, FS, DN>, dim3(G), dim3(256), 0, s, ev, 4, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const uint64_t n = (uint64_t)a.R * (a.H / 4);
   launch_k(k_grp_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ev, 6, a);
   return hipGetLastError();
 }
 
-template <int FR, int FS>
-static hipError_t launch_grouped_a(const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
-  return a.act_fp16 ? launch_grouped_t<FR, FS, 1>(a, s, ev) : launch_grouped_t<FR, FS, 0>(a, s, ev);
-}
-
 template <int FR>
 static hipError_t launch_grouped_s(int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
   switch (fs) {
-    case F_Q4: return launch_grouped_a<FR, F_Q4>(a, s, ev);
-    case F_Q3: return launch_grouped_a<FR, F_Q3>(a, s, ev);
-    case F_S4: return launch_grouped_a<FR, F_S4>(a, s, ev);
+    case F_Q4: return launch_grouped_t<FR, F_Q4>(a, s, ev);
+    case F_Q3: return launch_grouped_t<FR, F_Q3>(a, s, ev);
+    case F_S4: return launch_grouped_t<FR, F_S4>(a, s, ev);
   }
   return hipErrorInvalidValue;
 }

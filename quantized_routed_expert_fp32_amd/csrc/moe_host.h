@@ -59,7 +59,8 @@ struct GroupedWs {
   uint64_t perm_off;   // int32 [R*k + R]: expert-major position -> slot index (r*(k+1)+j)
   uint64_t h_off;      // f16 [R*(k+1), Imax] in expert-major order
   uint64_t e_off;      // f32 [R*(k+1), H] in slot order (r*(k+1)+j)
-  uint64_t tiles_off;  // int32 [2][max_tiles][3] tile lists
+  uint64_t x16_off;    // f16 [R, H] activations for the GEMMs (bf16 layers)
+  uint64_t tiles_off;  // int32 [max_tiles][3] work list of M-tiles
   uint64_t total;
   int max_tiles;
 };

@@ -56,13 +56,13 @@ struct GroupedArgs {
   const int32_t* ids;
   const float* p;
   const float* sg;
-  int32_t* meta;     // counts/offsets/tile count
+  const uint16_t* x16;  // [R, H] fp16 activations for the GEMMs (x itself, or a copy of bf16 x)
+  int32_t* meta;     // tile count, queue counters, expert offsets
   int32_t* perm;     // expert-major position -> slot index r*(k+1)+j
   uint16_t* hbuf;    // [R*(k+1), Imax] fp16 bits (expert-major order)
   float* e_ws;       // [R*(k+1), H] slot order
-  int32_t* tiles;    // two tile lists of (expert, first position, rows)
-  int max_tiles;     // capacity of each list
-  int gemm_nblk;     // column blocks of the GEMM being launched
+  int32_t* tiles;    // work list of M-tiles (expert, first position, rows)
+  int max_tiles;     // capacity of the list
   float* y;
   float* tap_gu;
   float* tap_h;

@@ -452,10 +452,11 @@ GroupedWs grouped_ws_layout(const moe_layer_desc* d, int rows) {
   w.perm_off = o; o = align256(o + slots * 4);
   w.h_off = o; o = align256(o + slots * Imax * 2);
   w.e_off = o; o = align256(o + slots * H * 4);
-  // tile lists: an expert's rows split into M-tiles of 32 or 128 rows
-  // (128 only from 96 rows on): each list holds at most slots/32 + E + 1
-  w.max_tiles = (int)(slots / 32 + E + 2);
-  w.tiles_off = o; o = align256(o + (uint64_t)w.max_tiles * 2 * 3 * 4);
+  w.x16_off = o; o = align256(o + (uint64_t)rows * H * 2);
+  // work list: an expert's rows split into M-tiles of 128 rows and one
+  // shorter last tile: at most slots/128 + E + 1 tiles
+  w.max_tiles = (int)(slots / 128 + E + 2);
+  w.tiles_off = o; o = align256(o + (uint64_t)w.max_tiles * 3 * 4);
   w.total = o;
   return w;
 }
