@@ -1,20 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert FFN (qwen3_5-MoE 35B-A3B shapes) on one MI355X.
 
-Workload (the headline): decode, 8 independent rows through 40 distinct MoE
-layer weight sets (hidden 2048, 256 experts, top-8, expert intermediate 512,
-shared expert 512), 4-bit affine g64 weights everywhere (~18 GB packed, so
-the ~4 GB of expert bytes a step touches cannot stay in cache). One step is
-one pass of the whole hot path over one batch: for each of the 40 layers,
-route (logits, top-8, weights, shared gate) then the decode experts
-(gate/up + SwiGLU, down, combine). Inputs are resident in HBM before the
-timed region; each step takes a fresh set of activations (4 sets rotate).
+Headline workload: decode, 8 independent rows through 40 distinct MoE layer
+weight sets (hidden 2048, 256 experts, top-8, expert intermediate 512, shared
+expert 512), 4-bit affine g64 weights everywhere (~18 GB packed, so the ~4 GB
+of expert bytes a step touches cannot stay in cache). One step is one pass of
+the whole hot path over one batch: for each of the 40 layers, route (logits,
+top-8, weights, shared gate) then the decode experts (gate/up + SwiGLU, down,
+combine). Inputs are resident in HBM before the timed region; each step takes
+a fresh set of activations (4 sets rotate).
 
 Prints ONE JSON line. `value` is MoE-layer tokens/s: rows x layers per
 second. `roofline` is the dominant kernel (decode gate/up) timed live with
 HIP events on its stream: algorithmic bytes per launch (the packed gate/up
 bytes of the unique experts the launch reads, plus x in and h out) over its
-mean duration. `cpu_baseline` is the FP64 oracle timed on a bounded sample.
+mean duration. `workloads` holds the other shapes on their own binding
+rooflines: one decode row and the mixed 3-bit layers (1 and 8 rows), both
+over 40 distinct layers, and the two prompt chunks (512 rows 4-bit against
+HBM, 2048 rows W4A16 Zipf against MFMA), each chunk timed over 4 rotating
+weight sets. `cpu_baseline` is the FP64 oracle timed on bounded samples on
+the host cores (all of them, and one thread).
+
+Per-kernel times come from HIP events recorded inside the library's launches
+on the bench stream; the launches of a timed pass are queued behind a GPU-side
+sleep so that the kernels run back to back (host launch gaps do not count).
 """
 from __future__ import annotations
 
@@ -33,6 +42,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2516.6
 METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA TFLOPS as % of peak"
+N_PREFILL_SETS = 4     # weight sets a prompt-chunk timing rotates through
 
 
 def log(*a):
@@ -89,19 +99,49 @@ def build_layers(spec, n_layers, B, to_abi, synth, keep_host=0):
     return layers, host_keep
 
 
-def cpu_baseline(spec, Lh, rows, budget_s=15.0):
-    """The FP64 oracle (as it stands) on one layer x `rows` rows, BLAS on 1 thread."""
-    import contextlib
+def cpu_model():
+    """The host CPU's model name (the first `model name` of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
-    import oracle.moe_oracle as O
-    import synth
+
+def host_threads():
+    """Threads the oracle's BLAS may use on this host: the CPUs this process
+    may run on, capped by OMP_NUM_THREADS when that is set."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def _blas_threads(n):
+    import contextlib
     try:
         from threadpoolctl import threadpool_limits
-        ctx = threadpool_limits(limits=1)
+        return threadpool_limits(limits=n)
     except Exception:  # pragma: no cover
-        ctx = contextlib.nullcontext()
+        return contextlib.nullcontext()
+
+
+def cpu_decode_baseline(spec, Lh, rows, threads, budget_s=12.0):
+    """The FP64 oracle (as it stands), per-row form, on one layer x up to
+    `rows` rows, numpy's BLAS on `threads` threads; experts are dequantised
+    on first use inside the timed region (part of the oracle's work)."""
+    import oracle.moe_oracle as O
+    import synth
     xb = synth.make_x(spec, 0, rows, rep=0)
-    with ctx:
+    with _blas_threads(threads):
         t0 = time.perf_counter()
         done = 0
         dense = O.DenseExperts(Lh, cache=True)
@@ -111,102 +151,285 @@ def cpu_baseline(spec, Lh, rows, budget_s=15.0):
             if time.perf_counter() - t0 > budget_s:
                 break
         dt = time.perf_counter() - t0
-    return dict(value=done / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{done} decode rows (x of the workload's first layer) through that "
-                       f"layer, per-row fp64 form, experts dequantised on first use, {dt:.1f} s")
+    return dict(value=done / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{done} decode rows through the first layer of {spec.name}, per-row fp64 "
+                       f"form, experts dequantised on first use, {dt:.1f} s")
 
 
-def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream, windows=False):
-    """One prompt chunk through one layer: route + grouped experts, timed as a
-    HIP graph; per-phase times from events inside the library's launches."""
+def cpu_prefill_baseline(spec, Lh, xb, threads):
+    """The FP64 oracle's expert-major form (each expert's rows as one matrix
+    product) on a whole prompt chunk, BLAS on `threads` threads; the timed
+    region includes dequantising every touched expert."""
+    import oracle.moe_oracle as O
+    with _blas_threads(threads):
+        t0 = time.perf_counter()
+        O.moe_forward(Lh, xb, form="expert_major")
+        dt = time.perf_counter() - t0
+    return dict(value=xb.shape[0] / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"one {xb.shape[0]}-row chunk of {spec.name}, expert-major fp64 form, {dt:.1f} s")
+
+
+class GpuSleep:
+    """Queues a GPU-side wait (torch.cuda._sleep) long enough for the host to
+    enqueue a timed pass behind it, so the pass's kernels run back to back."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 20_000_000
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(n // 10)
+            e0.record(stream)
+            torch.cuda._sleep(n)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        self.cycles_per_ms = n / max(e0.elapsed_time(e1), 1e-3)
+
+    def __call__(self, ms):
+        self.torch.cuda._sleep(int(self.cycles_per_ms * ms))
+
+
+def event_pass(torch, stream, sleeper, n_passes, n_ev, enqueue):
+    """Runs `enqueue(events)` n_passes times, each queued behind a GPU sleep of
+    twice the host's measured enqueue time, with n_ev timing events per pass.
+    Returns the events and the host enqueue time of one pass (ms)."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(n_passes)]
+    with torch.cuda.stream(stream):
+        for es in evs:              # torch creates the HIP event on first record
+            for e in es:
+                e.record(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        enqueue(None)
+        t_enq = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        for es in evs:
+            sleeper(2.0 * t_enq + 0.5)
+            enqueue(es)
+        torch.cuda.synchronize()
+    return evs, t_enq
+
+
+def prefill_algorithmic(spec, ids):
+    """Algorithmic bytes and flops of one prompt chunk: the packed bytes of
+    the unique routed experts its ids select plus the shared expert, router
+    and gate row, x in and y out (fp32); flops 2*3*H*I per (row, slot), the
+    shared expert's per row, and the router's 2*(E+1)*H per row."""
+    R, k = ids.shape
+    H, E = spec.hidden, spec.n_experts
+    uniq = len(np.unique(ids[(ids >= 0) & (ids < E)]))
+    gu_b, dn_b = expert_bytes(spec, spec.routed, spec.inter)
+    sgu_b, sdn_b = expert_bytes(spec, spec.shared, spec.shared_inter)
+    act_b = 2
+    nbytes = uniq * (gu_b + dn_b) + sgu_b + sdn_b + router_bytes(spec) + R * H * act_b + R * H * 4
+    f_routed = 2.0 * 3 * H * spec.inter * R * k
+    f_shared = 2.0 * 3 * H * spec.shared_inter * R
+    f_router = 2.0 * (E + 1) * H * R
+    return dict(bytes=nbytes, unique_experts=uniq, flop_routed=f_routed, flop_shared=f_shared,
+                flop_router=f_router)
+
+
+def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream, sleeper,
+                  n_sets=N_PREFILL_SETS, windows=False, keep_host=False):
+    """One prompt chunk through one layer: route + grouped experts. The timed
+    replays rotate through n_sets distinct weight sets (each with its own
+    activations), so the touched experts come from HBM, not the MALL. Whole
+    chunks are timed as HIP graph replays; per-phase times from events inside
+    the library's launches, queued behind a GPU sleep."""
     spec = synth.CONFIGS[cfg_id]
     R, k, H, E = spec.rows[0], spec.top_k, spec.hidden, spec.n_experts
-    I, Is = spec.inter, spec.shared_inter
-    Lh = synth.make_layer(spec, 0)
-    layer = B.pack_layer(B.layer_desc(*to_abi.desc_args(spec)), to_abi.tensors(Lh))
-    bias = torch.from_numpy(Lh.logit_bias).to(dev) if Lh.logit_bias is not None else None
-    del Lh
-    x = torch.from_numpy(synth.make_x(spec, 0, R, rep=0).view(np.int16)).to(dev)
+    desc = B.layer_desc(*to_abi.desc_args(spec))
+    layers, biases, xs, host = [], [], [], None
+    for l in range(n_sets):
+        Lh = synth.make_layer(spec, l)
+        layers.append(B.pack_layer(desc, to_abi.tensors(Lh)))
+        biases.append(torch.from_numpy(Lh.logit_bias).to(dev) if Lh.logit_bias is not None else None)
+        xs.append(torch.from_numpy(synth.make_x(spec, l, R, rep=0).view(np.int16)).to(dev))
+        if keep_host and l == 0:
+            host = Lh
+        del Lh
     ids = torch.empty((R, k), dtype=torch.int32, device=dev)
     p = torch.empty((R, k), dtype=torch.float32, device=dev)
     sg = torch.empty((R,), dtype=torch.float32, device=dev)
     y = torch.empty((R, H), dtype=torch.float32, device=dev)
-    ws = B.new_workspace(layer, R, True, dev)
+    ws = B.new_workspace(layers[0], R, True, dev, stream=stream)
 
-    def chunk(events=None):
-        B.route(layer, x, bias, taps=dict(events=events[:2]) if events else None,
+    def chunk(l, events=None):
+        B.route(layers[l], xs[l], biases[l], taps=dict(events=events[:2]) if events else None,
                 out=(ids, p, sg), ws=ws, stream=stream)
-        B.experts(layer, x, ids, p, sg, True, ws=ws, y=y,
+        B.experts(layers[l], xs[l], ids, p, sg, True, ws=ws, y=y,
                   taps=dict(events=events[2:]) if events else None, stream=stream)
 
+    # algorithmic work of each weight set's chunk
+    alg = []
     with torch.cuda.stream(stream):
-        chunk()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            chunk()
-        for _ in range(warmup):
-            g.replay()
+        for l in range(n_sets):
+            chunk(l)
+            stream.synchronize()
+            alg.append(prefill_algorithmic(spec, ids.cpu().numpy()))
+        graphs = []
+        for l in range(n_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                chunk(l)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % n_sets].replay()
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        for _ in range(steps):
-            g.replay()
+        for i in range(steps):
+            graphs[i % n_sets].replay()
         t1.record(stream)
         torch.cuda.synchronize()
     us = t0.elapsed_time(t1) / steps * 1e3
+    mean = lambda key: float(np.mean([alg[i % n_sets][key] for i in range(steps)]))
+    nbytes = mean("bytes")
+    f_rt, f_sh, f_ro = mean("flop_routed"), mean("flop_shared"), mean("flop_router")
     # per phase: route | sort | gate/up GEMMs | down GEMMs | combine
-    n_ev = 10
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
-    with torch.cuda.stream(stream):
-        for es in evs:
-            for e in es:
-                e.record(stream)
-        for es in evs:
-            chunk(events=es)
-        torch.cuda.synchronize()
+    evs, _ = event_pass(torch, stream, sleeper, steps, 10,
+                        lambda es, c=[0]: (chunk(c[0] % n_sets, es), c.__setitem__(0, c[0] + 1)))
     ph = np.zeros(5)
     for es in evs:
         for i in range(5):
             ph[i] += es[2 * i].elapsed_time(es[2 * i + 1])
     ph = ph / steps * 1e3
-    slots = R * k
-    f_gu = 2.0 * (slots * 2 * I + R * 2 * Is) * H
-    f_dn = 2.0 * (slots * I + R * Is) * H
-    f_rt = 2.0 * R * H * (E + 1)
-    ids_h = ids.cpu().numpy()
-    cnt = np.bincount(ids_h.reshape(-1), minlength=E)
     tf = lambda f, t: f / (t * 1e-6) / 1e12
+    cnt = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
     res = {
-        "workload": spec.name, "rows": R, "us_per_chunk": us, "tokens_per_s": R / (us * 1e-6),
-        "flop": f_gu + f_dn + f_rt, "tflops": tf(f_gu + f_dn + f_rt, us),
-        "frac_mfma_peak": tf(f_gu + f_dn + f_rt, us) / MFMA_F16_PEAK_TFLOPS,
-        "phase_us": {"route": ph[0], "sort": ph[1], "gate_up": ph[2], "down": ph[3],
-                     "combine": ph[4]},
-        "gate_up_tflops": tf(f_gu, ph[2]), "down_tflops": tf(f_dn, ph[3]),
+        "workload": spec.name, "rows": R, "weight_sets": n_sets, "us_per_chunk": us,
+        "tokens_per_s": R / (us * 1e-6),
+        "algorithmic_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+        "frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "flop": f_rt + f_sh + f_ro, "tflops": tf(f_rt + f_sh + f_ro, us),
+        "frac_mfma": tf(f_rt + f_sh + f_ro, us) / MFMA_F16_PEAK_TFLOPS,
+        "tflops_without_shared_flops": tf(f_rt + f_ro, us),
+        "phase_us": {"route": ph[0], "sort": ph[1], "gate_up": ph[2], "down": ph[3], "combine": ph[4]},
+        "gate_up_tflops": tf(2 * (f_rt + f_sh) / 3, ph[2]), "down_tflops": tf((f_rt + f_sh) / 3, ph[3]),
+        "mean_unique_experts": mean("unique_experts"),
         "rows_per_expert": {"max": int(cnt.max()), "mean": float(cnt.mean()),
                             "empty": int((cnt == 0).sum())},
     }
     if windows:
         # the same chunk through the decode step's arithmetic in 16-row windows
-        # (moe_forward_windows: same bits however the prompt is cut), eager;
-        # off by default so that the decode kernels' traced averages stay the
-        # 8-row workload's
-        wws = B.new_workspace(layer, 16, False, dev)
+        # (moe_forward_windows: same bits however the prompt is cut), eager
+        wws = B.new_workspace(layers[0], 16, False, dev, stream=stream)
         with torch.cuda.stream(stream):
-            B.forward_windows(layer, x, bias, ws=wws, out=(ids, p, sg), y=y, stream=stream)
+            B.forward_windows(layers[0], xs[0], biases[0], ws=wws, out=(ids, p, sg), y=y, stream=stream)
             torch.cuda.synchronize()
             t0.record(stream)
-            for _ in range(3):
-                B.forward_windows(layer, x, bias, ws=wws, out=(ids, p, sg), y=y, stream=stream)
+            for i in range(3):
+                B.forward_windows(layers[i % n_sets], xs[i % n_sets], biases[i % n_sets], ws=wws,
+                                  out=(ids, p, sg), y=y, stream=stream)
             t1.record(stream)
             torch.cuda.synchronize()
         res["windows_us_per_chunk"] = t0.elapsed_time(t1) / 3 * 1e3
-    log(f"[bench] prefill {spec.name}: {us:.1f} us/chunk, {res['tokens_per_s']:.0f} tokens/s, "
-        f"{res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma_peak']:.1f}% of f16 MFMA); "
+    log(f"[bench] prefill {spec.name} ({n_sets} weight sets): {us:.1f} us/chunk, "
+        f"{res['tokens_per_s']:.0f} tokens/s, {res['gbs']:.0f} GB/s ({100 * res['frac_hbm']:.1f}% of HBM), "
+        f"{res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma']:.1f}% of f16 MFMA); "
         + ", ".join(f"{k_} {v:.1f}" for k_, v in res["phase_us"].items())
         + (f"; 16-row windows {res['windows_us_per_chunk']:.1f} us/chunk" if windows else ""))
+    del graphs, ws
+    return res, host
+
+
+def bench_decode(spec, layers, R, steps, warmup, B, synth, torch, dev, stream, sleeper,
+                 graph=True, tag=""):
+    """Decode: R rows through every layer of `layers` (route, then the decode
+    experts), 4 activation sets rotating. Whole steps are timed as HIP graph
+    replays; per-kernel times from events inside the library's launches."""
+    L, k, H = len(layers), spec.top_k, spec.hidden
+    NX = 4
+    xs = [[torch.from_numpy(synth.make_x(spec, l, R, rep=s).view(np.int16)).to(dev)
+           for s in range(NX)] for l in range(L)]
+    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
+    p = torch.empty((R, k), dtype=torch.float32, device=dev)
+    sg = torch.empty((R,), dtype=torch.float32, device=dev)
+    y = torch.empty((R, H), dtype=torch.float32, device=dev)
+    ws = B.new_workspace(layers[0], R, False, dev, stream=stream)
+
+    def step(s, events=None):
+        for l in range(L):
+            x = xs[l][s % NX]
+            rt = dict(events=events[6 * l:6 * l + 2]) if events is not None else None
+            B.route(layers[l], x, taps=rt, out=(ids, p, sg), ws=ws, stream=stream)
+            tp = dict(events=events[6 * l + 2:6 * l + 6]) if events is not None else None
+            B.experts(layers[l], x, ids, p, sg, False, ws=ws, y=y, taps=tp, stream=stream)
+
+    # unique experts per (layer, x set): algorithmic bytes
+    uniq = np.zeros((L, NX), np.int64)
+    with torch.cuda.stream(stream):
+        for l in range(L):
+            for s in range(NX):
+                B.route(layers[l], xs[l][s], out=(ids, p, sg), ws=ws, stream=stream)
+                stream.synchronize()
+                uniq[l, s] = len(np.unique(ids.cpu().numpy()))
+    gu_b, dn_b = expert_bytes(spec, spec.routed, spec.inter)
+    sgu_b, sdn_b = expert_bytes(spec, spec.shared, spec.shared_inter)
+    x_b, y_b = R * H * 2, R * H * 4
+    h_b = R * (k + 1) * max(spec.inter, spec.shared_inter) * 4
+    gu_launch_bytes = uniq * gu_b + sgu_b + x_b + h_b            # per gate/up launch
+    step_bytes = (uniq * (gu_b + dn_b) + sgu_b + sdn_b + router_bytes(spec) + x_b + y_b).sum(0)
+
+    graphs = None
+    if graph:
+        try:
+            graphs = []
+            for s in range(NX):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(s)
+                graphs.append(g)
+        except Exception as e:  # graph capture unavailable: time eager launches
+            log(f"[bench] graph capture failed ({e}); timing eager launches")
+            graphs = None
+    run = (lambda s: graphs[s % NX].replay()) if graphs else (lambda s: step(s))
+    with torch.cuda.stream(stream):
+        for s in range(warmup):
+            run(s)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for s in range(steps):
+            run(s)
+        t1.record(stream)
+        torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    mean_step_bytes = float(np.mean([step_bytes[s % NX] for s in range(steps)]))
+
+    # per kernel: events around route, gate/up, down + combine of every layer
+    nk = max(1, min(steps, 20))
+    evs, t_enq = event_pass(torch, stream, sleeper, nk, 6 * L,
+                            lambda es, c=[0]: (step(c[0], es), c.__setitem__(0, c[0] + 1)))
+    dur = np.zeros(3)
+    gu_bytes_sum = 0.0
+    for s in range(nk):
+        e = evs[s]
+        for l in range(L):
+            for i in range(3):
+                dur[i] += e[6 * l + 2 * i].elapsed_time(e[6 * l + 2 * i + 1])
+            gu_bytes_sum += gu_launch_bytes[l, (s + 1) % NX]
+    n_launch = nk * L
+    kus = dur / n_launch * 1e3
+    gu_bytes = gu_bytes_sum / n_launch
+    achieved = gu_bytes / (kus[1] * 1e-6) / 1e9
+    res = {
+        "workload": spec.name, "rows": R, "layers": L, "ms_per_step": ms_step,
+        "us_per_layer": ms_step * 1e3 / L, "tokens_per_s": R * L / (ms_step / 1e3),
+        "algorithmic_bytes_per_step": mean_step_bytes,
+        "gbs": mean_step_bytes / ms_step / 1e6, "frac_hbm": mean_step_bytes / ms_step / 1e6 / HBM_PEAK_GBS,
+        "kernel_us": {"route": kus[0], "decode_gateup": kus[1], "decode_down_combine": kus[2]},
+        "gateup_bytes_per_launch": gu_bytes, "gateup_gbs": achieved,
+        "mean_unique_experts": float(uniq.mean()),
+        "timing": "hip graph replay" if graphs else "eager",
+    }
+    log(f"[bench] decode {tag or spec.name} rows={R} layers={L}: {res['us_per_layer']:.2f} us/layer, "
+        f"{res['tokens_per_s']:.0f} tokens/s, step HBM {res['gbs']:.0f} GB/s "
+        f"({100 * res['frac_hbm']:.1f}%); route {kus[0]:.2f}, gate/up {kus[1]:.2f} ({achieved:.0f} GB/s), "
+        f"down+combine {kus[2]:.2f} us")
+    del graphs, ws
     return res
 
 
@@ -251,17 +474,13 @@ def copy_calibration():
 
 
 def measured_ceilings(torch, dev, stream):
-    """Practical ceilings beside the published peaks: a plain 1 GiB device
-    copy (read + write bytes over its time) and a square fp16 GEMM of 8192
-    through torch's BLAS, each timed with events on the bench stream after
-    warm-up. Context for the roofline fractions, not their denominators."""
+    """A practical HBM ceiling beside the published peak: a plain 1 GiB device
+    copy (read + write bytes over its time), timed with events on the bench
+    stream after warm-up. Context for the roofline fractions, not their
+    denominator."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
-    m = 8192
-    A = torch.randn(m, m, dtype=torch.float16, device=dev)
-    Bm = torch.randn(m, m, dtype=torch.float16, device=dev)
-    C = torch.empty(m, m, dtype=torch.float16, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     out = {}
     with torch.cuda.stream(stream):
@@ -274,17 +493,62 @@ def measured_ceilings(torch, dev, stream):
         e1.record(stream)
         torch.cuda.synchronize()
         out["copy_1GiB_gbs"] = 2 * n * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
-        for _ in range(3):
-            torch.mm(A, Bm, out=C)
-        e0.record(stream)
-        for _ in range(10):
-            torch.mm(A, Bm, out=C)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        out["gemm_fp16_8192_tflops"] = 2 * m ** 3 * 10 / (e0.elapsed_time(e1) / 1e3) / 1e12
-    del a, b, A, Bm, C
+    del a, b
     torch.cuda.empty_cache()
     return out
+
+
+def grouped_source_hash():
+    """sha256 over the grouped-path kernel sources (what an MFMA counter
+    figure of the grouped GEMMs applies to)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("grouped.hip", "moe_kernels.h", "moe_launch.h"):
+        with open(os.path.join(ROOT, "quantized_routed_expert_fp32_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def mfma_summary(pmc_csv, trace_csv, commands, n_cu=256, simd_per_cu=4, n_xcd=8):
+    """Markdown summary of the grouped GEMMs' MFMA counters: per kernel, the
+    mean per dispatch of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F16,
+    GRBM_GUI_ACTIVE and the other SQ counters of the pass, with
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x CUs x SIMDs)
+    (GRBM_GUI_ACTIVE reads the sum over the 8 XCDs of their active cycles)
+    and the counted f16 MFMA flops (512 per MOPS unit) over the mean duration
+    from the kernel trace, against 2,516.6 TFLOP/s."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(pmc_csv)):
+        if "k_grp_" not in r["Kernel_Name"]:
+            continue
+        vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    dur = defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        if "k_grp_" in r["Kernel_Name"]:
+            dur[r["Kernel_Name"]].append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3)
+    lines = ["# MFMA counters of the grouped GEMMs, prompt chunks of 512 rows (4-bit g64) and 2048 rows (W4A16 Zipf)",
+             "", "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", f"- source_sha256: {grouped_source_hash()}",
+              f"- mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {n_xcd} XCDs x {n_cu} CUs x "
+              f"{simd_per_cu} SIMDs); GRBM_GUI_ACTIVE sums the XCDs' active cycles",
+              "- mfma_tflops = 512 x SQ_INSTS_VALU_MFMA_MOPS_F16 / mean duration (kernel trace)", ""]
+    names = sorted(vals)
+    cols = sorted({c for n in names for c in vals[n]})
+    lines.append("| kernel | dispatches | mean us | " + " | ".join(cols) + " | mfma_busy | mfma_tflops | of peak |")
+    lines.append("|---" * (len(cols) + 6) + "|")
+    for n in names:
+        m = {c: float(np.mean(v)) for c, v in vals[n].items()}
+        nd = max(len(v) for v in vals[n].values())
+        us = float(np.mean(dur[n])) if dur.get(n) else float("nan")
+        busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (
+            m.get("GRBM_GUI_ACTIVE", float("nan")) / n_xcd * n_cu * simd_per_cu)
+        tfl = 512.0 * m.get("SQ_INSTS_VALU_MFMA_MOPS_F16", float("nan")) / (us * 1e-6) / 1e12
+        lines.append(f"| `{n}` | {nd} | {us:.1f} | " + " | ".join(f"{m[c]:.4g}" for c in cols)
+                     + f" | {busy:.3f} | {tfl:.1f} | {tfl / MFMA_F16_PEAK_TFLOPS:.3f} |")
+    return "\n".join(lines) + "\n"
 
 
 def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel, commands):
@@ -322,20 +586,33 @@ def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel
     return "\n".join(lines) + "\n"
 
 
+def trace_summary(stats_csv, title, command, render, top=16):
+    """Markdown table of a rocprofv3 kernel-stats CSV: per kernel the calls
+    and the average, min and max duration in microseconds, and its share."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# {title}", "", "Command (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", "",
+             f"    {command}", f"    {render}", "",
+             "Durations in microseconds:", "",
+             "| kernel | calls | average | min | max | share |", "|---|---|---|---|---|---|"]
+    for r in rows[:top]:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=None, help="override the 40 layers (debug)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="only the prompt-chunk lines (debug)")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--decode-config", type=int, default=1, choices=(0, 1, 2),
-                    help="decode workload (default 1, the 8-row 40-layer 4-bit one; 2 is the mixed "
-                         "3-bit one, 0 the one-row one)")
-    ap.add_argument("--rows", type=int, default=None, help="decode rows (default: the workload's)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the headline decode workload and the prompt chunks (no 1-row and 3-bit lines)")
     ap.add_argument("--windows", action="store_true",
                     help="also time each prompt chunk through moe_forward_windows (16-row decode windows)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -343,17 +620,25 @@ def main():
     ap.add_argument("--counter-summary", nargs=4, metavar="CSV",
                     help="print the counter summary of k_dec_gateup from the FETCH_SIZE, "
                          "WRITE_SIZE, copy FETCH_SIZE and copy WRITE_SIZE counter CSVs")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("CSV", "PROGRAM", "TITLE"),
+                    help="print a markdown table of a kernel-stats CSV written by rocprofv3 "
+                         "--kernel-trace --stats around PROGRAM")
+    ap.add_argument("--mfma-summary", nargs=2, metavar="CSV",
+                    help="print the MFMA counter summary of the grouped GEMMs from a counter CSV "
+                         "and a kernel-trace CSV of `bench.py --prefill-only`")
     args = ap.parse_args()
     if args.copy_calib:
         copy_calibration()
         return
+
+    def run_of(path):
+        folder = os.path.dirname(path)
+        return folder, os.path.basename(path).split("_counter_collection")[0].split("_kernel_trace")[0]
+
     if args.counter_summary:
         # the commands that wrote the four CSVs: each pass's output folder and
         # file prefix are read back from the CSV path it was given
-        def run_of(path):
-            folder = os.path.dirname(path)
-            return folder, os.path.basename(path).split("_counter_collection")[0]
-        dec = "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-prefill --no-graph"
+        dec = "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-prefill --no-extra --no-graph"
         passes = [("FETCH_SIZE", dec), ("WRITE_SIZE", dec), ("FETCH_SIZE", "python3 bench.py --copy-calib"),
                   ("WRITE_SIZE", "python3 bench.py --copy-calib")]
         cmds = []
@@ -362,6 +647,26 @@ def main():
             cmds.append(f"rocprofv3 --pmc {counter} --output-format csv -d {folder} -o {prefix} -- {prog}")
         cmds.append("python3 bench.py --counter-summary " + " ".join(args.counter_summary))
         sys.stdout.write(counter_summary(*args.counter_summary, "k_dec_gateup", cmds))
+        return
+    if args.trace_summary:
+        path, prog, title = args.trace_summary
+        folder, prefix = run_of(path)
+        prefix = prefix.split("_kernel_stats")[0]
+        sys.stdout.write(trace_summary(path, title, f"rocprofv3 --kernel-trace --stats --output-format csv "
+                                                    f"-d {folder} -o {prefix} -- {prog}",
+                                       f'python3 bench.py --trace-summary {path} "{prog}" "{title}"'))
+        return
+    if args.mfma_summary:
+        import csv
+        pmc, trace = args.mfma_summary
+        counters = sorted({r["Counter_Name"] for r in csv.DictReader(open(pmc))})
+        prog = "python3 bench.py --prefill-only --steps 5 --warmup 1"
+        fp, pp = run_of(pmc)
+        ft, pt = run_of(trace)
+        cmds = [f"rocprofv3 --pmc {' '.join(counters)} --output-format csv -d {fp} -o {pp} -- {prog}",
+                f"rocprofv3 --kernel-trace --output-format csv -d {ft} -o {pt} -- {prog}",
+                "python3 bench.py --mfma-summary " + " ".join(args.mfma_summary)]
+        sys.stdout.write(mfma_summary(pmc, trace, cmds))
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not run "
@@ -378,133 +683,76 @@ def main():
     dev = torch.device("cuda:0")
 
     stream = torch.cuda.Stream()
-    prefill = None
+    sleeper = GpuSleep(torch, stream)
+    prefill, host_prefill = {}, {}
     if not args.no_prefill:
-        prefill = [bench_prefill(c, 20, 3, B, to_abi, synth, torch, dev, stream, args.windows) for c in (3, 4)]
+        for c in (3, 4):
+            r, h = bench_prefill(c, args.steps, args.warmup, B, to_abi, synth, torch, dev, stream, sleeper,
+                                 windows=args.windows, keep_host=not args.no_cpu_baseline)
+            prefill[f"c{c}"] = r
+            host_prefill[c] = h
+            torch.cuda.empty_cache()
         if args.prefill_only:
             print(json.dumps({"prefill": prefill}), flush=True)
             return
 
-    spec = synth.CONFIGS[args.decode_config]
+    spec = synth.CONFIGS[1]
     L = args.layers or spec.layers
-    R, k, H = args.rows or spec.rows[-1], spec.top_k, spec.hidden
-    NX = 4
-    # the stored counter summary covers the default decode workload only
-    default_workload = args.decode_config == 1 and R == spec.rows[-1] and L == spec.layers
-    log(f"[bench] workload {spec.name}: rows={R} layers={L}")
+    R, k, H = spec.rows[-1], spec.top_k, spec.hidden
+    default_workload = L == spec.layers
     layers, host = build_layers(spec, L, B, to_abi, synth, keep_host=1)
-    xs = [[torch.from_numpy(synth.make_x(spec, l, R, rep=s).view(np.int16)).to(dev)
-           for s in range(NX)] for l in range(L)]
-    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
-    p = torch.empty((R, k), dtype=torch.float32, device=dev)
-    sg = torch.empty((R,), dtype=torch.float32, device=dev)
-    y = torch.empty((R, H), dtype=torch.float32, device=dev)
-    ws = B.new_workspace(layers[0], R, False, dev)
-
-    def step(s, events=None):
-        for l in range(L):
-            x = xs[l][s % NX]
-            rt = dict(events=events[l][:2]) if events is not None else None
-            B.route(layers[l], x, taps=rt, out=(ids, p, sg), ws=ws, stream=stream)
-            tp = dict(events=events[l][2:]) if events is not None else None
-            B.experts(layers[l], x, ids, p, sg, False, ws=ws, y=y, taps=tp, stream=stream)
-
-    # unique experts per (layer, x set): algorithmic bytes
-    uniq = np.zeros((L, NX), np.int64)
-    with torch.cuda.stream(stream):
-        for l in range(L):
-            for s in range(NX):
-                B.route(layers[l], xs[l][s], out=(ids, p, sg), ws=ws, stream=stream)
-                stream.synchronize()
-                uniq[l, s] = len(np.unique(ids.cpu().numpy()))
-    gu_b, dn_b = expert_bytes(spec, spec.routed, spec.inter)
-    sgu_b, sdn_b = expert_bytes(spec, spec.shared, spec.shared_inter)
-    x_b, y_b = R * H * 2, R * H * 4
-    h_b = R * (k + 1) * max(spec.inter, spec.shared_inter) * 4
-    gu_launch_bytes = uniq * gu_b + sgu_b + x_b + h_b            # per gate/up launch
-    step_bytes = (uniq * (gu_b + dn_b) + sgu_b + sdn_b + router_bytes(spec) + x_b + y_b).sum(0)
-
-    # ---- timed region: whole steps
-    graphs = None
-    if not args.no_graph:
-        try:
-            graphs = []
-            for s in range(NX):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    step(s)
-                graphs.append(g)
-        except Exception as e:  # graph capture unavailable: time eager launches
-            log(f"[bench] graph capture failed ({e}); timing eager launches")
-            graphs = None
-    run = (lambda s: graphs[s % NX].replay()) if graphs else (lambda s: step(s))
-    with torch.cuda.stream(stream):
-        for s in range(args.warmup):
-            run(s)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for s in range(args.steps):
-            run(s)
-        t1.record(stream)
-        torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
-    tokens_per_s = R * L / (ms_step / 1e3)
-    mean_step_bytes = float(np.mean([step_bytes[s % NX] for s in range(args.steps)]))
-    log(f"[bench] {ms_step * 1e3:.1f} us/step, {ms_step * 1e3 / L:.2f} us/layer, "
-        f"{tokens_per_s:.0f} tokens/s, step HBM {mean_step_bytes / ms_step / 1e6:.0f} GB/s")
-
-    # ---- dominant kernel: events around each kernel of the decode call
-    nk = max(1, min(args.steps, 50))
-    # events bracket each kernel: route, gate/up, down + combine
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
-           for _ in range(nk)]
-    with torch.cuda.stream(stream):
-        for es in evs:              # torch creates the HIP event on first record
-            for el in es:
-                for e in el:
-                    e.record(stream)
-        step(0)
-        torch.cuda.synchronize()
-        for s in range(nk):
-            step(s, events=evs[s])
-        torch.cuda.synchronize()
-    dur = np.zeros((3,))  # route, gate/up, down+combine
-    gu_bytes_sum = 0.0
-    for s in range(nk):
-        for l in range(L):
-            e = evs[s][l]
-            for i in range(3):
-                dur[i] += e[2 * i].elapsed_time(e[2 * i + 1])
-            gu_bytes_sum += gu_launch_bytes[l, s % NX]
-    n_launch = nk * L
-    gu_ms = dur[1] / n_launch
-    gu_bytes = gu_bytes_sum / n_launch
-    achieved = gu_bytes / (gu_ms / 1e3) / 1e9
-    kus = dur / n_launch * 1e3
-    log(f"[bench] route {kus[0]:.2f} us, gate/up {kus[1]:.2f} us ({achieved:.0f} GB/s), "
-        f"down+combine {kus[2]:.2f} us")
+    head = bench_decode(spec, layers, R, args.steps, args.warmup, B, synth, torch, dev, stream, sleeper,
+                        graph=not args.no_graph)
+    workloads = {}
+    if not args.no_extra:
+        # one row through the same 40 layers (the one-row workload's shapes
+        # and formats, rotated over distinct weights so it is not cache-resident)
+        workloads["c0_1row_40layers"] = bench_decode(spec, layers, 1, args.steps, args.warmup, B, synth, torch,
+                                                    dev, stream, sleeper, graph=not args.no_graph,
+                                                    tag="decode-1row-q4g64 over 40 layers")
+    del layers
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        spec2 = synth.CONFIGS[2]
+        layers2, _ = build_layers(spec2, args.layers or spec2.layers, B, to_abi, synth)
+        for r2 in spec2.rows:
+            workloads[f"c2_{r2}rows"] = bench_decode(spec2, layers2, r2, args.steps, args.warmup, B, synth,
+                                                    torch, dev, stream, sleeper, graph=not args.no_graph)
+        del layers2
+        torch.cuda.empty_cache()
+    for name, r in prefill.items():
+        workloads[name] = r
 
     ceilings = measured_ceilings(torch, dev, stream)
-    log(f"[bench] measured ceilings: copy {ceilings['copy_1GiB_gbs']:.0f} GB/s, "
-        f"fp16 GEMM {ceilings['gemm_fp16_8192_tflops']:.0f} TFLOP/s")
+    log(f"[bench] measured ceiling: copy {ceilings['copy_1GiB_gbs']:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (fp64 oracle)")
-        cpu = cpu_baseline(spec, host[0], 64)
-        log(f"[bench] cpu baseline {cpu['value']:.3f} tokens/s")
+        nt = host_threads()
+        log(f"[bench] cpu baseline (fp64 oracle) on {nt} threads and on 1 thread")
+        cpu = cpu_decode_baseline(spec, host[0], 64, nt)
+        cpu["cpu_model"] = cpu_model()
+        cpu["one_thread"] = cpu_decode_baseline(spec, host[0], 64, 1)
+        pre = {}
+        for c, Lh in host_prefill.items():
+            if Lh is None:
+                continue
+            sp = synth.CONFIGS[c]
+            xb = synth.make_x(sp, 0, sp.rows[0], rep=0)
+            pre[f"c{c}"] = cpu_prefill_baseline(sp, Lh, xb, nt)
+        cpu["prefill"] = pre
+        log(f"[bench] cpu baseline: decode {cpu['value']:.2f} tokens/s ({nt} threads), "
+            f"{cpu['one_thread']['value']:.2f} (1 thread); "
+            + ", ".join(f"{k_} {v['value']:.1f} tokens/s" for k_, v in pre.items()))
 
     out = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -514,19 +762,17 @@ def main():
                    "experts": spec.n_experts, "top_k": k, "inter": spec.inter,
                    "shared_inter": spec.shared_inter, "weights": fmt_name(spec.routed),
                    "shared_weights": fmt_name(spec.shared), "router_weights": fmt_name(spec.router),
-                   "timing": "hip graph replay" if graphs else "eager"},
-        "roofline": {"bound": "hbm", "kernel": "k_dec_gateup", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic("k_dec_gateup") if default_workload else None, "mean_us": gu_ms * 1e3,
-                     "bytes_per_launch": gu_bytes},
-        "step_hbm": {"algorithmic_bytes": mean_step_bytes,
-                     "gbs": mean_step_bytes / ms_step / 1e6,
-                     "frac": mean_step_bytes / ms_step / 1e6 / HBM_PEAK_GBS,
-                     "us_per_layer": ms_step * 1e3 / L,
-                     "kernel_us": {"route": kus[0], "decode_gateup": kus[1],
-                                   "decode_down_combine": kus[2]},
-                     "mean_unique_experts": float(uniq.mean())},
-        "prefill": prefill,
+                   "timing": head["timing"]},
+        "roofline": {"bound": "hbm", "kernel": "k_dec_gateup", "achieved": head["gateup_gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["gateup_gbs"] / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("k_dec_gateup") if default_workload else None,
+                     "mean_us": head["kernel_us"]["decode_gateup"],
+                     "bytes_per_launch": head["gateup_bytes_per_launch"]},
+        "step_hbm": {"algorithmic_bytes": head["algorithmic_bytes_per_step"], "gbs": head["gbs"],
+                     "frac": head["frac_hbm"], "us_per_layer": head["us_per_layer"],
+                     "kernel_us": head["kernel_us"],
+                     "mean_unique_experts": head["mean_unique_experts"]},
+        "workloads": workloads,
         "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
     }

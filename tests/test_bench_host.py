@@ -69,3 +69,43 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_prefill_algorithmic_counts_unique_experts_once():
+    """A chunk's bytes: each selected expert's packed bytes once however many
+    rows pick it, plus shared expert, router, gate row, x in and fp32 y out;
+    flops per (row, slot), per row for the shared expert and the router."""
+    import numpy as np
+    spec = synth.CONFIGS[3]
+    ids = np.array([[0, 1, 2, 3, 4, 5, 6, 7], [7, 6, 5, 4, 3, 2, 1, 0], [8, 1, 2, 3, 4, 5, 6, 7]], np.int32)
+    a = bench.prefill_algorithmic(spec, ids)
+    gu, dn = bench.expert_bytes(spec, spec.routed, spec.inter)
+    H = spec.hidden
+    assert a["unique_experts"] == 9
+    assert a["bytes"] == 10 * (gu + dn) + bench.router_bytes(spec) + 3 * H * 2 + 3 * H * 4
+    assert a["flop_routed"] == 2 * 3 * H * 512 * 3 * 8
+    assert a["flop_shared"] == 2 * 3 * H * 512 * 3
+    assert a["flop_router"] == 2 * 257 * H * 3
+
+
+def test_host_threads_and_cpu_model():
+    assert bench.host_threads() >= 1
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_mfma_summary_formula(tmp_path):
+    """Busy fraction = MFMA busy cycles over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024
+    SIMDs; TFLOP/s = 512 flops per MOPS unit over the traced mean duration."""
+    pmc = tmp_path / "p_counter_collection.csv"
+    tr = tmp_path / "t_kernel_trace.csv"
+    k = "void moe::k_grp_gemm<0, 0, 0>(moe::GroupedArgs)"
+    pmc.write_text("Kernel_Name,Counter_Name,Counter_Value\n"
+                   f'"{k}",GRBM_GUI_ACTIVE,800000\n'
+                   f'"{k}",SQ_VALU_MFMA_BUSY_CYCLES,51200000\n'
+                   f'"{k}",SQ_INSTS_VALU_MFMA_MOPS_F16,1000000\n')
+    tr.write_text("Kernel_Name,Start_Timestamp,End_Timestamp\n" f'"{k}",1000,101000\n')
+    md = bench.mfma_summary(str(pmc), str(tr), ["cmd"])
+    row = [l for l in md.splitlines() if "k_grp_gemm" in l][0].split("|")
+    # 51.2e6 / (1e5 x 1024) = 0.5; 512e6 flop / 100 us = 5.12 TFLOP/s
+    assert row[-4].strip() == "0.500"
+    assert row[-3].strip() == "5.1"
