@@ -1,11 +1,13 @@
 // Grouped (prompt-chunk) path: the prefill form for chunks of many rows.
 //
 //  1. k_grp_sort: one workgroup sorts the slots (row r, pick j) by expert:
-//     per-wave expert histograms, an exclusive scan, and a scatter into
-//     expert-major order (the shared expert follows as expert E with every
-//     row). Lanes of a wave that hold the same expert are grouped by ballots,
-//     so one LDS atomic serves the group (the hot experts of a skewed chunk
-//     would otherwise serialise the wave). Then the work list: each expert's
+//     per-wave expert histograms (one LDS atomic per slot), an exclusive
+//     scan, and a scatter into expert-major order (the shared expert follows
+//     as expert E with every row). A slot's place inside its expert's run
+//     comes from the LDS atomic that counts it, so it can differ from call to
+//     call; nothing downstream depends on it (every row of an M-tile is
+//     computed from its own activations alone, and outputs go back to the
+//     slot's own place). Then the work list: each expert's
 //     run is cut into M-tiles of 128 rows, the last one 32, 64, 96 or 128
 //     rows tall; the list holds every 128-row tile first, then the 96-, 64-
 //     and 32-row ones, so the longest work starts first and the short tiles
@@ -72,27 +74,13 @@ __device__ __forceinline__ int wave_exclusive_scan(const int* in, int* out, int 
   return __shfl(inc, 63);
 }
 
-// The lanes of the wave whose expert id equals this lane's (ids < 512; only
-// valid lanes are counted; an invalid lane gets 0): one ballot per id bit.
-__device__ __forceinline__ uint64_t same_id_lanes(int e, bool valid) {
-  uint64_t m = __ballot(valid);
-#pragma unroll
-  for (int b = 0; b < 9; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t bb = __ballot(valid && bit);
-    m &= bit ? bb : ~bb;
-  }
-  return valid ? m : 0ull;
-}
-
 // Workgroup 0: the sort and the work list (1024 threads, 16 waves; wave w
 // owns the contiguous slot range [w S, (w+1) S), S = ceil(R k / 16)):
-//  1. per-wave expert histograms (one LDS atomic per group of lanes with the
-//     same expert);
+//  1. per-wave expert histograms (one LDS atomic per slot);
 //  2. exclusive scan over the experts (shared expert E with every row), then
 //     each wave's base per expert: the offset plus the earlier waves' counts;
-//  3. the same walk again scatters each slot to its position (the group's
-//     base plus the lane's rank in it), so positions are deterministic;
+//  3. the same walk again scatters each slot to the position its wave's
+//     running count for the expert returns;
 //  4. the work list of M-tiles (expert, first position, rows), 128-row tiles
 //     first, then 96-, 64- and 32-row ones, each class laid out by a scan
 //     over the experts; the queue counters of the two GEMMs are reset.
@@ -126,7 +114,6 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
   }
   const int E = a.E, k = a.k, R = a.R, nslot = R * k;
   const int S = (nslot + 15) / 16, s0 = w * S, s1 = min(nslot, s0 + S);
-  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   for (int q = tid; q < 16 * 258; q += 1024) (&wh[0][0])[q] = 0;
   __syncthreads();
   // 1. histograms (the ids of 16 rounds are loaded at once: one memory
@@ -141,9 +128,7 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int e = ev[q];
-      const bool valid = e >= 0 && e < E;
-      const uint64_t same = same_id_lanes(e, valid);
-      if (valid && (same & lt) == 0) atomicAdd(&wh[w][e], __popcll(same));
+      if (e >= 0 && e < E) atomicAdd(&wh[w][e], 1);
     }
   }
   __syncthreads();
@@ -191,13 +176,7 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
     for (int q = 0; q < 16; ++q) {
       const int i = bb + 64 * q + lane;
       const int e = ev[q];
-      const bool valid = e >= 0 && e < E;
-      const uint64_t same = same_id_lanes(e, valid);
-      const int leader = valid ? __ffsll((unsigned long long)same) - 1 : lane;
-      int base = 0;
-      if (valid && leader == lane) base = atomicAdd(&wh[w][e], __popcll(same));
-      base = __shfl(base, leader);
-      if (valid) a.perm[base + __popcll(same & lt)] = (i / k) * (k + 1) + i % k;
+      if (e >= 0 && e < E) a.perm[atomicAdd(&wh[w][e], 1)] = (i / k) * (k + 1) + i % k;
     }
   }
   for (int r = tid; r < R; r += 1024) a.perm[off[E] + r] = r * (k + 1) + k;
