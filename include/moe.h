@@ -58,16 +58,18 @@ enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1 };
  *       ("Sage-A1.5 ... on the XPU backend #1329", Proposal: affine 4/64 export)
  *   {3, 64, MOE_AFFINE, MOE_BF16}     MLX affine 3-bit, group 64 (routed/shared only)
  *       ("qwen3_5_moe on native CUDA with 3-bit routed experts #803", What I want to run)
- *   {8, 64, MOE_AFFINE, MOE_BF16}     MLX affine 8-bit, group 64 (router, gate row; experts
- *                                     on the decode path only: moe_experts_grouped refuses them)
+ *   {8, 64, MOE_AFFINE, MOE_BF16}     MLX affine 8-bit, group 64 (router, gate row, experts)
  *       (same page and section: routers and the shared-expert gate at 8 bits)
  *   {2, 64, MOE_AFFINE, MOE_BF16}     MLX affine 2-bit, group 64
  *   {5, 64, MOE_AFFINE, MOE_BF16}     MLX affine 5-bit, group 64
  *   {6, 64, MOE_AFFINE, MOE_BF16}     MLX affine 6-bit, group 64
- *                                     (these three: routed/shared only, on the decode path
- *                                     only: moe_experts_grouped refuses them; 5/6-bit experts
+ *                                     (these three: routed/shared only; 5/6-bit experts
  *                                     pair with a shared expert of the same width or 4-bit
  *                                     affine, other pairings are MOE_EUNSUPPORTED)
+ *       moe_experts_grouped reads the 3- and 4-bit expert formats in any pairing and
+ *       the 2-, 5-, 6- and 8-bit ones with a shared expert of the same width or 4-bit
+ *       affine; it refuses the other pairings the decode path reads
+ *       (MOE_EUNSUPPORTED, naming the pair; moe_forward_windows reads them)
  *       ("qwen3_5_moe on native CUDA with 3-bit routed experts #803", What exists on
  *       native: the loader reads MLX affine at 2 to 8 bits; Proposal and questions:
  *       affine experts at other widths)

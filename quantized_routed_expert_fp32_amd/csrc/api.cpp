@@ -298,13 +298,16 @@ int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const i
   int st = experts_common("moe_experts_grouped", layer, x, rows, ids, p, shared_gate, y, ws, 65536);
   if (st) return st;
   {
-    // the grouped GEMMs read 3- and 4-bit experts; the other widths are read
-    // by the decode kernels only
-    const int rb = layer->d.routed.bits, sb = layer->d.shared.bits;
-    const int wb = (rb != 3 && rb != 4) ? rb : (sb != 3 && sb != 4) ? sb : 0;
-    if (wb) {
-      set_error("moe_experts_grouped: " + std::to_string(wb) + "-bit experts are read by the decode kernels "
-                "only (moe_experts_decode, moe_forward_windows), not by the grouped GEMMs");
+    // the grouped GEMMs read the 3- and 4-bit formats in any pairing and
+    // the 2-, 5-, 6- and 8-bit ones with a shared expert of the same width
+    // or 4-bit affine
+    FmtInfo fr, fs;
+    if (!format_info(layer->d.routed, TC_ROUTED, &fr) || !format_info(layer->d.shared, TC_SHARED, &fs))
+      return MOE_EUNSUPPORTED;
+    if (!grouped_pair_supported(fr.kid, fs.kid)) {
+      set_error("moe_experts_grouped: routed " + fmt_name(layer->d.routed) + " with shared " +
+                fmt_name(layer->d.shared) + " is not read by the grouped GEMMs (a 2-, 5-, 6- or 8-bit routed "
+                "format needs a shared expert of the same width or 4-bit affine); moe_forward_windows reads it");
       return MOE_EUNSUPPORTED;
     }
   }

@@ -189,126 +189,6 @@ __device__ __forceinline__ f4v mfma4(uint32_t x0, uint32_t x1, uint32_t w0, uint
   }
 }
 
-// The pair unpack of one chunk for the matrix-core form: the same values
-// as unpack_for, written as plain code on masks the compiler cannot see as
-// constants, so it still selects one v_and_or_b32 per pair and, unlike for
-// inline asm, tracks the wait states a VALU write needs before a matrix-core
-// read of the same register.
-struct PairMasks {
-  uint32_t m, c, q0, q1, q2;   // field mask, 1.0 pair, 3-bit last-pair masks
-};
-template <int F, int ACT16>
-__device__ __forceinline__ PairMasks pair_masks() {
-  PairMasks k;
-  if constexpr (F == F_Q8) {
-    k.m = ACT16 ? 0x03FC03FCu : 0x00780078u;   // fp16: the byte; bf16: a nibble
-    k.q0 = k.q1 = k.q2 = 0u;
-  } else if constexpr (F == F_Q2) {
-    k.m = ACT16 ? 0x00C000C0u : 0x00180018u;
-    k.q0 = k.q1 = k.q2 = 0u;
-  } else if constexpr (F == F_Q5) {
-    k.m = ACT16 ? 0x03E003E0u : 0x007C007Cu;
-    k.q0 = k.q1 = k.q2 = 0u;
-  } else if constexpr (F == F_Q6) {
-    k.m = ACT16 ? 0x03F003F0u : 0x007E007Eu;
-    k.q0 = ACT16 ? 0x00F000F0u : 0x001E001Eu;   // low 4 bits of pairs 12..15
-    k.q1 = ACT16 ? 0x03000300u : 0x00600060u;   // their high 2 bits
-    k.q2 = 0u;
-  } else if constexpr (F == F_Q3) {
-    k.m = ACT16 ? 0x01C001C0u : 0x00380038u;
-    k.q0 = ACT16 ? 0x00400040u : 0x00080008u;
-    k.q1 = ACT16 ? 0x00800080u : 0x00100010u;
-    k.q2 = ACT16 ? 0x01000100u : 0x00200020u;
-  } else {
-    k.m = ACT16 ? 0x03C003C0u : 0x00780078u;
-    k.q0 = k.q1 = k.q2 = 0u;
-  }
-  k.c = ACT16 ? 0x3C003C00u : 0x3F803F80u;
-  asm volatile("" : "+s"(k.m), "+s"(k.q0), "+s"(k.q1), "+s"(k.q2), "+v"(k.c));
-  return k;
-}
-// 8-bit codes: with fp16 activations 16 pairs 1 + q/256; with bf16 ones
-// (7 mantissa bits) the low nibbles' 16 pairs in o[0..15] and the high
-// nibbles' in o[16..31], each 1 + n/16.
-template <int F, int ACT16>
-__device__ __forceinline__ void unpack_pairs(const uint32_t* w, const PairMasks& k, uint32_t* o) {
-  if constexpr (F == F_Q8) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t v = w[i];
-      if constexpr (ACT16) {
-        o[2 * i] = ((v << 2) & k.m) | k.c;
-        o[2 * i + 1] = ((v >> 6) & k.m) | k.c;
-      } else {
-        o[2 * i] = ((v << 3) & k.m) | k.c;
-        o[2 * i + 1] = ((v >> 5) & k.m) | k.c;
-        o[16 + 2 * i] = ((v >> 1) & k.m) | k.c;
-        o[16 + 2 * i + 1] = ((v >> 9) & k.m) | k.c;
-      }
-    }
-  } else if constexpr (F == F_Q2) {
-    // pair j of word i at bits 2j: moved to mantissa bit 6 (fp16) or 3 (bf16)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t v = w[i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        constexpr int T = ACT16 ? 6 : 3;
-        const uint32_t sv = 2 * j <= T ? v << (T - 2 * j) : v >> (2 * j - T);
-        o[8 * i + j] = (sv & k.m) | k.c;
-      }
-    }
-  } else if constexpr (F == F_Q5) {
-    // value 1 + q/32: code bit 0 to mantissa bit 5 (fp16) or 2 (bf16)
-    constexpr int T = ACT16 ? 5 : 2;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const uint32_t v = w[i];
-      o[3 * i + 0] = ((v << T) & k.m) | k.c;
-      o[3 * i + 1] = ((ACT16 ? v : v >> 3) & k.m) | k.c;
-      o[3 * i + 2] = ((v >> (10 - T)) & k.m) | k.c;
-    }
-    uint32_t t = k.c;
-#pragma unroll
-    for (int b = 0; b < 5; ++b) t |= (w[b] >> (15 - T - b)) & (0x00010001u << (T + b));
-    o[15] = t;
-  } else if constexpr (F == F_Q6) {
-    // value 1 + q/64: code bit 0 to mantissa bit 4 (fp16) or 1 (bf16)
-    constexpr int T = ACT16 ? 4 : 1;
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const uint32_t v = w[i];
-      o[2 * i + 0] = ((v << T) & k.m) | k.c;
-      o[2 * i + 1] = ((v >> (6 - T)) & k.m) | k.c;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      o[12 + m] = ((w[4 + m / 2] >> (8 + 2 * (m % 2) - T)) & k.q1) | (((w[m] >> (12 - T)) & k.q0) | k.c);
-  } else if constexpr (F == F_Q3) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const uint32_t v = w[i];
-      o[5 * i + 0] = ((ACT16 ? v << 6 : v << 3) & k.m) | k.c;
-      o[5 * i + 1] = ((ACT16 ? v << 3 : v) & k.m) | k.c;
-      o[5 * i + 2] = ((ACT16 ? v : v >> 3) & k.m) | k.c;
-      o[5 * i + 3] = ((ACT16 ? v >> 3 : v >> 6) & k.m) | k.c;
-      o[5 * i + 4] = ((ACT16 ? v >> 6 : v >> 9) & k.m) | k.c;
-    }
-    const uint32_t t0 = ((w[0] >> (ACT16 ? 9 : 12)) & k.q0) | k.c;
-    const uint32_t t1 = ((w[1] >> (ACT16 ? 8 : 11)) & k.q1) | t0;
-    o[15] = ((w[2] >> (ACT16 ? 7 : 10)) & k.q2) | t1;
-  } else {   // 4-bit affine or symmetric
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t v = w[i];
-      o[4 * i + 0] = ((ACT16 ? v << 6 : v << 3) & k.m) | k.c;
-      o[4 * i + 1] = ((ACT16 ? v << 2 : v >> 1) & k.m) | k.c;
-      o[4 * i + 2] = ((ACT16 ? v >> 2 : v >> 5) & k.m) | k.c;
-      o[4 * i + 3] = ((ACT16 ? v >> 6 : v >> 9) & k.m) | k.c;
-    }
-  }
-}
-
 template <int F, int ACT16, int W>
 __device__ __forceinline__ f4v gu_slice_mfma(const uint32_t (*w)[W], const uint32_t* sc, const uint32_t* xr,
                                              const float* xs0, const float* xs1, const float* xs2,

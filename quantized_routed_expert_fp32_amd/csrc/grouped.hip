@@ -45,7 +45,6 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 // meta layout (int32): [0] M-tiles in the work list, [1] gate/up queue
 // counter, [2] down queue counter, [8 .. E+10) expert offsets (E+2 entries)
 constexpr int META_OFF = 8;
-constexpr int GEMM_WG_PER_CU = 2;
 
 // ------------------------------------------------------------------ sort
 // Exclusive prefix sum of n <= 320 LDS counters by one wave (lane l owns
@@ -242,12 +241,28 @@ __device__ __forceinline__ void deq_word<F_S4>(const uint32_t* wv, half2v s16, h
   for (int i = 0; i < 4; ++i) o[i] = as_u((as_h2(p[i]) - off) * s16);
 }
 
-// For the 3-bit layout, the 8 codes k = 8v..8v+7 of a chunk (v = 0..3) sit
-// in pairs 4v..4v+3; the chunk's full unpack gives them.
+// Widths read through the generic B layout (the chunk block copied to LDS
+// as it is packed, every lane unpacking its row's whole chunk).
+template <int F> constexpr bool gen_fmt() { return F == F_Q2 || F == F_Q5 || F == F_Q6 || F == F_Q8; }
+
+// For the 3-bit layout and the generic widths, the 8 codes k = 8v..8v+7 of
+// a chunk (v = 0..3) sit in pairs 4v..4v+3 of the chunk's full unpack.
 template <int F>
 __device__ __forceinline__ void deq_chunk_half(const uint32_t* cw, int wsel, half2v s16, half2v b2,
                                                uint32_t* o) {
-  if constexpr (F == F_Q3) {
+  if constexpr (gen_fmt<F>()) {
+    // pairs 1 + q/M of the whole chunk, then the 4 of this lane's k range
+    uint32_t v[16];
+    unpack_pairs<F, 1>(cw, pair_masks<F, 1>(), v);
+    const half2v one = {(f16)1.0f, (f16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t pv = v[i];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) pv = (wsel == q) ? v[4 * q + i] : pv;
+      o[i] = as_u(__builtin_elementwise_fma(as_h2(pv) - one, s16, b2));
+    }
+  } else if constexpr (F == F_Q3) {
     uint32_t v[16];
     unpack_chunk<F_Q3>(cw, v);   // 1 + q/16 pairs
     const half2v one = {(f16)1.0f, (f16)1.0f};
@@ -277,9 +292,26 @@ enum { GU = 0, DN = 1 };
 // one step ahead.
 constexpr int NST = 3;
 constexpr int A_STAGE = 128 * 64;        // halves of the A tile of one step
-constexpr int B_WAVE = 2 * 1024 + 256;   // bytes of one wave's B area (codes of 2 chunks, scale words)
-constexpr int STAGE_BYTES = 2 * A_STAGE + 4 * B_WAVE;
-constexpr int B_LOADS = 3;               // B loads per thread and step: 2 chunk blocks, 1 scale word
+
+// LDS bytes of one chunk block (64 weight rows of one 32-k chunk): 12-byte
+// rows land at a 16-byte lane stride, the generic widths keep the packed
+// layout (64 rows of CB bytes, see row_word).
+template <int F> constexpr int chunk_lds() { return gen_fmt<F>() ? 64 * Fmt<F>::CB : 1024; }
+// Word q of weight row r inside a chunk block as packed: rows of CB bytes
+// one after another, except 8-bit rows, whose first and second 16 bytes sit
+// in two 1 KiB halves of the block (rows 0..63 each).
+template <int F> __device__ __forceinline__ int row_word(int r, int q) {
+  if constexpr (F == F_Q8) return (q >> 2) * 256 + 4 * r + (q & 3);
+  else return r * Fmt<F>::WORDS + q;
+}
+// One wave's B area: the codes of 2 chunk blocks, then the 64 rows' scale words.
+template <int F> constexpr int b_scale_off() { return 2 * chunk_lds<F>(); }
+template <int F> constexpr int b_wave() { return b_scale_off<F>() + 256; }
+// B loads per thread and step: 2 chunk blocks (one load each, or CB / 4
+// loads of 4 bytes each for the generic widths) and 1 scale word.
+template <int F> constexpr int b_loads() { return gen_fmt<F>() ? 2 * (Fmt<F>::CB / 4) + 1 : 3; }
+template <int FR, int FS> constexpr int stage_b_wave() { return b_wave<FR>() > b_wave<FS>() ? b_wave<FR>() : b_wave<FS>(); }
+template <int FR, int FS> constexpr int stage_bytes() { return 2 * A_STAGE + 4 * stage_b_wave<FR, FS>(); }
 
 // 4-bit codes: the lane of half hsel takes words 2 hsel, 2 hsel + 1 of each
 // chunk row (8 contiguous bytes), i.e. k = 16 hsel .. 16 hsel + 15 of the
@@ -316,7 +348,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // together read distinct bank groups.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// The B loads of one step into the wave's area bw (exactly B_LOADS loads:
+// The B loads of one step into the wave's area bw (exactly b_loads<F>() loads:
 // the wait counts rely on it): lane l copies row l of the layout tile's two
 // chunk blocks (CB bytes each) and row l's scale word: affine, the (s, b)
 // word of the step's group; symmetric, the word holding both fp16 scales of
@@ -330,17 +362,28 @@ __device__ __forceinline__ void issue_b(uint8_t* bw, const uint8_t* blk, uint32_
   constexpr int GPS = KBLK / Fmt<F>::G, CB = Fmt<F>::CB;
   const int kk0 = 64 * step;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-    __builtin_amdgcn_global_load_lds(blk + codes + chunk_off<F>(T, kk0 / 32 + c, nch) + lane * CB,
-                                     (__attribute__((address_space(3))) void*)(bw + 1024 * c), CB, 0, 0);
+  for (int c = 0; c < 2; ++c) {
+    if constexpr (gen_fmt<F>()) {
+      // the chunk block as packed: CB / 4 pieces of 256 bytes, a dword a lane
+#pragma unroll
+      for (int q = 0; q < CB / 4; ++q)
+        __builtin_amdgcn_global_load_lds(blk + codes + chunk_off<F>(T, kk0 / 32 + c, nch) + 256 * q + 4 * lane,
+                                         (__attribute__((address_space(3))) void*)(bw + chunk_lds<F>() * c + 256 * q),
+                                         4, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds(blk + codes + chunk_off<F>(T, kk0 / 32 + c, nch) + lane * CB,
+                                       (__attribute__((address_space(3))) void*)(bw + 1024 * c), CB, 0, 0);
+    }
+  }
   const uint8_t* sb = blk + scales + sblk_off<F>(T, kk0 / KBLK, nkb);
   if constexpr (Fmt<F>::AFF) {
     const int gi = (kk0 % KBLK) / Fmt<F>::G;
-    __builtin_amdgcn_global_load_lds(sb + (lane * GPS + gi) * 4, (__attribute__((address_space(3))) void*)(bw + 2048),
-                                     4, 0, 0);
+    __builtin_amdgcn_global_load_lds(sb + (lane * GPS + gi) * 4,
+                                     (__attribute__((address_space(3))) void*)(bw + b_scale_off<F>()), 4, 0, 0);
   } else {
     static_assert(GPS == 2, "two fp16 scales per row and block");
-    __builtin_amdgcn_global_load_lds(sb + lane * 4, (__attribute__((address_space(3))) void*)(bw + 2048), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(sb + lane * 4, (__attribute__((address_space(3))) void*)(bw + b_scale_off<F>()),
+                                     4, 0, 0);
   }
 #endif
 }
@@ -381,7 +424,21 @@ typedef uint32_t v3u __attribute__((ext_vector_type(3)));
 template <int F>
 __device__ __forceinline__ void read_b(BStage<F>& st, uint32_t bw, int col, int hsel, int step) {
   uint32_t s0, s1;
-  if constexpr (BFrag<F>::HALF) {
+  if constexpr (gen_fmt<F>()) {
+    // generic widths: plain LDS reads of the two rows' whole chunks (the
+    // compiler waits for every load to LDS in flight before them)
+    typedef const __attribute__((address_space(3))) uint32_t* lds_u32;
+    const lds_u32 b = (lds_u32)(uintptr_t)bw;
+    constexpr int WD = Fmt<F>::WORDS, CW = chunk_lds<F>() / 4;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q = 0; q < WD; ++q) st.w[nt][c][q] = b[c * CW + row_word<F>(col + 32 * nt, q)];
+    s0 = b[b_scale_off<F>() / 4 + col];
+    s1 = b[b_scale_off<F>() / 4 + 32 + col];
+  } else if constexpr (BFrag<F>::HALF) {
     const uint32_t ac = bw + col * 16 + 8 * hsel;
     v2u c00, c10, c01, c11;
     if constexpr (Fmt<F>::AFF) {
@@ -473,7 +530,7 @@ __device__ __forceinline__ void step_mma(f16v_t (&acc)[MT][2], const BStage<F>& 
       sc = f16_bits_to_f(st.sr[nt] & 0xFFFFu);
       bi = 0.f;
     }
-    const f16 sh = (f16)(16.0f * sc), bh = (f16)bi;
+    const f16 sh = (f16)((float)Fmt<F>::M * sc), bh = (f16)bi;   // M s: pairs hold 1 + q/M
     s16[nt] = {sh, sh};
     b2[nt] = {bh, bh};
   }
@@ -510,7 +567,7 @@ __device__ __forceinline__ void step_mma(f16v_t (&acc)[MT][2], const BStage<F>& 
 // t + 1 refill, is no longer read). __syncthreads would add a release fence,
 // which waits for every load to LDS in flight, the prefetched stage
 // included.
-template <int F, int MODE, int MT>
+template <int F, int MODE, int MT, int BW>
 __device__ __forceinline__ void gemm_item(const GroupedArgs& a, int e, int m0, int mc, int nb, uint8_t* const (&stg)[NST],
                                           int* slot_l) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -550,7 +607,7 @@ __device__ __forceinline__ void gemm_item(const GroupedArgs& a, int e, int m0, i
   const int steps = K / 64;   // a multiple of 4 (K is a multiple of 256)
   uint8_t* bw[NST];
 #pragma unroll
-  for (int q = 0; q < NST; ++q) bw[q] = stg[q] + 2 * A_STAGE + B_WAVE * w;
+  for (int q = 0; q < NST; ++q) bw[q] = stg[q] + 2 * A_STAGE + BW * w;
   issue_a<MT>(asrc, reinterpret_cast<uint16_t*>(stg[0]), w, 0);
   issue_b<F>(bw[0], blk, codes, scales, T, nch, nkb, lane, 0);
   for (int base = 0; base < steps; base += NST) {
@@ -564,7 +621,7 @@ __device__ __forceinline__ void gemm_item(const GroupedArgs& a, int e, int m0, i
       issue_a<MT>(asrc, reinterpret_cast<uint16_t*>(stg[(s + 1) % NST]), w, tn);
       issue_b<F>(bw[(s + 1) % NST], blk, codes, scales, T, nch, nkb, lane, tn);
       asm volatile("" ::: "memory");
-      wait_vm<MT + B_LOADS>();
+      wait_vm<MT + b_loads<F>()>();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -611,25 +668,31 @@ __device__ __forceinline__ void gemm_item(const GroupedArgs& a, int e, int m0, i
   }
 }
 
-template <int F, int MODE>
+template <int F, int MODE, int BW>
 __device__ __forceinline__ void gemm_item_mt(const GroupedArgs& a, int e, int m0, int mc, int nb,
                                              uint8_t* const (&stg)[NST], int* slot_l) {
   switch ((mc + 31) >> 5) {
-    case 4: gemm_item<F, MODE, 4>(a, e, m0, mc, nb, stg, slot_l); break;
-    case 3: gemm_item<F, MODE, 3>(a, e, m0, mc, nb, stg, slot_l); break;
-    case 2: gemm_item<F, MODE, 2>(a, e, m0, mc, nb, stg, slot_l); break;
-    default: gemm_item<F, MODE, 1>(a, e, m0, mc, nb, stg, slot_l); break;
+    case 4: gemm_item<F, MODE, 4, BW>(a, e, m0, mc, nb, stg, slot_l); break;
+    case 3: gemm_item<F, MODE, 3, BW>(a, e, m0, mc, nb, stg, slot_l); break;
+    case 2: gemm_item<F, MODE, 2, BW>(a, e, m0, mc, nb, stg, slot_l); break;
+    default: gemm_item<F, MODE, 1, BW>(a, e, m0, mc, nb, stg, slot_l); break;
   }
+}
+
+// Workgroups per CU the LDS ring allows (two when three stages fit twice).
+template <int FR, int FS> constexpr int gemm_wg_per_cu() {
+  return 2 * (NST * stage_bytes<FR, FS>() + 1024) <= 160 * 1024 ? 2 : 1;
 }
 
 // Persistent workgroups: each takes items q = (M-tile q / nblk, column block
 // q % nblk) from the queue counter until the list is done. The work list is
 // ordered by tile height, so the long items start first.
 template <int FR, int FS, int MODE>
-__global__ __launch_bounds__(256, GEMM_WG_PER_CU) void k_grp_gemm(GroupedArgs a) {
-  __shared__ __align__(16) uint8_t stg0[STAGE_BYTES];
-  __shared__ __align__(16) uint8_t stg1[STAGE_BYTES];
-  __shared__ __align__(16) uint8_t stg2[STAGE_BYTES];
+__global__ __launch_bounds__(256, (gemm_wg_per_cu<FR, FS>())) void k_grp_gemm(GroupedArgs a) {
+  constexpr int SB = stage_bytes<FR, FS>(), BW = stage_b_wave<FR, FS>();
+  __shared__ __align__(16) uint8_t stg0[SB];
+  __shared__ __align__(16) uint8_t stg1[SB];
+  __shared__ __align__(16) uint8_t stg2[SB];
   uint8_t* const stg[NST] = {stg0, stg1, stg2};
   __shared__ int slot_l[128];
   __shared__ int s_item[2];
@@ -652,8 +715,8 @@ __global__ __launch_bounds__(256, GEMM_WG_PER_CU) void k_grp_gemm(GroupedArgs a)
     const int I = shared ? a.sh.inter : a.rt.inter;
     const int nlt = MODE == GU ? 2 * I / 64 : a.H / 64;
     if (nb * 4 >= nlt) continue;
-    if (shared) gemm_item_mt<FS, MODE>(a, e, m0, mc, nb, stg, slot_l);
-    else gemm_item_mt<FR, MODE>(a, e, m0, mc, nb, stg, slot_l);
+    if (shared) gemm_item_mt<FS, MODE, BW>(a, e, m0, mc, nb, stg, slot_l);
+    else gemm_item_mt<FR, MODE, BW>(a, e, m0, mc, nb, stg, slot_l);
   }
 }
 
@@ -689,16 +752,16 @@ __global__ __launch_bounds__(256) void k_grp_combine(GroupedArgs a) {
 }
 
 // ------------------------------------------------------------------ launch
-static int gemm_grid() {
+static int gemm_grid(int wg_per_cu) {
   static int cus[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * GEMM_WG_PER_CU;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * wg_per_cu;
   if (!cus[dev]) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
     cus[dev] = n;
   }
-  return cus[dev] * GEMM_WG_PER_CU;
+  return cus[dev] * wg_per_cu;
 }
 
 template <int FR, int FS>
@@ -709,7 +772,7 @@ static hipError_t launch_grouped_t(const GroupedArgs& a, hipStream_t s, hipEvent
   launch_k(k_grp_sort, dim3(1 + nconv), dim3(1024), 0, s, ev, 0, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int G = gemm_grid();
+  const int G = gemm_grid(gemm_wg_per_cu<FR, FS>());
   launch_k(k_grp_gemm<FR, FS, GU>, dim3(G), dim3(256), 0, s, ev, 2, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   launch_k(k_grp_gemm<FR, FS, DN>, dim3(G), dim3(256), 0, s, ev, 4, a);
@@ -719,14 +782,28 @@ static hipError_t launch_grouped_t(const GroupedArgs& a, hipStream_t s, hipEvent
   return hipGetLastError();
 }
 
+// Routed / shared format pairs the grouped GEMMs read: the 3- and 4-bit
+// formats in any pairing, the other widths with a shared expert of the same
+// width or 4-bit affine.
 template <int FR>
 static hipError_t launch_grouped_s(int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
-  switch (fs) {
-    case F_Q4: return launch_grouped_t<FR, F_Q4>(a, s, ev);
-    case F_Q3: return launch_grouped_t<FR, F_Q3>(a, s, ev);
-    case F_S4: return launch_grouped_t<FR, F_S4>(a, s, ev);
+  if constexpr (FR == F_Q4 || FR == F_Q3 || FR == F_S4) {
+    switch (fs) {
+      case F_Q4: return launch_grouped_t<FR, F_Q4>(a, s, ev);
+      case F_Q3: return launch_grouped_t<FR, F_Q3>(a, s, ev);
+      case F_S4: return launch_grouped_t<FR, F_S4>(a, s, ev);
+    }
+  } else {
+    if (fs == FR) return launch_grouped_t<FR, FR>(a, s, ev);
+    if (fs == F_Q4) return launch_grouped_t<FR, F_Q4>(a, s, ev);
   }
   return hipErrorInvalidValue;
+}
+
+bool grouped_pair_supported(int fr, int fs) {
+  const bool low = [](int f) { return f == F_Q4 || f == F_Q3 || f == F_S4; }(fr);
+  if (low) return fs == F_Q4 || fs == F_Q3 || fs == F_S4;
+  return (fr == F_Q2 || fr == F_Q5 || fr == F_Q6 || fr == F_Q8) && (fs == fr || fs == F_Q4);
 }
 
 hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
@@ -734,6 +811,10 @@ hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s, h
     case F_Q4: return launch_grouped_s<F_Q4>(fs, a, s, ev);
     case F_Q3: return launch_grouped_s<F_Q3>(fs, a, s, ev);
     case F_S4: return launch_grouped_s<F_S4>(fs, a, s, ev);
+    case F_Q2: return launch_grouped_s<F_Q2>(fs, a, s, ev);
+    case F_Q5: return launch_grouped_s<F_Q5>(fs, a, s, ev);
+    case F_Q6: return launch_grouped_s<F_Q6>(fs, a, s, ev);
+    case F_Q8: return launch_grouped_s<F_Q8>(fs, a, s, ev);
   }
   return hipErrorInvalidValue;
 }

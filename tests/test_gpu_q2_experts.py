@@ -7,8 +7,8 @@ other than 4 beside the 4-bit form ("qwen3_5_moe on native CUDA with 3-bit
 routed experts #803", What exists on native; Proposal and questions). The
 decode kernels read them as pairs 1 + q/16, the 4-bit pair value, so the
 control is the pages' own kind: the same codes widened to 4-bit words give
-the same bytes. The grouped GEMMs refuse them by name and moe_forward_windows
-serves prompt rows exactly. Layers: the full-size decode layer with 2-bit
+the same bytes. moe_forward_windows serves prompt rows exactly (the grouped
+GEMMs' parity at this width is in test_gpu_grouped_widths.py). Layers: the full-size decode layer with 2-bit
 routed and shared experts (bf16 and fp16 activations), a mixed one (2-bit
 routed, 4-bit shared) and a small one (H=512, E=64, k=4).
 """
@@ -111,15 +111,12 @@ def test_q2_equals_widened_4bit_bit_for_bit(act16):
     check_parity(Lh2, xb, a, name=f"q2-widened-{act16}", strict_y=1e-4)
 
 
-def test_q2_experts_grouped_refused_windows_served():
+def test_q2_experts_windows_served():
     B = binding()
     torch = torch_mod()
     Lh, dev, dense = layer_of(FULL_Q2)
     xb = synth.make_x(FULL_Q2, 0, 20, rep=3)
     x = to_dev_x(xb)
-    ids, p, sg = B.route(dev, x)
-    with pytest.raises(B.MoeError, match="2-bit experts"):
-        B.experts(dev, x, ids, p, sg, True)
     ids, p, sg, y = B.forward_windows(dev, x)
     torch.cuda.synchronize()
     g = dict(ids=ids.cpu().numpy(), p=p.cpu().numpy(), sg=sg.cpu().numpy(), y=y.cpu().numpy())

@@ -6,8 +6,9 @@ reads, and the proposal there adds affine experts at widths other than 4
 beside the 4-bit form ("qwen3_5_moe on native CUDA with 3-bit routed experts
 #803", the issue's "Affine experts at other widths" proposal). The decode kernels
 read them (with bf16 activations as low and high nibble pairs, with fp16
-ones as one pair set); the grouped GEMMs refuse them by name, and
-moe_forward_windows serves prompt rows exactly. Layers: the full-size decode
+ones as one pair set), and moe_forward_windows serves prompt rows exactly
+(the grouped GEMMs' parity at this width is in test_gpu_grouped_widths.py).
+Layers: the full-size decode
 layer with 8-bit routed and shared experts (bf16 and fp16 activations), a
 mixed one (8-bit routed, 4-bit shared) and a small one (H=512, E=64, k=4).
 """
@@ -68,15 +69,12 @@ def test_q8_experts_batch_equals_solo_bit_for_bit(spec):
             assert np.array_equal(u, v), f"row {r} {key} differs"
 
 
-def test_q8_experts_grouped_refused_windows_served():
+def test_q8_experts_windows_served():
     B = binding()
     torch = torch_mod()
     Lh, dev, dense = layer_of(FULL_Q8)
     xb = synth.make_x(FULL_Q8, 0, 20, rep=3)
     x = to_dev_x(xb)
-    ids, p, sg = B.route(dev, x)
-    with pytest.raises(B.MoeError, match="8-bit experts"):
-        B.experts(dev, x, ids, p, sg, True)
     ids, p, sg, y = B.forward_windows(dev, x)
     torch.cuda.synchronize()
     g = dict(ids=ids.cpu().numpy(), p=p.cpu().numpy(), sg=sg.cpu().numpy(), y=y.cpu().numpy())

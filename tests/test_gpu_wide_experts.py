@@ -9,8 +9,9 @@ native; Proposal and questions). The decode kernels read them as pairs
 halves hold whole fields for most pairs and the rest in the spare bits (see
 the kernel layout notes). Layers: full-size decode layers with 5-bit and
 6-bit routed and shared experts (bf16 and fp16 activations), 6-bit routed
-beside a 4-bit shared expert, and small ones (H=512, E=64, k=4). The grouped
-GEMMs refuse these widths by name and moe_forward_windows serves prompt rows.
+beside a 4-bit shared expert, and small ones (H=512, E=64, k=4). Prompt rows
+through moe_forward_windows here; the grouped GEMMs' parity at these widths is
+in test_gpu_grouped_widths.py.
 """
 from dataclasses import replace
 
@@ -76,15 +77,12 @@ def test_wide_experts_batch_equals_solo_bit_for_bit(spec):
 
 
 @pytest.mark.parametrize("spec", [FULL_Q5, MIXED_Q6], ids=["q5", "q6-mixed"])
-def test_wide_experts_grouped_refused_windows_served(spec):
+def test_wide_experts_windows_served(spec):
     B = binding()
     torch = torch_mod()
     Lh, dev, dense = layer_of(spec)
     xb = synth.make_x(spec, 0, 20, rep=3)
     x = to_dev_x(xb)
-    ids, p, sg = B.route(dev, x)
-    with pytest.raises(B.MoeError, match=f"{spec.routed.bits}-bit experts"):
-        B.experts(dev, x, ids, p, sg, True)
     ids, p, sg, y = B.forward_windows(dev, x)
     torch.cuda.synchronize()
     g = dict(ids=ids.cpu().numpy(), p=p.cpu().numpy(), sg=sg.cpu().numpy(), y=y.cpu().numpy())
