@@ -14,7 +14,9 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIBRARY names another build of the same library (the host-only
+# sanitizer flavour of the host tests); it must exist like the default one
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
 
 MOE_AFFINE, MOE_SYMMETRIC, MOE_DENSE = 0, 1, 2
 MOE_BF16, MOE_FP16 = 0, 1

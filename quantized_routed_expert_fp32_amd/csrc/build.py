@@ -1,6 +1,11 @@
 """Builds libmoe.so (HIP kernels for gfx950 + host C ABI) in-tree.
 
     python -m quantized_routed_expert_fp32_amd.csrc.build   (or build())
+
+build_host_sanitized() builds _build/libmoe_hostsan.so: the host sources
+(packer, layout arithmetic, C ABI validation) with AddressSanitizer and
+UndefinedBehaviorSanitizer and the device entry points replaced by refusals
+(host_stubs.cpp), for running the host tests sanitised without a GPU.
 """
 import os
 import shutil
@@ -50,6 +55,31 @@ def build(verbose=False):
     if verbose:
         print("built", OUT)
     return OUT
+
+
+SAN_OUT = os.path.join(BUILD, "libmoe_hostsan.so")
+SAN_FLAGS = ["-O1", "-g", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(verbose=False):
+    """The host-only sanitizer flavour (g++ only, no GPU code)."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    jobs = []
+    for s in CXX_SOURCES + ["host_stubs.cpp"]:
+        o = os.path.join(BUILD, "san_" + s.replace(".cpp", ".o"))
+        objs.append(o)
+        jobs.append(["g++", *SAN_FLAGS, "-c", os.path.join(HERE, s), "-o", o])
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        list(ex.map(_run, jobs))
+    tmp = SAN_OUT + ".tmp"
+    _run(["g++", "-shared", "-fsanitize=address,undefined", "-o", tmp, *objs, f"-L{ROCM}/lib", "-lamdhip64",
+          "-lpthread"])
+    os.replace(tmp, SAN_OUT)
+    if verbose:
+        print("built", SAN_OUT)
+    return SAN_OUT
 
 
 if __name__ == "__main__":

@@ -782,9 +782,9 @@ static hipError_t launch_grouped_t(const GroupedArgs& a, hipStream_t s, hipEvent
   return hipGetLastError();
 }
 
-// Routed / shared format pairs the grouped GEMMs read: the 3- and 4-bit
-// formats in any pairing, the other widths with a shared expert of the same
-// width or 4-bit affine.
+// Routed / shared format pairs the grouped GEMMs read (grouped_pair_supported):
+// the 3- and 4-bit formats in any pairing, the other widths with a shared
+// expert of the same width or 4-bit affine.
 template <int FR>
 static hipError_t launch_grouped_s(int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
   if constexpr (FR == F_Q4 || FR == F_Q3 || FR == F_S4) {
@@ -798,12 +798,6 @@ static hipError_t launch_grouped_s(int fs, const GroupedArgs& a, hipStream_t s, 
     if (fs == F_Q4) return launch_grouped_t<FR, F_Q4>(a, s, ev);
   }
   return hipErrorInvalidValue;
-}
-
-bool grouped_pair_supported(int fr, int fs) {
-  const bool low = [](int f) { return f == F_Q4 || f == F_Q3 || f == F_S4; }(fr);
-  if (low) return fs == F_Q4 || fs == F_Q3 || fs == F_S4;
-  return (fr == F_Q2 || fr == F_Q5 || fr == F_Q6 || fr == F_Q8) && (fs == fr || fs == F_Q4);
 }
 
 hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {

@@ -73,7 +73,5 @@ struct GroupedArgs {
 hipError_t launch_route(int fr, int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev);
-// The routed / shared kernel-side format pair the grouped GEMMs read.
-bool grouped_pair_supported(int fr, int fs);
 
 }  // namespace moe

@@ -68,6 +68,12 @@ bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* o) {
   return ok;
 }
 
+bool grouped_pair_supported(int fr, int fs) {
+  const auto low = [](int f) { return f == KF_Q4 || f == KF_Q3 || f == KF_S4; };
+  if (low(fr)) return low(fs);
+  return (fr == KF_Q2 || fr == KF_Q5 || fr == KF_Q6 || fr == KF_Q8) && (fs == fr || fs == KF_Q4);
+}
+
 int validate_desc(const moe_layer_desc* d) {
   if (!d) { set_error("layer descriptor is NULL"); return MOE_EINVAL; }
   char buf[256];
