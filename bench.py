@@ -311,6 +311,30 @@ def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream, s
         "rows_per_expert": {"max": int(cnt.max()), "mean": float(cnt.mean()),
                             "empty": int((cnt == 0).sum())},
     }
+    # the exact chunk form (moe_forward_exact: every row with its one-row
+    # decode step's bits), timed as graph replays over the same weight sets
+    xws = B.new_workspace(layers[0], R, B.MOE_WS_EXACT, dev, stream=stream)
+    y2 = torch.empty_like(y)
+    with torch.cuda.stream(stream):
+        B.forward_exact(layers[0], xs[0], biases[0], ws=xws, out=(ids, p, sg), y=y2, stream=stream)
+        torch.cuda.synchronize()
+        xgraphs = []
+        for l in range(n_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                B.forward_exact(layers[l], xs[l], biases[l], ws=xws, out=(ids, p, sg), y=y2, stream=stream)
+            xgraphs.append(g)
+        for i in range(warmup):
+            xgraphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(steps):
+            xgraphs[i % n_sets].replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+    res["exact_us_per_chunk"] = t0.elapsed_time(t1) / steps * 1e3
+    res["exact_over_grouped"] = res["exact_us_per_chunk"] / us
+    del xgraphs, xws
     if windows:
         # the same chunk through the decode step's arithmetic in 16-row windows
         # (moe_forward_windows: same bits however the prompt is cut), eager
@@ -329,6 +353,7 @@ def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream, s
         f"{res['tokens_per_s']:.0f} tokens/s, {res['gbs']:.0f} GB/s ({100 * res['frac_hbm']:.1f}% of HBM), "
         f"{res['tflops']:.1f} TFLOP/s ({100 * res['frac_mfma']:.1f}% of f16 MFMA); "
         + ", ".join(f"{k_} {v:.1f}" for k_, v in res["phase_us"].items())
+        + f"; exact form {res['exact_us_per_chunk']:.1f} us/chunk ({res['exact_over_grouped']:.2f}x grouped)"
         + (f"; 16-row windows {res['windows_us_per_chunk']:.1f} us/chunk" if windows else ""))
     del graphs, ws
     return res, host

@@ -190,8 +190,12 @@ int moe_layer_bind(moe_layer* layer, const void* dev_ptr);
 int moe_pack_layer(const moe_layer_desc* d, const moe_layer_src* src,
                    void* dev_dst, uint64_t dst_bytes, void* stream, moe_layer* out);
 
-/* Workspace bytes for moe_route plus moe_experts_decode (grouped = 0) or
- * plus moe_experts_grouped (grouped = 1) at `rows` rows. One buffer of this
+/* Workspace kinds of moe_workspace_size. */
+enum moe_ws_kind { MOE_WS_DECODE = 0, MOE_WS_GROUPED = 1, MOE_WS_EXACT = 2 };
+
+/* Workspace bytes for moe_route plus moe_experts_decode (grouped =
+ * MOE_WS_DECODE, rows <= 16), plus moe_experts_grouped (MOE_WS_GROUPED), or
+ * for moe_forward_exact (MOE_WS_EXACT) at `rows` rows. One buffer of this
  * size serves both calls of a layer (calls on one stream run in order).
  * A workspace must be zero-filled once, before its first use: its first
  * bytes hold the decode router's hand-off words, tagged with a call counter
@@ -294,6 +298,27 @@ int moe_forward_windows(const moe_layer* layer, const void* x, int rows, const f
  * the array's device address cannot be resolved. */
 int moe_forward_windows_noalloc(const moe_layer* layer, const void* x, int rows, const float* logit_bias,
                                 int32_t* ids, float* p, float* shared_gate, float* y, void* stream);
+
+/* A prompt chunk through the layer with the decode step's arithmetic for
+ * every row, at chunk cost: each row's ids, weights, gate and y are bit for
+ * bit those of its one-row moe_route + moe_experts_decode step, so the
+ * result does not depend on how a prompt is cut into calls ("Native server:
+ * --backend xpu for Nemotron on Intel Arc", maintainer comment: wide prompts
+ * wait until a prompt wider than 16 rows takes the same sum as one row).
+ * The router runs the decode router's per-row logits and pick for all rows;
+ * the rows are sorted by expert and cut into blocks of at most 16 rows, and
+ * gate/up runs the decode kernel's per-row arithmetic on each block (an
+ * expert's weights read once per block, not once per 16-row window as in
+ * moe_forward_windows); down and the combine are the decode kernel's, per
+ * row. Arguments as moe_forward_windows, with a workspace of
+ * moe_workspace_size(MOE_WS_EXACT, rows) bytes (zero-filled once, like every
+ * workspace); taps as moe_experts_decode plus logits, kernel_events[0..7]
+ * bracketing route, sort, gate/up and down.
+ *   rows       1 .. 65536
+ * Errors: MOE_EINVAL, MOE_ENOSPACE, MOE_EHIP. */
+int moe_forward_exact(const moe_layer* layer, const void* x, int rows, const float* logit_bias, int32_t* ids,
+                      float* p, float* shared_gate, float* y, void* ws, uint64_t ws_bytes, const moe_taps* taps,
+                      void* stream);
 
 /* The same layer for prompt chunks (the prefill form): rows are sorted by
  * expert (histogram, prefix scan, stable scatter), then grouped GEMMs on

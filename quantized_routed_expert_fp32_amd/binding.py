@@ -68,7 +68,9 @@ class TapsC(C.Structure):
 EXPORTS = ["moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
            "moe_workspace_size", "moe_route", "moe_experts_decode", "moe_experts_grouped",
            "moe_forward_windows", "moe_forward_windows_noalloc", "moe_route_failures",
-           "moe_status_string", "moe_last_error", "moe_version"]
+           "moe_forward_exact", "moe_status_string", "moe_last_error", "moe_version"]
+
+MOE_WS_DECODE, MOE_WS_GROUPED, MOE_WS_EXACT = 0, 1, 2
 
 _lib = None
 
@@ -98,9 +100,12 @@ def lib() -> C.CDLL:
     L.moe_forward_windows.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, vp, u64, vp]
     L.moe_route_failures.argtypes = [vp, u64, i32, C.POINTER(C.c_uint32), vp]
     L.moe_forward_windows_noalloc.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, vp]
+    L.moe_forward_exact.argtypes = [C.POINTER(LayerC), vp, i32, vp, vp, vp, vp, vp, vp, u64,
+                                    C.POINTER(TapsC), vp]
     for f in ("moe_pack_size", "moe_pack_layer_host", "moe_layer_bind", "moe_pack_layer",
               "moe_workspace_size", "moe_route", "moe_experts_decode", "moe_experts_grouped",
-              "moe_forward_windows", "moe_forward_windows_noalloc", "moe_route_failures"):
+              "moe_forward_windows", "moe_forward_windows_noalloc", "moe_route_failures",
+              "moe_forward_exact"):
         getattr(L, f).restype = C.c_int
     L.moe_status_string.argtypes = [C.c_int]
     L.moe_status_string.restype = C.c_char_p
@@ -201,14 +206,15 @@ def pack_layer(desc: LayerDescC, tensors: dict, device="cuda", stream=None) -> L
     return Layer(out, buf, desc)
 
 
-def workspace_size(desc: LayerDescC, rows: int, grouped: bool) -> int:
+def workspace_size(desc: LayerDescC, rows: int, grouped) -> int:
+    """grouped: False / True (decode / grouped form) or one of MOE_WS_*."""
     n = C.c_uint64()
     _check(lib().moe_workspace_size(C.byref(desc), rows, int(grouped), C.byref(n)),
            "moe_workspace_size")
     return n.value
 
 
-def new_workspace(layer: "Layer", rows: int, grouped: bool, device="cuda", stream=None):
+def new_workspace(layer: "Layer", rows: int, grouped, device="cuda", stream=None):
     """A zero-filled workspace for `rows` rows (route + experts of one layer),
     allocated and cleared on `stream` (default: the current stream), so that
     calls enqueued on that stream find it cleared."""
@@ -317,6 +323,29 @@ def forward_windows(layer: Layer, x, logit_bias=None, ws=None, out=None, y=None,
     _check(lib().moe_forward_windows(C.byref(layer.c), _ptr(x), R, _ptr(logit_bias), _ptr(ids), _ptr(p),
                                      _ptr(sg), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream_ptr(stream)), "moe_forward_windows")
+    return ids, p, sg, y
+
+
+def forward_exact(layer: Layer, x, logit_bias=None, ws=None, out=None, y=None, taps=None, stream=None):
+    """moe_forward_exact: the chunk with the decode step's bits for every row
+    (sorted into expert blocks); returns (ids, p, shared_gate, y)."""
+    import torch
+    R = x.shape[0]
+    k = layer.desc.top_k
+    with _on(stream):
+        if out is None:
+            ids = torch.empty((R, k), dtype=torch.int32, device=x.device)
+            p = torch.empty((R, k), dtype=torch.float32, device=x.device)
+            sg = torch.empty((R,), dtype=torch.float32, device=x.device)
+        else:
+            ids, p, sg = out
+        if y is None:
+            y = torch.empty((R, layer.desc.hidden), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = new_workspace(layer, R, MOE_WS_EXACT, x.device, stream)
+    _check(lib().moe_forward_exact(C.byref(layer.c), _ptr(x), R, _ptr(logit_bias), _ptr(ids), _ptr(p),
+                                   _ptr(sg), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _taps(taps),
+                                   _stream_ptr(stream)), "moe_forward_exact")
     return ids, p, sg, y
 
 

@@ -121,12 +121,19 @@ int moe_workspace_size(const moe_layer_desc* d, int rows, int grouped, uint64_t*
   if (!d || !bytes) { set_error("moe_workspace_size: NULL argument"); return MOE_EINVAL; }
   int st = validate_desc(d);
   if (st) return st;
-  if (rows < 1 || (!grouped && rows > 16) || rows > 65536) {
-    set_error(std::string("moe_workspace_size: rows=") + std::to_string(rows) +
-              (grouped ? " outside 1..65536" : " outside 1..16 (decode)"));
+  if (grouped < MOE_WS_DECODE || grouped > MOE_WS_EXACT) {
+    set_error("moe_workspace_size: kind " + std::to_string(grouped) + " is not MOE_WS_DECODE, MOE_WS_GROUPED "
+              "or MOE_WS_EXACT");
     return MOE_EINVAL;
   }
-  *bytes = grouped ? grouped_ws_layout(d, rows).total : decode_ws_layout(d, rows).total;
+  if (rows < 1 || (grouped == MOE_WS_DECODE && rows > 16) || rows > 65536) {
+    set_error(std::string("moe_workspace_size: rows=") + std::to_string(rows) +
+              (grouped != MOE_WS_DECODE ? " outside 1..65536" : " outside 1..16 (decode)"));
+    return MOE_EINVAL;
+  }
+  *bytes = grouped == MOE_WS_GROUPED ? grouped_ws_layout(d, rows).total
+           : grouped == MOE_WS_EXACT ? exact_ws_layout(d, rows).total
+                                     : decode_ws_layout(d, rows).total;
   return MOE_OK;
 }
 
@@ -153,7 +160,7 @@ static int route_impl(const moe_layer* layer, const void* x, int rows, const flo
   FmtInfo fr, fg;
   format_info(layer->d.router, TC_ROUTER, &fr);
   format_info(layer->d.gate_row, TC_GATE_ROW, &fg);
-  RouteArgs a;
+  RouteArgs a{};
   a.base = static_cast<const uint8_t*>(layer->dev);
   a.r_off = layer->router_off;
   a.r_soff = layer->router_scale_off;
@@ -220,7 +227,7 @@ int moe_experts_decode(const moe_layer* layer, const void* x, int rows, const in
   FmtInfo fe, fs;
   format_info(layer->d.routed, TC_ROUTED, &fe);
   format_info(layer->d.shared, TC_SHARED, &fs);
-  DecodeArgs a;
+  DecodeArgs a{};
   a.base = static_cast<const uint8_t*>(layer->dev);
   a.rt = expert_class(layer, false);
   a.sh = expert_class(layer, true);
@@ -292,6 +299,100 @@ int moe_forward_windows(const moe_layer* layer, const void* x, int rows, const f
   return forward_windows_impl(layer, x, rows, logit_bias, ids, p, shared_gate, y, ws, ws_bytes, stream, 1);
 }
 
+int moe_forward_exact(const moe_layer* layer, const void* x, int rows, const float* logit_bias, int32_t* ids,
+                      float* p, float* shared_gate, float* y, void* ws, uint64_t ws_bytes, const moe_taps* taps,
+                      void* stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if (!x || !ids || !p || !shared_gate || !y || !ws) {
+    set_error("moe_forward_exact: NULL x/ids/p/shared_gate/y/ws");
+    return MOE_EINVAL;
+  }
+  if (rows < 1 || rows > 65536) { set_error("moe_forward_exact: rows outside 1..65536"); return MOE_EINVAL; }
+  const moe_layer_desc* d = &layer->d;
+  const ExactWs wl = exact_ws_layout(d, rows);
+  if (ws_bytes < wl.total) {
+    set_error("moe_forward_exact: workspace of " + std::to_string(ws_bytes) + " bytes, needs " +
+              std::to_string(wl.total) + " (moe_workspace_size with MOE_WS_EXACT)");
+    return MOE_ENOSPACE;
+  }
+  FmtInfo fr, fg, fe, fs;
+  format_info(d->router, TC_ROUTER, &fr);
+  format_info(d->gate_row, TC_GATE_ROW, &fg);
+  format_info(d->routed, TC_ROUTED, &fe);
+  format_info(d->shared, TC_SHARED, &fs);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = taps_events(taps);
+  // 1. the router with the decode router's per-row arithmetic
+  RouteArgs ra{};
+  ra.base = static_cast<const uint8_t*>(layer->dev);
+  ra.r_off = layer->router_off;
+  ra.r_soff = layer->router_scale_off;
+  ra.g_off = layer->gate_row_off;
+  ra.g_soff = layer->gate_row_scale_off;
+  ra.x = static_cast<const uint16_t*>(x);
+  ra.act_fp16 = d->act_dtype == MOE_FP16;
+  ra.H = d->hidden;
+  ra.E = d->n_experts;
+  ra.k = d->top_k;
+  ra.bias = logit_bias;
+  ra.ids = ids;
+  ra.p = p;
+  ra.sg = shared_gate;
+  ra.R = rows;
+  ra.logits = taps ? taps->logits : nullptr;
+  const RouteWs rw = route_ws_layout(d, rows);
+  ra.lg_ws = reinterpret_cast<float*>(w + rw.lg_off);
+  ra.gl_ws = reinterpret_cast<float*>(w + rw.gl_off);
+  ra.cand = reinterpret_cast<uint64_t*>(w + rw.cand_off);
+  ra.sync = reinterpret_cast<uint32_t*>(w + rw.sync_off);
+  hipError_t e = launch_route_exact(fr.kid, fg.kid, ra, s, ev);
+  if (e != hipSuccess) return hip_fail("moe_forward_exact: route launch", e);
+  // 2. the slots in expert-major order and the expert blocks of 16 rows
+  GroupedArgs ga{};
+  ga.E = d->n_experts;
+  ga.k = d->top_k;
+  ga.R = rows;
+  ga.H = d->hidden;
+  ga.ids = ids;
+  ga.meta = reinterpret_cast<int32_t*>(w + wl.meta_off);
+  ga.perm = reinterpret_cast<int32_t*>(w + wl.perm_off);
+  ga.tiles = reinterpret_cast<int32_t*>(w + wl.blocks_off);
+  ga.max_tiles = wl.max_blocks;
+  ga.blk16 = 1;
+  e = launch_grp_sort(ga, s, ev ? ev + 2 : nullptr);
+  if (e != hipSuccess) return hip_fail("moe_forward_exact: sort launch", e);
+  // 3. gate/up on the blocks, then the decode down + combine of every row
+  DecodeArgs da{};
+  da.base = static_cast<const uint8_t*>(layer->dev);
+  da.rt = expert_class(layer, false);
+  da.sh = expert_class(layer, true);
+  da.x = static_cast<const uint16_t*>(x);
+  da.act_fp16 = d->act_dtype == MOE_FP16;
+  da.H = d->hidden;
+  da.E = d->n_experts;
+  da.k = d->top_k;
+  da.R = rows;
+  da.Imax = std::max(d->inter, d->shared_inter);
+  da.ids = ids;
+  da.p = p;
+  da.sg = shared_gate;
+  da.hhi = reinterpret_cast<uint16_t*>(w + wl.dec.hhi_off);
+  da.hlo = reinterpret_cast<uint16_t*>(w + wl.dec.hlo_off);
+  da.hc = reinterpret_cast<float*>(w + wl.dec.hc_off);
+  da.y = y;
+  da.tap_gu = taps ? taps->gu : nullptr;
+  da.tap_h = taps ? taps->h : nullptr;
+  da.tap_e = taps ? taps->e : nullptr;
+  da.perm = ga.perm;
+  da.blocks = ga.tiles;
+  da.nblocks = ga.meta;
+  e = launch_exact_experts(fe.kid, fs.kid, da, s, ev ? ev + 4 : nullptr);
+  if (e != hipSuccess) return hip_fail("moe_forward_exact: experts launch", e);
+  return MOE_OK;
+}
+
 int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const int32_t* ids,
                         const float* p, const float* shared_gate, float* y, void* ws,
                         uint64_t ws_bytes, const moe_taps* taps, void* stream) {
@@ -320,7 +421,7 @@ int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const i
   FmtInfo fe, fs;
   format_info(layer->d.routed, TC_ROUTED, &fe);
   format_info(layer->d.shared, TC_SHARED, &fs);
-  GroupedArgs a;
+  GroupedArgs a{};
   a.base = static_cast<const uint8_t*>(layer->dev);
   a.rt = expert_class(layer, false);
   a.sh = expert_class(layer, true);

@@ -286,16 +286,45 @@ __device__ __forceinline__ int pick4(int v, int a0, int a1, int a2, int a3) {
   return v == 0 ? a0 : v == 1 ? a1 : v == 2 ? a2 : a3;   // selects, not an indexed array (scratch)
 }
 
-// The rows of an item in passes of up to 4 (slot order = pick order): the
-// slice dots of a pass, the partials of every wave to LDS, one barrier, then
-// wave v finishes the pass's slot v. Slots past the pass's rows repeat its
-// first row; their results are not used. With fewer waves than slots a
-// wave finishes several.
+// One pass: up to 4 rows of an item against the wave's K slices, the slice
+// partials of every wave to LDS, one barrier, then wave v finishes the
+// pass's slot v (with fewer waves than slots a wave finishes several). lr:
+// the slots' rows in the LDS activation block (and their chunk-sum rows),
+// rr / jj: the slots' rows and picks in the outputs; slots past m repeat
+// slot 0 and their results are not used.
+template <int F, int ACT16, typename SB>
+__device__ __forceinline__ void gu_pass(const DecodeArgs& a, const GuItem& it, const SB& b, const uint32_t* xl,
+                                        const float* cs, float* red, int& rb, int wv, int nw, int lane,
+                                        const int (&lr)[4], const int (&rr)[4], const int (&jj)[4], int m) {
+  const int H = a.H, nch = H / 32, nsl = H / KBLK;
+  const int rl = pick4(lane & 3, lr[0], lr[1], lr[2], lr[3]);
+  const uint32_t* xr = xl + (uint64_t)rl * (H / 2);
+  const float *xs0 = cs + lr[0] * nch, *xs1 = cs + lr[1] * nch, *xs2 = cs + lr[2] * nch, *xs3 = cs + lr[3] * nch;
+  f4v out = {0.f, 0.f, 0.f, 0.f};
+  out = gu_slice_mfma<F, ACT16>(b.w, b.sc, xr, xs0, xs1, xs2, xs3, wv, out);
+  for (int sl = wv + nw; sl < nsl; sl += nw) {     // hidden > 256 * waves: further slices in place
+    SB c2;
+    load_slice<F>(it.r, it.codes, it.scales, it.tl, sl, nch, nsl, lane, c2);
+    out = gu_slice_mfma<F, ACT16>(c2.w, c2.sc, xr, xs0, xs1, xs2, xs3, sl, out);
+  }
+  float* rbuf = red + rb * (4 * nw * 64);
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    if (v < m) rbuf[(v * nw + wv) * 64 + lane] = out[v];
+  __syncthreads();
+  for (int v = wv; v < m; v += nw)    // fewer waves than slots: waves take several
+    gu_finish(a, rbuf + v * nw * 64, nw, pick4(v, rr[0], rr[1], rr[2], rr[3]),
+              pick4(v, jj[0], jj[1], jj[2], jj[3]), it.t, lane);
+  rb ^= 1;   // the other buffer next: its readers passed this barrier
+}
+
+// The rows of an item in passes of up to 4 (slot order = pick order); all
+// rows of the batch sit in LDS, so a slot's LDS row is its row.
 template <int F, int ACT16, typename SB>
 __device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P, const GuItem& it,
                                              const SB& b, const uint32_t* xl, const float* cs,
                                              float* red, int& rb, int wv, int nw, int lane) {
-  const int H = a.H, nch = H / 32, nsl = H / KBLK, k = a.k;
+  const int k = a.k;
   uint64_t m0 = 0, m1 = 0;
   int n = min(GU_SHARED_ROWS, a.R - GU_SHARED_ROWS * it.e);   // shared: rows 4e .. 4e + n - 1
   if (!it.shared) {
@@ -319,25 +348,7 @@ __device__ __forceinline__ void gu_process_t(const DecodeArgs& a, const Picks& P
       rr[v] = (v == 0 || v < m) ? r : rr[0];
       jj[v] = (v == 0 || v < m) ? j : jj[0];
     }
-    const int rl = pick4(lane & 3, rr[0], rr[1], rr[2], rr[3]);
-    const uint32_t* xr = xl + (uint64_t)rl * (H / 2);
-    const float *xs0 = cs + rr[0] * nch, *xs1 = cs + rr[1] * nch, *xs2 = cs + rr[2] * nch, *xs3 = cs + rr[3] * nch;
-    f4v out = {0.f, 0.f, 0.f, 0.f};
-    out = gu_slice_mfma<F, ACT16>(b.w, b.sc, xr, xs0, xs1, xs2, xs3, wv, out);
-    for (int sl = wv + nw; sl < nsl; sl += nw) {     // hidden > 256 * waves: further slices in place
-      SB c2;
-      load_slice<F>(it.r, it.codes, it.scales, it.tl, sl, nch, nsl, lane, c2);
-      out = gu_slice_mfma<F, ACT16>(c2.w, c2.sc, xr, xs0, xs1, xs2, xs3, sl, out);
-    }
-    float* rbuf = red + rb * (4 * nw * 64);
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (v < m) rbuf[(v * nw + wv) * 64 + lane] = out[v];
-    __syncthreads();
-    for (int v = wv; v < m; v += nw)    // fewer waves than slots: waves take several
-      gu_finish(a, rbuf + v * nw * 64, nw, pick4(v, rr[0], rr[1], rr[2], rr[3]),
-                pick4(v, jj[0], jj[1], jj[2], jj[3]), it.t, lane);
-    rb ^= 1;   // the other buffer next: its readers passed this barrier
+    gu_pass<F, ACT16>(a, it, b, xl, cs, red, rb, wv, nw, lane, rr, rr, jj, m);
   }
 }
 
@@ -457,6 +468,108 @@ __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
     gu_process<FR, FS, ACT16>(a, P, ib, B, c.xl, c.cs, c.red, rb, c.wv, c.nw, c.lane);
     if (nx2 >= c.n_items) break;
     it_i = nx2;
+  }
+}
+
+// The exact chunk form of gate/up: the same per-row arithmetic as
+// k_dec_gateup (gu_pass: slices owned by fixed waves, chunks and groups in K
+// order, slices reduced in slice order, each output element formed from its
+// own row and column alone), on the expert blocks of the grouped sort
+// (expert, first position, up to 16 rows) instead of a decode batch's units:
+// every row's h is its one-row decode step's, however the prompt is cut,
+// while an expert's weights are read once per block instead of once per
+// 16-row window. Item = (block, group of GU_TG layout tiles); a workgroup
+// stages the block's activations (16 rows) and their chunk sums in LDS once
+// per item, then streams the group's tiles with the next tile's loads in
+// flight, each tile in passes of 4 of the block's slots.
+constexpr int GU_TG = 4;   // layout tiles per exact-form item
+
+// One tile of an exact-form item: the block's mc slots (positions p0 ..) in
+// passes of 4; a slot's LDS row is its place in the block.
+template <int FR, int FS, int ACT16, typename SB>
+__device__ __forceinline__ void exact_tile(const DecodeArgs& a, const GuItem& it, const SB& b, const uint32_t* xl,
+                                           const float* cs, float* red, int& rb, int wv, int nw, int lane, int p0,
+                                           int mc) {
+  const int k = a.k;
+  for (int i = 0; i < mc; i += 4) {
+    const int m = min(4, mc - i);
+    int lr[4], rr[4], jj[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int l = (v < m) ? i + v : i;
+      const int slot = a.perm[p0 + l];
+      lr[v] = l;
+      rr[v] = slot / (k + 1);
+      jj[v] = slot % (k + 1);
+    }
+    if (it.shared) gu_pass<FS, ACT16>(a, it, b, xl, cs, red, rb, wv, nw, lane, lr, rr, jj, m);
+    else gu_pass<FR, ACT16>(a, it, b, xl, cs, red, rb, wv, nw, lane, lr, rr, jj, m);
+  }
+}
+
+template <int FR, int FS, int ACT16>
+__global__ __launch_bounds__(512) void k_exact_gateup(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int RB = 16;   // rows per block
+  const int H = a.H, k = a.k;
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
+  const int nw = nthr >> 6, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = H / 32, nsl = H / KBLK;
+  uint32_t* xl = reinterpret_cast<uint32_t*>(smem);
+  float* cs = reinterpret_cast<float*>(smem + (size_t)RB * H * 2);
+  float* red = cs + RB * nch;
+  const int Tmax = 2 * a.Imax / 64, ngr = (Tmax + GU_TG - 1) / GU_TG;
+  const int n_items = *a.nblocks * ngr;
+  const GuCls rcl = gu_cls(a.rt), scl = gu_cls(a.sh);
+  constexpr int SW = Fmt<FR>::WORDS > Fmt<FS>::WORDS ? Fmt<FR>::WORDS : Fmt<FS>::WORDS;
+  SliceBuf<SW> A, B;
+  int rb = 0;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int* blk = a.blocks + 3 * (item / ngr);
+    const int e = blk[0], p0 = blk[1], mc = blk[2];
+    const bool shared = e == a.E;
+    const GuCls& cl = shared ? scl : rcl;
+    const int t0 = (item % ngr) * GU_TG, t1 = min(t0 + GU_TG, cl.tlast + 1);
+    if (t0 >= t1 || mc <= 0) continue;
+    GuItem it;
+    it.r = make_rsrc(a.base + (shared ? cl.base_off : cl.base_off + (uint64_t)e * cl.stride), cl.blk_bytes);
+    it.codes = cl.codes;
+    it.scales = cl.scales;
+    it.shared = shared;
+    it.e = e;
+    it.t = it.tl = t0;
+    gu_issue<FR, FS>(it, wv, nch, nsl, lane, A);
+    // the block's rows (the previous item's readers are past its last barrier)
+    __syncthreads();
+    const uint4* xg = reinterpret_cast<const uint4*>(a.x);
+    for (int q = tid; q < mc * (H / 8); q += nthr) {
+      const int lr = q / (H / 8), c8 = q % (H / 8);
+      const int row = a.perm[p0 + lr] / (k + 1);
+      reinterpret_cast<uint4*>(xl)[q] = xg[(uint64_t)row * (H / 8) + c8];
+    }
+    __syncthreads();
+    for (int r = 0; r < mc; ++r) {
+      for (int sl = wv; sl < nsl; sl += nw) {
+        const uint2 v = reinterpret_cast<const uint2*>(xl + (uint64_t)r * (H / 2) + sl * (KBLK / 2))[lane];
+        const float sm = sum8(sum4<ACT16>(v));
+        if ((lane & 7) == 0) cs[r * nch + sl * 8 + (lane >> 3)] = sm;
+      }
+    }
+    __syncthreads();
+    // tiles in pairs, A and B alternating; the next tile's loads go out
+    // before this tile's arithmetic
+    for (int t = t0; t < t1; t += 2) {
+      GuItem nx = it;
+      nx.t = nx.tl = t + 1;
+      if (t + 1 < t1) gu_issue<FR, FS>(nx, wv, nch, nsl, lane, B);
+      it.t = it.tl = t;
+      exact_tile<FR, FS, ACT16>(a, it, A, xl, cs, red, rb, wv, nw, lane, p0, mc);
+      if (t + 1 >= t1) break;
+      nx.t = nx.tl = t + 2;
+      if (t + 2 < t1) gu_issue<FR, FS>(nx, wv, nch, nsl, lane, A);
+      it.t = it.tl = t + 1;
+      exact_tile<FR, FS, ACT16>(a, it, B, xl, cs, red, rb, wv, nw, lane, p0, mc);
+    }
   }
 }
 
@@ -740,6 +853,27 @@ static hipError_t launch_gateup(const DecodeArgs& a, hipStream_t s, hipEvent_t* 
   return hipGetLastError();
 }
 
+// The exact chunk form's experts: gate/up on the sort's expert blocks, then
+// k_dec_down over every row (its per-(row, column tile) workgroups read the
+// row's experts' down tiles; the rows of a tile share one XCD's L2).
+template <int FR, int FS>
+static hipError_t launch_exact_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
+  const int nw = std::min(8, a.H / KBLK);
+  const size_t gsm = decode_gu_smem(16, a.H), dsm = decode_dn_smem(a.k, a.Imax);
+  hipError_t err;
+  if (a.act_fp16) {
+    if ((err = allow_smem(k_exact_gateup<FR, FS, 1>, gsm)) != hipSuccess) return err;
+    launch_k(k_exact_gateup<FR, FS, 1>, dim3(GU_GRID), dim3(64 * nw), (uint32_t)gsm, s, ev, 0, a);
+  } else {
+    if ((err = allow_smem(k_exact_gateup<FR, FS, 0>, gsm)) != hipSuccess) return err;
+    launch_k(k_exact_gateup<FR, FS, 0>, dim3(GU_GRID), dim3(64 * nw), (uint32_t)gsm, s, ev, 0, a);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = allow_smem(k_dec_down<FR, FS>, dsm)) != hipSuccess) return err;
+  launch_k(k_dec_down<FR, FS>, dim3((a.H / 64) * a.R), dim3(64 * a.k * DN_KS), (uint32_t)dsm, s, ev, 2, a);
+  return hipGetLastError();
+}
+
 template <int FR, int FS>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   const int nw = std::min(8, a.H / KBLK);
@@ -766,6 +900,36 @@ static hipError_t launch_decode_s(int fs, const DecodeArgs& a, hipStream_t s, hi
       case F_Q8: return launch_decode_t<FR, F_Q8>(a, s, ev);
       case F_Q2: return launch_decode_t<FR, F_Q2>(a, s, ev);
     }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FR>
+static hipError_t launch_exact_s(int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
+  if constexpr (FR == F_Q5 || FR == F_Q6) {
+    if (fs == FR) return launch_exact_t<FR, FR>(a, s, ev);
+    if (fs == F_Q4) return launch_exact_t<FR, F_Q4>(a, s, ev);
+  } else {
+    switch (fs) {
+      case F_Q4: return launch_exact_t<FR, F_Q4>(a, s, ev);
+      case F_Q3: return launch_exact_t<FR, F_Q3>(a, s, ev);
+      case F_S4: return launch_exact_t<FR, F_S4>(a, s, ev);
+      case F_Q8: return launch_exact_t<FR, F_Q8>(a, s, ev);
+      case F_Q2: return launch_exact_t<FR, F_Q2>(a, s, ev);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_exact_experts(int fr, int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
+  switch (fr) {
+    case F_Q4: return launch_exact_s<F_Q4>(fs, a, s, ev);
+    case F_Q3: return launch_exact_s<F_Q3>(fs, a, s, ev);
+    case F_S4: return launch_exact_s<F_S4>(fs, a, s, ev);
+    case F_Q8: return launch_exact_s<F_Q8>(fs, a, s, ev);
+    case F_Q2: return launch_exact_s<F_Q2>(fs, a, s, ev);
+    case F_Q5: return launch_exact_s<F_Q5>(fs, a, s, ev);
+    case F_Q6: return launch_exact_s<F_Q6>(fs, a, s, ev);
   }
   return hipErrorInvalidValue;
 }

@@ -82,7 +82,9 @@ __device__ __forceinline__ int wave_exclusive_scan(const int* in, int* out, int 
 //     running count for the expert returns;
 //  4. the work list of M-tiles (expert, first position, rows), 128-row tiles
 //     first, then 96-, 64- and 32-row ones, each class laid out by a scan
-//     over the experts; the queue counters of the two GEMMs are reset.
+//     over the experts; the queue counters of the two GEMMs are reset. With
+//     blk16 (the exact chunk form) the list holds instead each expert's run
+//     cut into blocks of 16 rows (the last one shorter), in expert order.
 // Workgroups 1.. (bf16 activations only): x -> fp16 copy for the gate/up GEMM.
 __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
   __shared__ int cnt[320];
@@ -157,10 +159,10 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
   for (int e = tid; e <= E; e += 1024) {
     const int c = cnt[e];
     const int mtr = ((c & 127) + 31) >> 5;       // height of the last tile in 32-row units (0: none)
-    nt[0][e] = (c >> 7) + (mtr == 4);
-    nt[1][e] = mtr == 3;
-    nt[2][e] = mtr == 2;
-    nt[3][e] = mtr == 1;
+    nt[0][e] = a.blk16 ? (c + 15) >> 4 : (c >> 7) + (mtr == 4);
+    nt[1][e] = !a.blk16 && mtr == 3;
+    nt[2][e] = !a.blk16 && mtr == 2;
+    nt[3][e] = !a.blk16 && mtr == 1;
   }
   __syncthreads();
   // 3. scatter (positions from the wave's own LDS row)
@@ -186,7 +188,17 @@ __global__ __launch_bounds__(1024) void k_grp_sort(GroupedArgs a) {
   }
   __syncthreads();
   const int b1 = s_tot[0], b2 = b1 + s_tot[1], b3 = b2 + s_tot[2];
-  for (int e = tid; e <= E; e += 1024) {
+  for (int e = tid; e <= E && a.blk16; e += 1024) {
+    // the exact chunk form: blocks of 16 rows, the last one shorter
+    const int c = cnt[e];
+    int* t = a.tiles + 3 * nt[0][e];
+    for (int m = 0; 16 * m < c; ++m, t += 3) {
+      t[0] = e;
+      t[1] = off[e] + 16 * m;
+      t[2] = min(16, c - 16 * m);
+    }
+  }
+  for (int e = tid; e <= E && !a.blk16; e += 1024) {
     const int c = cnt[e];
     const int full = c >> 7, rem = c & 127, mtr = (rem + 31) >> 5;
     int* t = a.tiles + 3 * nt[0][e];
@@ -762,6 +774,11 @@ static int gemm_grid(int wg_per_cu) {
     cus[dev] = n;
   }
   return cus[dev] * wg_per_cu;
+}
+
+hipError_t launch_grp_sort(const GroupedArgs& a, hipStream_t s, hipEvent_t* ev) {
+  launch_k(k_grp_sort, dim3(1), dim3(1024), 0, s, ev, 0, a);
+  return hipGetLastError();
 }
 
 template <int FR, int FS>

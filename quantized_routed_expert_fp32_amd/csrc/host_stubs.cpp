@@ -13,6 +13,9 @@ namespace moe {
 hipError_t launch_route(int, int, const RouteArgs&, hipStream_t, hipEvent_t*) { return hipErrorNoDevice; }
 hipError_t launch_decode(int, int, const DecodeArgs&, hipStream_t, hipEvent_t*) { return hipErrorNoDevice; }
 hipError_t launch_grouped(int, int, const GroupedArgs&, hipStream_t, hipEvent_t*) { return hipErrorNoDevice; }
+hipError_t launch_grp_sort(const GroupedArgs&, hipStream_t, hipEvent_t*) { return hipErrorNoDevice; }
+hipError_t launch_route_exact(int, int, const RouteArgs&, hipStream_t, hipEvent_t*) { return hipErrorNoDevice; }
+hipError_t launch_exact_experts(int, int, const DecodeArgs&, hipStream_t, hipEvent_t*) { return hipErrorNoDevice; }
 
 }  // namespace moe
 

@@ -70,6 +70,19 @@ struct GroupedWs {
 };
 GroupedWs grouped_ws_layout(const moe_layer_desc* d, int rows);
 
+// Workspace layout of the exact chunk form (moe_forward_exact): the decode
+// layout for all rows (route scratch with [rows, E] logits, then the h
+// parts of every slot), then the sort's arrays and its list of expert blocks.
+struct ExactWs {
+  DecodeWs dec;
+  uint64_t meta_off;     // int32: block count, queue words, expert offsets [E+2]
+  uint64_t perm_off;     // int32 [R*(k+1)]: expert-major position -> slot index r*(k+1)+j
+  uint64_t blocks_off;   // int32 [max_blocks][3]: (expert, first position, rows <= 16)
+  uint64_t total;
+  int max_blocks;
+};
+ExactWs exact_ws_layout(const moe_layer_desc* d, int rows);
+
 // moe_forward_windows with the router's sticky-failure rule switchable
 // (sticky = 0: a failure recorded in the workspace by an earlier call does
 // not mark this call's rows).

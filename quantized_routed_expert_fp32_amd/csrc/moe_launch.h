@@ -46,6 +46,12 @@ struct DecodeArgs {
   float* tap_gu;  // [R, k+1, 2, Imax] or null
   float* tap_h;   // [R, k+1, Imax] or null
   float* tap_e;   // [R, k+1, H] or null
+  // the exact chunk form only (null otherwise): the sort's expert-major
+  // slot order, its list of expert blocks (expert, first position, rows <=
+  // 16) and the block count on the device
+  const int32_t* perm;
+  const int32_t* blocks;
+  const int32_t* nblocks;
 };
 
 struct GroupedArgs {
@@ -63,6 +69,7 @@ struct GroupedArgs {
   float* e_ws;       // [R*(k+1), H] slot order
   int32_t* tiles;    // work list of M-tiles (expert, first position, rows)
   int max_tiles;     // capacity of the list
+  int blk16;         // nonzero: the list holds blocks of at most 16 rows (the exact chunk form)
   float* y;
   float* tap_gu;
   float* tap_h;
@@ -72,6 +79,12 @@ struct GroupedArgs {
 // ev: NULL or 8 events; ev[2i] / ev[2i+1] (each may be NULL) bracket kernel i
 hipError_t launch_route(int fr, int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
+// The exact chunk form: the sort alone (16-row blocks), the router with the
+// decode router's per-row arithmetic for any number of rows, and gate/up on
+// expert blocks followed by the decode down + combine over every row.
+hipError_t launch_grp_sort(const GroupedArgs& a, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_route_exact(int fr, int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_exact_experts(int fr, int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s, hipEvent_t* ev);
 
 }  // namespace moe

@@ -448,6 +448,20 @@ DecodeWs decode_ws_layout(const moe_layer_desc* d, int rows) {
   return w;
 }
 
+ExactWs exact_ws_layout(const moe_layer_desc* d, int rows) {
+  const uint64_t E = d->n_experts, slots = (uint64_t)rows * (d->top_k + 1);
+  ExactWs w;
+  w.dec = decode_ws_layout(d, rows);
+  uint64_t o = w.dec.total;
+  w.meta_off = o; o = align256(o + (E + 16) * 4);
+  w.perm_off = o; o = align256(o + slots * 4);
+  // an expert's run of c rows is ceil(c / 16) blocks: at most slots/16 + E + 1
+  w.max_blocks = (int)(slots / 16 + E + 2);
+  w.blocks_off = o; o = align256(o + (uint64_t)w.max_blocks * 3 * 4);
+  w.total = o;
+  return w;
+}
+
 GroupedWs grouped_ws_layout(const moe_layer_desc* d, int rows) {
   const uint64_t E = d->n_experts, k = d->top_k, H = d->hidden;
   const uint64_t Imax = std::max(d->inter, d->shared_inter);

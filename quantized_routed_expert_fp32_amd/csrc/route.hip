@@ -549,6 +549,47 @@ static hipError_t launch_route_t(const RouteArgs& a, hipStream_t s, hipEvent_t* 
   return hipGetLastError();
 }
 
+// The exact chunk form: logits on the vector units (k_route_logits, whose
+// per-row slice dots and wave sums are those of k_route) and the one-wave
+// pick (the same order and weights as k_route's two-level pick), for any
+// number of rows: every row's ids, weights and gate equal its one-row
+// decode step's.
+template <int FR, int FG, int ACT16>
+static hipError_t launch_route_exact_t(const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
+  const int nw = min(8, a.H / KBLK);
+  hipEvent_t e0[2] = {ev ? ev[0] : nullptr, nullptr}, e1[2] = {nullptr, ev ? ev[1] : nullptr};
+  launch_k(k_route_logits<FR, ACT16, 8>, dim3(a.E / 64, (a.R + 7) / 8), dim3(64 * nw), 0, s, e0, 0, a, a.x);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  launch_k(k_route_pick<FG, ACT16>, dim3((a.R + 3) / 4), dim3(256), 0, s, e1, 0, a, a.x);
+  return hipGetLastError();
+}
+
+template <int FR, int ACT16>
+static hipError_t launch_route_exact_g(int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
+  switch (fg) {
+    case F_Q4: return launch_route_exact_t<FR, F_Q4, ACT16>(a, s, ev);
+    case F_Q8: return launch_route_exact_t<FR, F_Q8, ACT16>(a, s, ev);
+    case F_S4: return launch_route_exact_t<FR, F_S4, ACT16>(a, s, ev);
+    case F_DENSE: return launch_route_exact_t<FR, F_DENSE, ACT16>(a, s, ev);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FR>
+static hipError_t launch_route_exact_a(int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
+  return a.act_fp16 ? launch_route_exact_g<FR, 1>(fg, a, s, ev) : launch_route_exact_g<FR, 0>(fg, a, s, ev);
+}
+
+hipError_t launch_route_exact(int fr, int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
+  switch (fr) {
+    case F_Q4: return launch_route_exact_a<F_Q4>(fg, a, s, ev);
+    case F_Q8: return launch_route_exact_a<F_Q8>(fg, a, s, ev);
+    case F_S4: return launch_route_exact_a<F_S4>(fg, a, s, ev);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int FR, int ACT16>
 static hipError_t launch_route_g(int fg, const RouteArgs& a, hipStream_t s, hipEvent_t* ev) {
   switch (fg) {
