@@ -388,6 +388,7 @@ int moe_forward_exact(const moe_layer* layer, const void* x, int rows, const flo
   da.perm = ga.perm;
   da.blocks = ga.tiles;
   da.nblocks = ga.meta;
+  da.e_ws = reinterpret_cast<float*>(w + wl.e_off);
   e = launch_exact_experts(fe.kid, fs.kid, da, s, ev ? ev + 4 : nullptr);
   if (e != hipSuccess) return hip_fail("moe_forward_exact: experts launch", e);
   return MOE_OK;

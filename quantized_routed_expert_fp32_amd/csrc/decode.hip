@@ -483,13 +483,14 @@ __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
 // per item, then streams the group's tiles with the next tile's loads in
 // flight, each tile in passes of 4 of the block's slots.
 constexpr int GU_TG = 4;   // layout tiles per exact-form item
+constexpr int GX_RB = 16;  // rows per expert block
 
-// One tile of an exact-form item: the block's mc slots (positions p0 ..) in
-// passes of 4; a slot's LDS row is its place in the block.
+// One tile of an exact-form item through gu_pass: the
+// block's mc slots in passes of 4; a slot's LDS row is its place in the block.
 template <int FR, int FS, int ACT16, typename SB>
 __device__ __forceinline__ void exact_tile(const DecodeArgs& a, const GuItem& it, const SB& b, const uint32_t* xl,
-                                           const float* cs, float* red, int& rb, int wv, int nw, int lane, int p0,
-                                           int mc) {
+                                           const float* cs, float* red, int& rb, int wv, int nw, int lane,
+                                           const int* sslot, int mc) {
   const int k = a.k;
   for (int i = 0; i < mc; i += 4) {
     const int m = min(4, mc - i);
@@ -497,7 +498,7 @@ __device__ __forceinline__ void exact_tile(const DecodeArgs& a, const GuItem& it
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int l = (v < m) ? i + v : i;
-      const int slot = a.perm[p0 + l];
+      const int slot = sslot[l];
       lr[v] = l;
       rr[v] = slot / (k + 1);
       jj[v] = slot % (k + 1);
@@ -510,14 +511,16 @@ __device__ __forceinline__ void exact_tile(const DecodeArgs& a, const GuItem& it
 template <int FR, int FS, int ACT16>
 __global__ __launch_bounds__(512) void k_exact_gateup(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr int RB = 16;   // rows per block
+  constexpr int RB = GX_RB;   // rows per block
   const int H = a.H, k = a.k;
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
   const int nw = nthr >> 6, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = H / 32, nsl = H / KBLK;
   uint32_t* xl = reinterpret_cast<uint32_t*>(smem);
   float* cs = reinterpret_cast<float*>(smem + (size_t)RB * H * 2);
-  float* red = cs + RB * nch;
+  float* red = cs + RB * nch;                  // [2][4][nw][64]
+  __shared__ int sslot[GX_RB];                  // the block's slot indexes
+
   const int Tmax = 2 * a.Imax / 64, ngr = (Tmax + GU_TG - 1) / GU_TG;
   const int n_items = *a.nblocks * ngr;
   const GuCls rcl = gu_cls(a.rt), scl = gu_cls(a.sh);
@@ -539,13 +542,26 @@ __global__ __launch_bounds__(512) void k_exact_gateup(DecodeArgs a) {
     it.e = e;
     it.t = it.tl = t0;
     gu_issue<FR, FS>(it, wv, nch, nsl, lane, A);
-    // the block's rows (the previous item's readers are past its last barrier)
+    // the block's slots, then its rows (the previous item's readers are past
+    // its last barrier); the gather issues all of a thread's loads at once
+    __syncthreads();
+    if (tid < mc) sslot[tid] = a.perm[p0 + tid];
     __syncthreads();
     const uint4* xg = reinterpret_cast<const uint4*>(a.x);
-    for (int q = tid; q < mc * (H / 8); q += nthr) {
-      const int lr = q / (H / 8), c8 = q % (H / 8);
-      const int row = a.perm[p0 + lr] / (k + 1);
-      reinterpret_cast<uint4*>(xl)[q] = xg[(uint64_t)row * (H / 8) + c8];
+    const int npc = mc * (H / 8);
+    for (int q0 = 0; q0 < npc; q0 += 4 * nthr) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = min(q0 + u * nthr + tid, npc - 1);
+        const int lr = q / (H / 8), c8 = q % (H / 8);
+        v[u] = xg[(uint64_t)(sslot[lr] / (k + 1)) * (H / 8) + c8];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + u * nthr + tid;
+        if (q < npc) reinterpret_cast<uint4*>(xl)[q] = v[u];
+      }
     }
     __syncthreads();
     for (int r = 0; r < mc; ++r) {
@@ -563,12 +579,12 @@ __global__ __launch_bounds__(512) void k_exact_gateup(DecodeArgs a) {
       nx.t = nx.tl = t + 1;
       if (t + 1 < t1) gu_issue<FR, FS>(nx, wv, nch, nsl, lane, B);
       it.t = it.tl = t;
-      exact_tile<FR, FS, ACT16>(a, it, A, xl, cs, red, rb, wv, nw, lane, p0, mc);
+      exact_tile<FR, FS, ACT16>(a, it, A, xl, cs, red, rb, wv, nw, lane, sslot, mc);
       if (t + 1 >= t1) break;
       nx.t = nx.tl = t + 2;
       if (t + 2 < t1) gu_issue<FR, FS>(nx, wv, nch, nsl, lane, A);
       it.t = it.tl = t + 1;
-      exact_tile<FR, FS, ACT16>(a, it, B, xl, cs, red, rb, wv, nw, lane, p0, mc);
+      exact_tile<FR, FS, ACT16>(a, it, B, xl, cs, red, rb, wv, nw, lane, sslot, mc);
     }
   }
 }
@@ -822,6 +838,228 @@ __global__ __launch_bounds__(1024) void k_dec_down(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ exact down
+// The exact chunk form of down: k_dec_down's per-(row, slot) arithmetic on
+// the expert blocks, so an expert's down tiles are read once per block of
+// up to 16 rows instead of once per row. Two rows share each 4x4x4 MFMA: row
+// slots 0 / 1 hold the first row's high / low h parts, slots 2 / 3 the
+// second row's (k_dec_down repeats one row's parts there); an output element
+// depends on its own row slot alone, so each row's sums are k_dec_down's.
+// Item = (block, group of DX_TG 64-column tiles); wave w takes tile w / 2 of
+// the group and the K blocks w % 2, w % 2 + 2, ... (k_dec_down's two parts).
+// A routed slot's output is (0 + part 0) + part 1, as k_dec_down adds them;
+// the shared expert's is k_dec_down's sum over its k * DN_KS wave partials,
+// each the sum of the groups that wave takes (dn_group per group). Outputs
+// go to e_ws in slot order; k_exact_combine adds them as k_dec_down does.
+constexpr int DX_TG = 4;        // 64-column tiles per exact-form down item
+constexpr int DX_MAXG = 32;     // shared-expert groups kept per row and tile
+
+template <int F>
+__device__ __forceinline__ void dn_block2(const uint32_t (&w)[8][Fmt<F>::WORDS], const uint32_t* sc,
+                                          const uint32_t* src, const float* hca, const float* hcb, float& oa,
+                                          float& ob) {
+  constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
+  const PairMasks pk = pair_masks<F, 1>();
+#pragma unroll
+  for (int gi = 0; gi < GPS; ++gi) {
+    float ms, bm;
+    coef_reg<F>(sc, gi, ms, bm);
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    float Xa = 0.f, Xb = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < CPG; ++cc) {
+      const int c = gi * CPG + cc;
+      acc = dn_chunk<F>(w[c], pk, src + 16 * c, acc);
+      Xa += hca[c];
+      Xb += hcb[c];
+    }
+    oa = fmaf(ms, acc[0] + acc[1], oa);
+    oa = fmaf(bm, Xa, oa);
+    ob = fmaf(ms, acc[2] + acc[3], ob);
+    ob = fmaf(bm, Xb, ob);
+  }
+}
+
+// The groups of one 256-wide K block of the shared expert for two rows:
+// each group's value is dn_group's (its own fma chain from 0).
+template <int F>
+__device__ __forceinline__ void dn_groups2(const uint32_t (&w)[8][Fmt<F>::WORDS], const uint32_t* sc,
+                                           const uint32_t* src, const float* hca, const float* hcb,
+                                           float (&va)[KBLK / Fmt<F>::G], float (&vb)[KBLK / Fmt<F>::G]) {
+  constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
+  const PairMasks pk = pair_masks<F, 1>();
+#pragma unroll
+  for (int gi = 0; gi < GPS; ++gi) {
+    float ms, bm;
+    coef_reg<F>(sc, gi, ms, bm);
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    float Xa = 0.f, Xb = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < CPG; ++cc) {
+      const int c = gi * CPG + cc;
+      acc = dn_chunk<F>(w[c], pk, src + 16 * c, acc);
+      Xa += hca[c];
+      Xb += hcb[c];
+    }
+    va[gi] = fmaf(bm, Xa, fmaf(ms, acc[0] + acc[1], 0.f));
+    vb[gi] = fmaf(bm, Xb, fmaf(ms, acc[2] + acc[3], 0.f));
+  }
+}
+
+// One class's part of an exact-form down item (F: the class's format). The
+// block's slots are in LDS (sslot). Routed blocks: each wave's parts of all
+// the block's slots go to LDS (pr: [16 slots][tiles][DN_KS][64]) and one
+// barrier precedes the part sums; the shared expert's group values are
+// summed per pass (sgp). The next pass's h is loaded during this pass's
+// arithmetic when a wave has one K block (inter <= 512).
+template <int F>
+__device__ __forceinline__ void exact_down_item(const DecodeArgs& a, uint32_t (*hw)[264], float* pr, float* sgp,
+                                                const int* sslot, int e, int mc, int t, int ti, int kp, int lane) {
+  const bool shared = e == a.E;
+  const ExpertClass& ec = shared ? a.sh : a.rt;
+  const int k = a.k, H = a.H, inter = ec.inter;
+  const int nch = inter / 32, nkb = inter / KBLK;
+  constexpr int GPS = KBLK / Fmt<F>::G;
+  const int sng = inter / Fmt<F>::G, nwv = k * DN_KS;
+  const rsrc_t rs = make_rsrc(a.base + ec.base_off + (shared ? 0 : (uint64_t)e * ec.stride), ec.blk_bytes);
+  const uint32_t codes = (uint32_t)ec.dn_codes, scales = (uint32_t)ec.dn_scales;
+  uint32_t wr[8][Fmt<F>::WORDS], sc[4];
+  const int kb0 = min(kp, nkb - 1);
+  load_scales_rs<F>(rs, scale_voff<F>(lane), scales + (uint32_t)sblk_off<F>(t, kb0, nkb), sc);
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc)
+    load_chunk_rs<F>(rs, chunk_voff<F>(lane), codes + (uint32_t)chunk_off<F>(t, kb0 * 8 + cc, nch), wr[cc]);
+  // this lane's MFMA row slot: 0 / 1 the first row's hi / lo, 2 / 3 the second's
+  const uint32_t* src = hw[(lane >> 1) & 1] + ((lane & 1) ? 128 : 0);
+  const float* hca = reinterpret_cast<const float*>(hw[0] + 256);
+  const float* hcb = reinterpret_cast<const float*>(hw[1] + 256);
+  const bool one_kb = nkb <= DN_KS;
+  HBlk ha, hb;
+  if (one_kb && kp < nkb) {
+    ha = dn_load_block(a, (uint64_t)sslot[0], kp, lane);
+    hb = dn_load_block(a, (uint64_t)sslot[min(1, mc - 1)], kp, lane);
+  }
+  for (int i = 0; i < mc; i += 2) {
+    const int m = min(2, mc - i);
+    const int sa = sslot[i], sb = sslot[i + m - 1];
+    float oa = 0.f, ob = 0.f;
+    for (int kb = kp; kb < nkb; kb += DN_KS) {
+      if (one_kb) {
+        dn_store_block(ha, hw[0], lane);
+        dn_store_block(hb, hw[1], lane);
+        if (i + 2 < mc) {
+          ha = dn_load_block(a, (uint64_t)sslot[i + 2], kb, lane);
+          hb = dn_load_block(a, (uint64_t)sslot[min(i + 3, mc - 1)], kb, lane);
+        }
+      } else {
+        if (kb != kb0) {
+          load_scales_rs<F>(rs, scale_voff<F>(lane), scales + (uint32_t)sblk_off<F>(t, kb, nkb), sc);
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc)
+            load_chunk_rs<F>(rs, chunk_voff<F>(lane), codes + (uint32_t)chunk_off<F>(t, kb * 8 + cc, nch), wr[cc]);
+        }
+        dn_store_block(dn_load_block(a, (uint64_t)sa, kb, lane), hw[0], lane);
+        dn_store_block(dn_load_block(a, (uint64_t)sb, kb, lane), hw[1], lane);
+      }
+      if (!shared) {
+        dn_block2<F>(wr, sc, src, hca, hcb, oa, ob);
+      } else {
+        float va[GPS], vb[GPS];
+        dn_groups2<F>(wr, sc, src, hca, hcb, va, vb);
+#pragma unroll
+        for (int gi = 0; gi < GPS; ++gi) {
+          sgp[((0 * DX_TG + ti) * DX_MAXG + kb * GPS + gi) * 64 + lane] = va[gi];
+          sgp[((1 * DX_TG + ti) * DX_MAXG + kb * GPS + gi) * 64 + lane] = vb[gi];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (!shared) {
+      pr[((i * DX_TG + ti) * DN_KS + kp) * 64 + lane] = oa;
+      if (m > 1) pr[(((i + 1) * DX_TG + ti) * DN_KS + kp) * 64 + lane] = ob;
+      continue;
+    }
+    __syncthreads();
+    if (kp == 0) {
+      for (int v = 0; v < m; ++v) {
+        float o = 0.f;
+        for (int q = 0; q < nwv; ++q) {
+          float ps = 0.f;
+          for (int g = q; g < sng; g += nwv) ps += sgp[((v * DX_TG + ti) * DX_MAXG + g) * 64 + lane];
+          o += ps;
+        }
+        a.e_ws[(uint64_t)(v ? sb : sa) * H + 64 * t + lane] = o;
+      }
+    }
+    __syncthreads();
+  }
+  if (!shared) {
+    __syncthreads();
+    if (kp == 0) {
+      for (int sl = 0; sl < mc; ++sl) {
+        float o = 0.f;
+#pragma unroll
+        for (int q = 0; q < DN_KS; ++q) o += pr[((sl * DX_TG + ti) * DN_KS + q) * 64 + lane];
+        a.e_ws[(uint64_t)sslot[sl] * H + 64 * t + lane] = o;
+      }
+    }
+  }
+}
+
+template <int FR, int FS>
+__global__ __launch_bounds__(512) void k_exact_down(DecodeArgs a) {
+  __shared__ __align__(16) uint32_t hw_all[8][2][264];           // per wave: the pass's two rows' h parts
+  __shared__ float pr[GX_RB * DX_TG * DN_KS * 64];                // routed parts of the block's slots
+  __shared__ float sgp[2 * DX_TG * DX_MAXG * 64];                 // shared-expert group values of the pass
+  __shared__ int sslot[GX_RB];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ti = w >> 1, kp = w & 1;
+  const int ngr = (a.H / 64) / DX_TG;
+  const int n_items = *a.nblocks * ngr;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int* blk = a.blocks + 3 * (item / ngr);
+    const int e = blk[0], p0 = blk[1], mc = blk[2];
+    if (mc <= 0 || e < 0 || e > a.E) continue;
+    // the previous item's readers of sslot and pr are past this barrier
+    __syncthreads();
+    if (tid < mc) sslot[tid] = a.perm[p0 + tid];
+    __syncthreads();
+    const int t = (item % ngr) * DX_TG + ti;
+    if (e == a.E) exact_down_item<FS>(a, hw_all[w], pr, sgp, sslot, e, mc, t, ti, kp, lane);
+    else exact_down_item<FR>(a, hw_all[w], pr, sgp, sslot, e, mc, t, ti, kp, lane);
+  }
+}
+
+// y = sum_j p_j e_j + sigma e_shared per row, in k_dec_down's order (a slot
+// whose id is outside [0, E) adds p_j * 0); 4 columns per thread.
+__global__ __launch_bounds__(256) void k_exact_combine(DecodeArgs a) {
+  const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  const int H = a.H, k = a.k, H4 = H / 4;
+  if (i >= (uint64_t)a.R * H4) return;
+  const int r = (int)(i / H4), n = (int)(i % H4) * 4;
+  const float* e = a.e_ws + (uint64_t)r * (k + 1) * H + n;
+  float y[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < k; ++q) {
+    const int id = a.ids[r * k + q];
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (id >= 0 && id < a.E) v = *reinterpret_cast<const float4*>(e + (uint64_t)q * H);
+    const float pq = a.p[r * k + q];
+    y[0] = fmaf(pq, v.x, y[0]);
+    y[1] = fmaf(pq, v.y, y[1]);
+    y[2] = fmaf(pq, v.z, y[2]);
+    y[3] = fmaf(pq, v.w, y[3]);
+    if (a.tap_e) *reinterpret_cast<float4*>(a.tap_e + ((uint64_t)r * (k + 1) + q) * H + n) = v;
+  }
+  const float4 v = *reinterpret_cast<const float4*>(e + (uint64_t)k * H);
+  const float sg = a.sg[r];
+  y[0] = fmaf(sg, v.x, y[0]);
+  y[1] = fmaf(sg, v.y, y[1]);
+  y[2] = fmaf(sg, v.z, y[2]);
+  y[3] = fmaf(sg, v.w, y[3]);
+  if (a.tap_e) *reinterpret_cast<float4*>(a.tap_e + ((uint64_t)r * (k + 1) + k) * H + n) = v;
+  *reinterpret_cast<float4*>(a.y + (uint64_t)r * H + n) = make_float4(y[0], y[1], y[2], y[3]);
+}
+
 // ------------------------------------------------------------------ launch
 constexpr int GU_GRID = 256;   // persistent gate/up workgroups (a multiple of 8)
 
@@ -853,13 +1091,12 @@ static hipError_t launch_gateup(const DecodeArgs& a, hipStream_t s, hipEvent_t* 
   return hipGetLastError();
 }
 
-// The exact chunk form's experts: gate/up on the sort's expert blocks, then
-// k_dec_down over every row (its per-(row, column tile) workgroups read the
-// row's experts' down tiles; the rows of a tile share one XCD's L2).
+// The exact chunk form's experts: gate/up and down on the sort's expert
+// blocks, then the combine of every row.
 template <int FR, int FS>
 static hipError_t launch_exact_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   const int nw = std::min(8, a.H / KBLK);
-  const size_t gsm = decode_gu_smem(16, a.H), dsm = decode_dn_smem(a.k, a.Imax);
+  const size_t gsm = decode_gu_smem(GX_RB, a.H), dsm = decode_dn_smem(a.k, a.Imax);
   hipError_t err;
   if (a.act_fp16) {
     if ((err = allow_smem(k_exact_gateup<FR, FS, 1>, gsm)) != hipSuccess) return err;
@@ -869,8 +1106,12 @@ static hipError_t launch_exact_t(const DecodeArgs& a, hipStream_t s, hipEvent_t*
     launch_k(k_exact_gateup<FR, FS, 0>, dim3(GU_GRID), dim3(64 * nw), (uint32_t)gsm, s, ev, 0, a);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if ((err = allow_smem(k_dec_down<FR, FS>, dsm)) != hipSuccess) return err;
-  launch_k(k_dec_down<FR, FS>, dim3((a.H / 64) * a.R), dim3(64 * a.k * DN_KS), (uint32_t)dsm, s, ev, 2, a);
+  (void)dsm;
+  hipEvent_t e2[2] = {ev ? ev[2] : nullptr, nullptr}, e3[2] = {nullptr, ev ? ev[3] : nullptr};
+  launch_k(k_exact_down<FR, FS>, dim3(GU_GRID), dim3(512), 0, s, e2, 0, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const uint64_t n4 = (uint64_t)a.R * (a.H / 4);
+  launch_k(k_exact_combine, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, e3, 0, a);
   return hipGetLastError();
 }
 

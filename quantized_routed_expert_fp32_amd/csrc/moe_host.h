@@ -78,6 +78,7 @@ struct ExactWs {
   uint64_t meta_off;     // int32: block count, queue words, expert offsets [E+2]
   uint64_t perm_off;     // int32 [R*(k+1)]: expert-major position -> slot index r*(k+1)+j
   uint64_t blocks_off;   // int32 [max_blocks][3]: (expert, first position, rows <= 16)
+  uint64_t e_off;        // f32 [R*(k+1), H]: slot outputs of down, in slot order
   uint64_t total;
   int max_blocks;
 };

@@ -52,6 +52,7 @@ struct DecodeArgs {
   const int32_t* perm;
   const int32_t* blocks;
   const int32_t* nblocks;
+  float* e_ws;    // [R*(k+1), H] fp32 slot outputs (exact chunk form)
 };
 
 struct GroupedArgs {

@@ -458,6 +458,7 @@ ExactWs exact_ws_layout(const moe_layer_desc* d, int rows) {
   // an expert's run of c rows is ceil(c / 16) blocks: at most slots/16 + E + 1
   w.max_blocks = (int)(slots / 16 + E + 2);
   w.blocks_off = o; o = align256(o + (uint64_t)w.max_blocks * 3 * 4);
+  w.e_off = o; o = align256(o + slots * d->hidden * 4);
   w.total = o;
   return w;
 }
