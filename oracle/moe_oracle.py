@@ -22,10 +22,18 @@ Sources (page title, then section):
   * "Sage-1.5-W4A16" model card, Model details and Recipe: int4 symmetric
     weights, group 128, 16-bit compute, no activation quantisation; the
     shared-expert gate kept in BF16.
+  * same card, Performance, the decode speed table: a reference checkpoint
+    whose experts are MXFP4. The pages name the format and do not define it;
+    `dequant` takes the public OCP Microscaling (MX) v1.0 definition: blocks
+    of 32 FP4 E2M1 elements sharing one E8M0 scale (parity of real MXFP4
+    checkpoints against this layout is unpinned).
 Readings where the pages are silent (each listed in the design notes):
   * the weights are divided by their sum over the k picks (renormalised softmax);
   * the affine dequantisation is w = scale*q + bias per group, the symmetric
     one w = scale*(u - 8) for the stored nibble u;
+  * MXFP4: element i of a row is stream nibble i (low nibble first, as for
+    every other width), w = e2m1(nibble) * 2^(e - 127) for its block's
+    exponent byte e, e = 255 giving NaN; no bias term;
   * SwiGLU is h = silu(gate.x) * (up.x), silu(z) = z*sigmoid(z);
   * the shared gate is one row of H weights with no bias: sigma(row.x);
   * NaN orders above +inf above every finite value, then the lower id;
@@ -39,8 +47,8 @@ from typing import Callable, Dict, Optional, Tuple
 
 import numpy as np
 
-AFFINE, SYMMETRIC, DENSE = 0, 1, 2
-BF16, FP16 = 0, 1
+AFFINE, SYMMETRIC, DENSE, MXFP4 = 0, 1, 2, 3
+BF16, FP16, E8M0 = 0, 1, 2
 
 
 # ------------------------------------------------------------------ numbers
@@ -68,10 +76,35 @@ def unpack_codes(words: np.ndarray, bits: int, cols: int) -> np.ndarray:
     return np.packbits(stream, axis=2, bitorder="little")[:, :, 0].astype(np.int64)
 
 
+def e2m1_to_f64(code) -> np.ndarray:
+    """FP4 E2M1 elements (OCP MX v1.0) -> float64.
+
+    Bit 3 is the sign, bits 2..1 the exponent (bias 1), bit 0 the mantissa:
+    exponent 0 is subnormal (0 or 0.5), otherwise 2^(E-1) * (1 + m/2). The
+    eight magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+    """
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    ex, m = (c >> 1) & 3, (c & 1).astype(np.float64)
+    mag = np.where(ex == 0, 0.5 * m, np.exp2(ex - 1.0) * (1.0 + 0.5 * m))
+    return sign * mag
+
+
+def e8m0_to_f64(e) -> np.ndarray:
+    """E8M0 scale bytes (OCP MX v1.0) -> float64: 2^(e - 127), 0xFF is NaN."""
+    v = np.asarray(e, dtype=np.int64)
+    return np.where(v == 255, np.nan, np.exp2(v - 127.0))
+
+
 def dequant(fmt, codes, scales, biases, cols: int) -> np.ndarray:
     """Dense float64 matrix [rows, cols] of one quantised matrix."""
     if fmt.mode == DENSE:
         return half_bits_to_f64(codes, fmt.scale_dtype).reshape(-1, cols)
+    if fmt.mode == MXFP4:
+        if fmt.bits != 4 or fmt.group != 32 or fmt.scale_dtype != E8M0:
+            raise ValueError("MXFP4 is 4-bit E2M1 in blocks of 32 with E8M0 scales")
+        q = unpack_codes(codes, 4, cols)
+        return e2m1_to_f64(q) * e8m0_to_f64(scales)[:, np.arange(cols) // 32]
     q = unpack_codes(codes, fmt.bits, cols).astype(np.float64)
     gidx = np.arange(cols) // fmt.group
     s = half_bits_to_f64(scales, fmt.scale_dtype)[:, gidx]

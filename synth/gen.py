@@ -37,8 +37,8 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-AFFINE, SYMMETRIC, DENSE = 0, 1, 2
-BF16, FP16 = 0, 1
+AFFINE, SYMMETRIC, DENSE, MXFP4 = 0, 1, 2, 3
+BF16, FP16, E8M0 = 0, 1, 2
 
 KIND = dict(router=0, gate_row=1, gate=2, up=3, down=4, sh_gate=5, sh_up=6,
             sh_down=7, x=8, zipf=9)
@@ -46,10 +46,10 @@ KIND = dict(router=0, gate_row=1, gate=2, up=3, down=4, sh_gate=5, sh_up=6,
 
 @dataclass(frozen=True)
 class QFormat:
-    bits: int          # 3, 4, 8 (16 for DENSE)
-    group: int         # 64 or 128 (0 for DENSE)
-    mode: int          # AFFINE, SYMMETRIC, DENSE
-    scale_dtype: int   # BF16 or FP16 (value dtype for DENSE)
+    bits: int          # 2..8 (16 for DENSE)
+    group: int         # 32, 64 or 128 (0 for DENSE)
+    mode: int          # AFFINE, SYMMETRIC, DENSE, MXFP4
+    scale_dtype: int   # BF16, FP16 (value dtype for DENSE) or E8M0 (uint8 exponents)
 
 
 Q4G64 = QFormat(4, 64, AFFINE, BF16)
@@ -59,6 +59,7 @@ Q2G64 = QFormat(2, 64, AFFINE, BF16)
 Q5G64 = QFormat(5, 64, AFFINE, BF16)
 Q6G64 = QFormat(6, 64, AFFINE, BF16)
 S4G128 = QFormat(4, 128, SYMMETRIC, FP16)
+MX4G32 = QFormat(4, 32, MXFP4, E8M0)
 DENSE_BF16 = QFormat(16, 0, DENSE, BF16)
 
 
@@ -198,6 +199,11 @@ def _draw_qtensor(rng: np.random.Generator, fmt: QFormat, rows: int, cols: int,
     wpr = words_per_row(fmt, cols)
     codes = rng.integers(0, 1 << 32, size=(rows, wpr), dtype=np.uint32)
     ng = cols // fmt.group
+    if fmt.mode == MXFP4:
+        # every 4-bit code equally likely; block scales 2^-9 .. 2^-6 uniformly
+        # (weights of rms ~0.03, the order of the affine draws' ~0.06)
+        return QTensor(fmt, rows, cols, codes,
+                       rng.integers(127 - 9, 127 - 5, size=(rows, ng)).astype(np.uint8), None)
     s_bits = _to_bits(rng.uniform(0.002, 0.02, size=(rows, ng)) * mult, fmt.scale_dtype)
     if fmt.mode == SYMMETRIC:
         return QTensor(fmt, rows, cols, codes, s_bits, None)

@@ -5,6 +5,7 @@ words and values (tests/golden), a bit-by-bit pure-Python unpacker, exact
 integer arithmetic, brute force over all experts, and invariants.
 """
 import math
+from dataclasses import replace
 import os
 from fractions import Fraction
 
@@ -13,7 +14,8 @@ import pytest
 
 import oracle.moe_oracle as O
 import synth
-from synth.gen import Q2G64, Q3G64, Q4G64, Q5G64, Q6G64, Q8G64, S4G128, QFormat, QTensor
+from synth.gen import (MX4G32, Q2G64, Q3G64, Q4G64, Q5G64, Q6G64, Q8G64, S4G128, QFormat,
+                       QTensor)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -61,6 +63,60 @@ def test_hand_worked_dequant(case):
     x = np.zeros(cols)
     x[: int(c["ones_prefix"][0])] = 1.0
     assert float(W @ x) == float(c["dot"][0])
+
+
+@pytest.mark.parametrize("case", list(_blocks("mxfp4_words.txt")))
+def test_hand_worked_mxfp4(case):
+    """E2M1 elements and E8M0 block scales against hand-worked values."""
+    c = _blocks("mxfp4_words.txt")[case]
+    cols = int(c["cols"][0])
+    words = np.zeros((1, cols // 8), np.uint32)
+    for i, w in enumerate(c["words"]):
+        words[0, i] = int(w, 16)
+    s = np.array([[int(v, 16) for v in c["scales"]]], np.uint8)
+    W = O.dequant(MX4G32, words, s, None, cols)[0]
+    for item in c["w_at"]:
+        i, v = item.split(":")
+        got, want = W[int(i)], float(v)
+        if math.isnan(want):
+            assert math.isnan(got)
+        else:
+            assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want)
+    x = np.zeros(cols)
+    x[: int(c["ones_prefix"][0])] = 1.0
+    dot, want = float(W @ x), float(c["dot"][0])
+    assert (math.isnan(dot) and math.isnan(want)) or dot == want
+
+
+def test_e8m0_matches_torch_dtype():
+    """Every E8M0 byte against torch's float8_e8m0fnu conversion (a library
+    implementation of the same OCP type)."""
+    torch = pytest.importorskip("torch")
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = O.e8m0_to_f64(b)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def test_mxfp4_row_is_blockwise_scaled_codes():
+    """A random MXFP4 row equals its codes' values times its block scales:
+    scaling one block's exponent by +1 doubles exactly that block."""
+    rng = np.random.default_rng(11)
+    cols = 256
+    words = rng.integers(0, 1 << 32, size=(1, cols // 8), dtype=np.uint32)
+    s = rng.integers(100, 150, size=(1, cols // 32)).astype(np.uint8)
+    W = O.dequant(MX4G32, words, s, None, cols)[0]
+    s2 = s.copy()
+    s2[0, 3] += 1
+    W2 = O.dequant(MX4G32, words, s2, None, cols)[0]
+    blk = np.arange(cols) // 32
+    assert np.array_equal(W2[blk == 3], 2.0 * W[blk == 3])
+    assert np.array_equal(W2[blk != 3], W[blk != 3])
+    # magnitudes come from the 8-value set times the block scale
+    mags = np.abs(W) / np.exp2(s[0, blk].astype(np.float64) - 127.0)
+    assert set(np.unique(mags)) <= {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}
 
 
 def _py_unpack(words_row, bits, cols):
@@ -123,6 +179,28 @@ def test_integer_exact_projection(fmt):
         for i in range(cols):
             k = int(kexp[r, i // fmt.group])
             acc += Fraction(q[i] - off, 2 ** k) * int(x_int[i])
+        assert Fraction(got[r]) == acc
+
+
+def test_mxfp4_exact_projection():
+    """Scales 2^(e-127) for random e and small integer activations: every
+    projection is a dyadic rational, checked against exact sums of the
+    hand-worked E2M1 values (tests/golden/mxfp4_words.txt, all 16 codes)."""
+    table = {}
+    for item in _blocks("mxfp4_words.txt")["e2m1_table"]["w_at"][:16]:
+        i, v = item.split(":")
+        table[int(i)] = Fraction(float(v))
+    rng = np.random.default_rng(12)
+    rows, cols = 5, 256
+    words = rng.integers(0, 1 << 32, size=(rows, cols // 8), dtype=np.uint32)
+    e = rng.integers(117, 137, size=(rows, cols // 32)).astype(np.uint8)
+    x_int = rng.integers(-4, 5, size=cols)
+    got = O.dequant(MX4G32, words, e, None, cols) @ x_int.astype(np.float64)
+    for r in range(rows):
+        q = _py_unpack(words[r], 4, cols)
+        acc = Fraction(0)
+        for i in range(cols):
+            acc += table[q[i]] * Fraction(2) ** (int(e[r, i // 32]) - 127) * int(x_int[i])
         assert Fraction(got[r]) == acc
 
 
@@ -228,11 +306,14 @@ def _tiny(base_id, cfg_id, **kw):
     return synth.make_tiny_config(synth.CONFIGS[base_id], cfg_id=cfg_id, **kw)
 
 
-@pytest.mark.parametrize("base", [0, 2, 4])
+@pytest.mark.parametrize("base", [0, 2, 4, "mx"])
 def test_brute_force_all_experts(base):
     """Dense evaluation of every expert for every row, combined by a dense
     routing-weight matrix that is zero off the picks."""
-    spec = _tiny(base, 110 + base)
+    if base == "mx":
+        spec = replace(_tiny(2, 116), routed=MX4G32, shared=MX4G32)
+    else:
+        spec = _tiny(base, 110 + base)
     L = synth.make_layer(spec, 0)
     R = 9
     xb = synth.make_x(spec, 0, R)
