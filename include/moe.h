@@ -49,8 +49,8 @@ enum moe_status {
 };
 
 /* ----------------------------------------------------------------- formats */
-enum moe_mode { MOE_AFFINE = 0, MOE_SYMMETRIC = 1, MOE_DENSE = 2 };
-enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1 };
+enum moe_mode { MOE_AFFINE = 0, MOE_SYMMETRIC = 1, MOE_DENSE = 2, MOE_MXFP4 = 3 };
+enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1, MOE_E8M0 = 2 };
 
 /* Quantised format of one tensor class.
  * Accepted combinations (anything else is MOE_EUNSUPPORTED):
@@ -76,7 +76,14 @@ enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1 };
  *   {4, 128, MOE_SYMMETRIC, MOE_FP16} int4 symmetric, group 128, fp16 scales (W4A16)
  *       ("Sage-1.5-W4A16" model card, Model details)
  *   {16, 0, MOE_DENSE, MOE_BF16}      bf16 values (gate row only; the W4A16 export
- *       keeps the shared-expert gate in BF16: same card, Recipe) */
+ *       keeps the shared-expert gate in BF16: same card, Recipe)
+ *   {4, 32, MOE_MXFP4, MOE_E8M0}      MXFP4 (routed/shared only): FP4 E2M1 elements in
+ *       blocks of 32 sharing one E8M0 exponent byte e, w = e2m1 * 2^(e - 127), e = 255
+ *       NaN, no bias (the public OCP Microscaling v1.0 definition: the pages name an
+ *       MXFP4-expert checkpoint, "Sage-1.5-W4A16" model card, Performance, decode speed
+ *       table, and do not define it). Routed MXFP4 experts pair with an MXFP4 or 4-bit
+ *       affine shared expert; read by moe_forward, moe_forward_windows and
+ *       moe_forward_exact, refused by moe_experts_grouped (MOE_EUNSUPPORTED). */
 typedef struct moe_qformat {
   int32_t bits;
   int32_t group;
@@ -98,12 +105,13 @@ typedef struct moe_layer_desc {
  *           (element i in stream bits [bits*i, bits*i+bits), stream bit t is
  *           bit t%32 of word t/32). SYMMETRIC stores the nibble u = q + 8.
  *           DENSE: uint16 bf16 values [rows, cols].
- *   scales: uint16 bit patterns [rows, cols/group] (bf16 or fp16)
+ *   scales: uint16 bit patterns [rows, cols/group] (bf16 or fp16); for E8M0
+ *           uint8 exponent bytes [rows, cols/32]
  *   biases: uint16 bit patterns [rows, cols/group] (AFFINE only, else NULL)
  * Stacked routed experts carry a leading [n_experts] axis, experts contiguous. */
 typedef struct moe_qtensor {
   const void* codes;
-  const uint16_t* scales;
+  const void* scales;     /* uint16 entries, or uint8 for E8M0 */
   const uint16_t* biases;
 } moe_qtensor;
 
@@ -315,7 +323,8 @@ int moe_forward_windows_noalloc(const moe_layer* layer, const void* x, int rows,
  * workspace); taps as moe_experts_decode plus logits, kernel_events[0..7]
  * bracketing route, sort, gate/up and down.
  *   rows       1 .. 65536
- * Errors: MOE_EINVAL, MOE_ENOSPACE, MOE_EHIP. */
+ * Errors: MOE_EINVAL, MOE_ENOSPACE, MOE_EHIP; MOE_EUNSUPPORTED for a shared
+ * expert of more than 32 groups per row (an MXFP4 one wider than 1024). */
 int moe_forward_exact(const moe_layer* layer, const void* x, int rows, const float* logit_bias, int32_t* ids,
                       float* p, float* shared_gate, float* y, void* ws, uint64_t ws_bytes, const moe_taps* taps,
                       void* stream);

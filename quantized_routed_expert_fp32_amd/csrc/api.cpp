@@ -321,6 +321,13 @@ int moe_forward_exact(const moe_layer* layer, const void* x, int rows, const flo
   format_info(d->gate_row, TC_GATE_ROW, &fg);
   format_info(d->routed, TC_ROUTED, &fe);
   format_info(d->shared, TC_SHARED, &fs);
+  if (d->shared_inter / fs.group > 32) {
+    // the down kernel keeps at most 32 shared-expert group values per row
+    set_error("moe_forward_exact: shared expert " + fmt_name(d->shared) + " with shared_inter=" +
+              std::to_string(d->shared_inter) + " has more than 32 groups per row (moe_forward_windows "
+              "reads it)");
+    return MOE_EUNSUPPORTED;
+  }
   uint8_t* w = static_cast<uint8_t*>(ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = taps_events(taps);

@@ -650,8 +650,9 @@ __device__ __forceinline__ float dn_group(const uint32_t (*w)[Fmt<F>::WORDS], ui
   constexpr int CPG = Fmt<F>::G / 32;
   uint32_t sc[4] = {scw, scw, scw, scw};
   float ms, bm;
-  // the word holds this group's entry: affine one u32, symmetric the u16 at gi % 2
-  coef_reg<F>(sc, Fmt<F>::AFF ? 0 : (gi & 1), ms, bm);
+  // the word holds this group's entry: affine one u32, symmetric the u16 at
+  // gi % 2, MXFP4 the byte at gi % 4
+  coef_reg<F>(sc, Fmt<F>::AFF ? 0 : F == F_MX4 ? (gi & 3) : (gi & 1), ms, bm);
   const PairMasks pk = pair_masks<F, 1>();
   const uint32_t* src = dn_slot_src(hh, hl);
   f4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -666,11 +667,13 @@ __device__ __forceinline__ float dn_group(const uint32_t (*w)[Fmt<F>::WORDS], ui
 
 // Per-lane byte offset, inside its scale block, of the 4-byte word holding
 // group g's entry: affine the group's u32, symmetric the u32 holding both
-// fp16 scales of the block (the entry at half g % 2).
+// fp16 scales of the block (the entry at half g % 2), MXFP4 the u32 of the
+// lane's 8 exponent bytes that holds byte g % 8 (at byte g % 4).
 template <int F>
 __device__ __forceinline__ uint32_t group_word_voff(int g, int lane) {
   constexpr int GPS = KBLK / Fmt<F>::G;
   if constexpr (Fmt<F>::AFF) return (uint32_t)(lane * GPS + (g % GPS)) * 4;
+  else if constexpr (F == F_MX4) return (uint32_t)lane * 8 + (uint32_t)((g % GPS) >> 2) * 4;
   else return (uint32_t)lane * 4;
 }
 
@@ -852,7 +855,7 @@ __global__ __launch_bounds__(1024) void k_dec_down(DecodeArgs a) {
 // each the sum of the groups that wave takes (dn_group per group). Outputs
 // go to e_ws in slot order; k_exact_combine adds them as k_dec_down does.
 constexpr int DX_TG = 4;        // 64-column tiles per exact-form down item
-constexpr int DX_MAXG = 32;     // shared-expert groups kept per row and tile
+constexpr int DX_MAXG = 32;     // shared-expert groups kept per row and tile (the host refuses more)
 
 template <int F>
 __device__ __forceinline__ void dn_block2(const uint32_t (&w)[8][Fmt<F>::WORDS], const uint32_t* sc,
@@ -1129,8 +1132,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t
 
 template <int FR>
 static hipError_t launch_decode_s(int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
-  if constexpr (FR == F_Q5 || FR == F_Q6) {
-    // 5/6-bit routed experts: shared of the same width or 4-bit affine
+  if constexpr (FR == F_Q5 || FR == F_Q6 || FR == F_MX4) {
+    // 5/6-bit and MXFP4 routed experts: shared of the same format or 4-bit affine
     if (fs == FR) return launch_decode_t<FR, FR>(a, s, ev);
     if (fs == F_Q4) return launch_decode_t<FR, F_Q4>(a, s, ev);
   } else {
@@ -1147,7 +1150,7 @@ static hipError_t launch_decode_s(int fs, const DecodeArgs& a, hipStream_t s, hi
 
 template <int FR>
 static hipError_t launch_exact_s(int fs, const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
-  if constexpr (FR == F_Q5 || FR == F_Q6) {
+  if constexpr (FR == F_Q5 || FR == F_Q6 || FR == F_MX4) {
     if (fs == FR) return launch_exact_t<FR, FR>(a, s, ev);
     if (fs == F_Q4) return launch_exact_t<FR, F_Q4>(a, s, ev);
   } else {
@@ -1171,6 +1174,7 @@ hipError_t launch_exact_experts(int fr, int fs, const DecodeArgs& a, hipStream_t
     case F_Q2: return launch_exact_s<F_Q2>(fs, a, s, ev);
     case F_Q5: return launch_exact_s<F_Q5>(fs, a, s, ev);
     case F_Q6: return launch_exact_s<F_Q6>(fs, a, s, ev);
+    case F_MX4: return launch_exact_s<F_MX4>(fs, a, s, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -1184,6 +1188,7 @@ hipError_t launch_decode(int fr, int fs, const DecodeArgs& a, hipStream_t s, hip
     case F_Q2: return launch_decode_s<F_Q2>(fs, a, s, ev);
     case F_Q5: return launch_decode_s<F_Q5>(fs, a, s, ev);
     case F_Q6: return launch_decode_s<F_Q6>(fs, a, s, ev);
+    case F_MX4: return launch_decode_s<F_MX4>(fs, a, s, ev);
   }
   return hipErrorInvalidValue;
 }

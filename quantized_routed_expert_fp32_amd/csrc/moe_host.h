@@ -9,14 +9,14 @@
 namespace moe {
 
 // kernel-side format ids (match moe_kernels.h)
-enum { KF_Q4 = 0, KF_Q3 = 1, KF_Q8 = 2, KF_S4 = 3, KF_DENSE = 4, KF_Q2 = 5, KF_Q5 = 6, KF_Q6 = 7 };
+enum { KF_Q4 = 0, KF_Q3 = 1, KF_Q8 = 2, KF_S4 = 3, KF_DENSE = 4, KF_Q2 = 5, KF_Q5 = 6, KF_Q6 = 7, KF_MX4 = 8 };
 
 struct FmtInfo {
   int kid;      // kernel format id
   int bits;     // code width (16 for dense)
   int group;    // group size (0 for dense)
   int cb;       // bytes per lane per 32-code chunk
-  int scb;      // bytes per group scale entry
+  int scb;      // bytes per group scale entry in the kernel layout
   bool affine;
 };
 

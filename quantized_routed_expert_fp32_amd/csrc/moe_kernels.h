@@ -43,7 +43,7 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 // kernel-side format ids
-enum { F_Q4 = 0, F_Q3 = 1, F_Q8 = 2, F_S4 = 3, F_DENSE = 4, F_Q2 = 5, F_Q5 = 6, F_Q6 = 7 };
+enum { F_Q4 = 0, F_Q3 = 1, F_Q8 = 2, F_S4 = 3, F_DENSE = 4, F_Q2 = 5, F_Q5 = 6, F_Q6 = 7, F_MX4 = 8 };
 
 template <int F> struct Fmt;
 template <> struct Fmt<F_Q4> {
@@ -77,6 +77,13 @@ template <> struct Fmt<F_Q6> {
 };
 template <> struct Fmt<F_S4> {
   static constexpr int BITS = 4, G = 128, M = 16, CB = 16, WORDS = 4, SCB = 2;
+  static constexpr bool AFF = false;
+};
+template <> struct Fmt<F_MX4> {
+  // MXFP4: E2M1 elements whose pairs are the bytes of the canonical words,
+  // one E8M0 exponent byte per group of 32 (M is unused: the pair values are
+  // the elements themselves, the block scale multiplies the group's dot)
+  static constexpr int BITS = 4, G = 32, M = 1, CB = 16, WORDS = 4, SCB = 1;
   static constexpr bool AFF = false;
 };
 
@@ -214,6 +221,9 @@ template <int F> __device__ __forceinline__ void load_scales_rs(rsrc_t r, uint32
   if constexpr (Fmt<F>::AFF) {
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
     sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+  } else if constexpr (F == F_MX4) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    sc[0] = v.x; sc[1] = v.y;
   } else {
     sc[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
   }
@@ -397,9 +407,20 @@ template <int F> __device__ __forceinline__ void load_scales(const uint8_t* sblk
     sc[0] = *reinterpret_cast<const uint32_t*>(sblk + lane * 4);
   }
 }
-// Multiplier M*s and offset (b - M s) of group gi of a block from its words.
+// The E8M0 block scale 2^(e - 127) as fp32: e = 0 is the subnormal 2^-127,
+// e = 255 NaN (OCP MX v1.0).
+__device__ __forceinline__ float e8m0_to_f(uint32_t e) {
+  const uint32_t bits = e == 0u ? 0x00400000u : e == 255u ? 0x7FC00000u : e << 23;
+  return __uint_as_float(bits);
+}
+
+// Multiplier M*s and offset (b - M s) of group gi of a block from its words
+// (MXFP4: the block scale and 0; the pair values are the elements).
 template <int F> __device__ __forceinline__ void coef_reg(const uint32_t* sc, int gi, float& ms, float& bm) {
-  if constexpr (Fmt<F>::AFF) {
+  if constexpr (F == F_MX4) {
+    ms = e8m0_to_f((sc[gi >> 2] >> (8 * (gi & 3))) & 0xFFu);
+    bm = 0.f;
+  } else if constexpr (Fmt<F>::AFF) {
     const uint32_t v = sc[gi];
     const float s = bf16_to_f(v & 0xFFFFu), b = bf16_to_f(v >> 16);
     ms = (float)Fmt<F>::M * s;
@@ -644,6 +665,27 @@ __device__ __forceinline__ PairMasks pair_masks() {
 // 8-bit codes: with fp16 activations 16 pairs 1 + q/256; with bf16 ones
 // (7 mantissa bits) the low nibbles' 16 pairs in o[0..15] and the high
 // nibbles' in o[16..31], each 1 + n/16.
+// The two E2M1 elements of byte B of v as an fp16 (ACT16) or bf16 pair,
+// element 2B's low nibble in the low half.
+template <int ACT16>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t v, int b) {
+  if constexpr (ACT16) {
+    switch (b) {
+      case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0));
+      case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1));
+      case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2));
+      default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3));
+    }
+  } else {
+    switch (b) {
+      case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0));
+      case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1));
+      case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2));
+      default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3));
+    }
+  }
+}
+
 template <int F, int ACT16>
 __device__ __forceinline__ void unpack_pairs(const uint32_t* w, const PairMasks& k, uint32_t* o) {
   if constexpr (F == F_Q8) {
@@ -711,6 +753,12 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t* w, const PairMasks&
     const uint32_t t0 = ((w[0] >> (ACT16 ? 9 : 12)) & k.q0) | k.c;
     const uint32_t t1 = ((w[1] >> (ACT16 ? 8 : 11)) & k.q1) | t0;
     o[15] = ((w[2] >> (ACT16 ? 7 : 10)) & k.q2) | t1;
+  } else if constexpr (F == F_MX4) {
+    // pair p = byte p of the chunk (elements 2p in the low nibble, 2p + 1 in
+    // the high one), converted exactly by the FP4 unit at scale 1
+#pragma unroll
+    for (int p = 0; p < 16; ++p) o[p] = fp4_pair<ACT16>(w[p >> 2], p & 3);
+    (void)k;
   } else {   // 4-bit affine or symmetric
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -22,8 +22,9 @@ uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255u); }
 
 std::string fmt_name(const moe_qformat& f) {
   const char* m = f.mode == MOE_AFFINE ? "affine" : f.mode == MOE_SYMMETRIC ? "symmetric"
-                : f.mode == MOE_DENSE ? "dense" : "unknown-mode";
-  const char* s = f.scale_dtype == MOE_BF16 ? "bf16" : f.scale_dtype == MOE_FP16 ? "fp16" : "unknown-dtype";
+                : f.mode == MOE_DENSE ? "dense" : f.mode == MOE_MXFP4 ? "mxfp4" : "unknown-mode";
+  const char* s = f.scale_dtype == MOE_BF16 ? "bf16" : f.scale_dtype == MOE_FP16 ? "fp16"
+                : f.scale_dtype == MOE_E8M0 ? "e8m0" : "unknown-dtype";
   char buf[128];
   snprintf(buf, sizeof buf, "{bits=%d, group=%d, %s, %s}", f.bits, f.group, m, s);
   return buf;
@@ -47,6 +48,7 @@ bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* o) {
   const bool q6 = f.bits == 6 && f.group == 64 && f.mode == MOE_AFFINE && f.scale_dtype == MOE_BF16;
   const bool s4 = f.bits == 4 && f.group == 128 && f.mode == MOE_SYMMETRIC && f.scale_dtype == MOE_FP16;
   const bool dn = f.bits == 16 && f.mode == MOE_DENSE && f.scale_dtype == MOE_BF16;
+  const bool mx = f.bits == 4 && f.group == 32 && f.mode == MOE_MXFP4 && f.scale_dtype == MOE_E8M0;
   const bool expert = tc == TC_ROUTED || tc == TC_SHARED;
   bool ok = false;
   if (q4) { *o = {KF_Q4, 4, 64, 16, 4, true}; ok = true; }
@@ -57,9 +59,10 @@ bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* o) {
   else if (q6 && expert) { *o = {KF_Q6, 6, 64, 24, 4, true}; ok = true; }
   else if (s4) { *o = {KF_S4, 4, 128, 16, 2, false}; ok = true; }
   else if (dn && tc == TC_GATE_ROW) { *o = {KF_DENSE, 16, 0, 0, 0, false}; ok = true; }
+  else if (mx && expert) { *o = {KF_MX4, 4, 32, 16, 1, false}; ok = true; }
   if (!ok) {
     std::string acc = expert ? "{4,64,affine,bf16}, {3,64,affine,bf16}, {8,64,affine,bf16}, {2,64,affine,bf16}, "
-                               "{5,64,affine,bf16}, {6,64,affine,bf16}, {4,128,symmetric,fp16}"
+                               "{5,64,affine,bf16}, {6,64,affine,bf16}, {4,128,symmetric,fp16}, {4,32,mxfp4,e8m0}"
                      : tc == TC_ROUTER ? "{4,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}"
                      : "{4,64,affine,bf16}, {8,64,affine,bf16}, {4,128,symmetric,fp16}, {16,0,dense,bf16}";
     set_error(std::string(class_name(tc)) + " format " + fmt_name(f) +
@@ -113,6 +116,14 @@ int validate_desc(const moe_layer_desc* d) {
     snprintf(buf, sizeof buf, "routed %d-bit with shared %d-bit experts unsupported: 5- and 6-bit experts pair "
              "with a shared expert of the same width or 4-bit affine", rb, sb);
     set_error(buf); return MOE_EUNSUPPORTED;
+  }
+  // MXFP4 experts: routed MXFP4 with an MXFP4 or 4-bit affine shared expert
+  const bool mx_r = d->routed.mode == MOE_MXFP4, mx_s = d->shared.mode == MOE_MXFP4;
+  if ((mx_r || mx_s) && !(mx_r && (mx_s || q4_s))) {
+    set_error("routed " + fmt_name(d->routed) + " with shared " + fmt_name(d->shared) +
+              " experts unsupported: MXFP4 routed experts pair with an MXFP4 or 4-bit affine "
+              "shared expert");
+    return MOE_EUNSUPPORTED;
   }
   return MOE_OK;
 }
@@ -263,14 +274,36 @@ static inline void pack_chunk(int kid, const uint32_t* canon, uint32_t* o) {
     case KF_Q6:
       q6_chunk(canon, o);
       break;
+    case KF_MX4:
+      // byte b of the chunk holds elements 2b (low nibble) and 2b + 1: the
+      // canonical words are the kernel's pair order as they stand
+      for (int w = 0; w < 4; ++w) o[w] = canon[w];
+      break;
   }
 }
 
 struct SrcMat {
   const uint32_t* codes;   // [rows, wpr]
-  const uint16_t* scales;  // [rows, ng]
+  const uint8_t* scales;   // [rows, ng] entries of src_scale_bytes(f) bytes
   const uint16_t* biases;  // [rows, ng] or null
 };
+
+// Bytes per source scale entry: bf16 / fp16 2, E8M0 1.
+static int src_scale_bytes(const FmtInfo& f) { return f.kid == KF_MX4 ? 1 : 2; }
+
+// Kernel-layout scale entry of group g: affine s | b << 16, else the source
+// entry's bytes as they stand.
+static void put_scale(const FmtInfo& f, const uint8_t* sr, const uint16_t* br, int g, uint8_t* dst) {
+  const int sb = src_scale_bytes(f);
+  if (f.affine) {
+    uint16_t sv;
+    memcpy(&sv, sr + (size_t)g * 2, 2);
+    const uint32_t v = (uint32_t)sv | ((uint32_t)br[g] << 16);
+    memcpy(dst, &v, 4);
+  } else {
+    memcpy(dst, sr + (size_t)g * sb, (size_t)sb);
+  }
+}
 
 // Writes one matrix [O, K] in the tile layout. rowmap(t, lane) -> (which
 // source matrix 0/1, source row).
@@ -297,19 +330,11 @@ static void pack_matrix(const FmtInfo& f, int O, int K, const SrcMat* srcs, RowM
           memcpy(blk + lane * f.cb, o, f.cb);
         }
       }
-      const uint16_t* sr = s.scales + (uint64_t)row * ng;
+      const uint8_t* sr = s.scales + (uint64_t)row * ng * src_scale_bytes(f);
       const uint16_t* br = s.biases ? s.biases + (uint64_t)row * ng : nullptr;
       for (int kb = 0; kb < nkb; ++kb) {
         uint8_t* sb = dst_scales + (((uint64_t)t * nkb + kb) * 64 + lane) * (uint64_t)(gpb * f.scb);
-        for (int gi = 0; gi < gpb; ++gi) {
-          const int g = kb * gpb + gi;
-          if (f.affine) {
-            const uint32_t v = (uint32_t)sr[g] | ((uint32_t)br[g] << 16);
-            memcpy(sb + gi * 4, &v, 4);
-          } else {
-            memcpy(sb + gi * 2, &sr[g], 2);
-          }
-        }
+        for (int gi = 0; gi < gpb; ++gi) put_scale(f, sr, br, kb * gpb + gi, sb + gi * f.scb);
       }
     }
   }
@@ -328,14 +353,8 @@ static void pack_row(const FmtInfo& f, int K, const moe_qtensor& t, uint8_t* dst
     pack_chunk(f.kid, rw + (uint64_t)c * f.bits, o);
     memcpy(dst_codes + (uint64_t)c * f.cb, o, f.cb);
   }
-  for (int g = 0; g < ng; ++g) {
-    if (f.affine) {
-      const uint32_t v = (uint32_t)t.scales[g] | ((uint32_t)t.biases[g] << 16);
-      memcpy(dst_scales + g * 4, &v, 4);
-    } else {
-      memcpy(dst_scales + g * 2, &t.scales[g], 2);
-    }
-  }
+  for (int g = 0; g < ng; ++g)
+    put_scale(f, static_cast<const uint8_t*>(t.scales), t.biases, g, dst_scales + g * f.scb);
 }
 
 static bool check_src(const moe_qtensor& t, const FmtInfo& f, const char* name) {
@@ -352,16 +371,18 @@ static void pack_expert(const FmtInfo& f, int H, int I, const moe_qtensor& g, co
                         const moe_mat_off& dno) {
   const uint64_t wg = (uint64_t)I * H * f.bits / 32, sg = (uint64_t)I * (H / f.group);
   const uint64_t wd = (uint64_t)H * I * f.bits / 32, sd = (uint64_t)H * (I / f.group);
+  const uint64_t sb = (uint64_t)src_scale_bytes(f);
+  const auto sp = [](const moe_qtensor& t) { return static_cast<const uint8_t*>(t.scales); };
   SrcMat gu_src[2] = {
-      {static_cast<const uint32_t*>(g.codes) + e * wg, g.scales + e * sg, g.biases ? g.biases + e * sg : nullptr},
-      {static_cast<const uint32_t*>(u.codes) + e * wg, u.scales + e * sg, u.biases ? u.biases + e * sg : nullptr}};
+      {static_cast<const uint32_t*>(g.codes) + e * wg, sp(g) + e * sg * sb, g.biases ? g.biases + e * sg : nullptr},
+      {static_cast<const uint32_t*>(u.codes) + e * wg, sp(u) + e * sg * sb, u.biases ? u.biases + e * sg : nullptr}};
   pack_matrix(f, 2 * I, H, gu_src,
               [](int t, int lane, int* which, int* row) {
                 *which = lane >= 32;
                 *row = 32 * t + (lane & 31);
               },
               blk + gu.codes, blk + gu.scales);
-  SrcMat d_src[1] = {{static_cast<const uint32_t*>(dn.codes) + e * wd, dn.scales + e * sd,
+  SrcMat d_src[1] = {{static_cast<const uint32_t*>(dn.codes) + e * wd, sp(dn) + e * sd * sb,
                       dn.biases ? dn.biases + e * sd : nullptr}};
   pack_matrix(f, H, I, d_src,
               [](int t, int lane, int* which, int* row) {
@@ -397,7 +418,7 @@ int pack_layer_host(const moe_layer_desc* d, const moe_layer_src* src, void* hos
   uint8_t* base = static_cast<uint8_t*>(host_dst);
   memset(base, 0, L.bytes);
   const int H = d->hidden, E = d->n_experts, I = d->inter, Is = d->shared_inter;
-  SrcMat rsrc[1] = {{static_cast<const uint32_t*>(src->router.codes), src->router.scales,
+  SrcMat rsrc[1] = {{static_cast<const uint32_t*>(src->router.codes), static_cast<const uint8_t*>(src->router.scales),
                      src->router.biases}};
   pack_matrix(fr, E, H, rsrc,
               [](int t, int lane, int* which, int* row) { *which = 0; *row = 64 * t + lane; },

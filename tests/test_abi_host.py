@@ -14,7 +14,7 @@ import pytest
 import oracle.moe_oracle as O
 import synth
 from synth import to_abi
-from synth.gen import Q2G64, Q3G64, Q4G64, Q5G64, Q6G64
+from synth.gen import MX4G32, Q2G64, Q3G64, Q4G64, Q5G64, Q6G64, S4G128
 from dataclasses import replace
 
 qr = pytest.importorskip("quantized_routed_expert_fp32_amd")
@@ -91,6 +91,31 @@ def test_wide_expert_pairings(routed, shared, ok):
             B.pack_size(d)
 
 
+@pytest.mark.parametrize("routed,shared,ok", [(MX4G32, MX4G32, True), (MX4G32, Q4G64, True),
+                                               (Q4G64, MX4G32, False), (MX4G32, S4G128, False),
+                                               (MX4G32, Q3G64, False)])
+def test_mxfp4_expert_pairings(routed, shared, ok):
+    """MXFP4 routed experts pair with an MXFP4 or 4-bit affine shared expert;
+    other pairings are refused by name before anything is built."""
+    _lib()
+    spec = replace(synth.CONFIGS[0], routed=routed, shared=shared)
+    d = B.layer_desc(*to_abi.desc_args(spec))
+    if ok:
+        assert B.pack_size(d) > 0
+    else:
+        with pytest.raises(B.MoeError, match="MOE_EUNSUPPORTED.*MXFP4 routed experts pair"):
+            B.pack_size(d)
+
+
+@pytest.mark.parametrize("cls", ["router", "gate_row"])
+def test_mxfp4_router_and_gate_row_refused(cls):
+    _lib()
+    args = list(to_abi.desc_args(synth.CONFIGS[0]))
+    args[{"router": 6, "gate_row": 7}[cls]] = (4, 32, 3, 2)
+    with pytest.raises(B.MoeError, match="MOE_EUNSUPPORTED.*mxfp4"):
+        B.pack_size(B.layer_desc(*args))
+
+
 @pytest.mark.parametrize("field,val", [("hidden", 300), ("n_experts", 100), ("top_k", 9),
                                        ("inter", 384)])
 def test_unsupported_shapes_refused(field, val):
@@ -111,15 +136,18 @@ def test_workspace_limits():
 
 
 # ------------------------------------------------------------ layout reader
-def _read_chunk_codes(lane_words, bits):
+def _read_chunk_codes(lane_words, bits, mx=False):
     """32 codes of one lane's chunk, from the pair arrangement in include/moe.h
-    and the kernel header: pair p holds codes 2p (low half) and 2p+1 (high half)."""
+    and the kernel header: pair p holds codes 2p (low half) and 2p+1 (high half);
+    MXFP4 pair p is byte p (code 2p in its low nibble)."""
     q = np.zeros(32, np.int64)
     w = [int(v) for v in lane_words]
     for p in range(16):
         for hi in (0, 1):
             i = 2 * p + hi
-            if bits == 4:
+            if mx:
+                q[i] = (w[p // 4] >> (8 * (p % 4) + 4 * hi)) & 0xF
+            elif bits == 4:
                 q[i] = (w[p // 4] >> (16 * hi + 4 * (p % 4))) & 0xF
             elif bits == 2:
                 q[i] = (w[p // 8] >> (16 * hi + 2 * (p % 8))) & 3
@@ -144,10 +172,10 @@ def _read_chunk_codes(lane_words, bits):
     return q
 
 
-def _read_matrix(buf, codes_off, scales_off, bits, group, affine, O_rows, K, rowmap):
+def _read_matrix(buf, codes_off, scales_off, bits, group, affine, O_rows, K, rowmap, mx=False):
     cb = 4 * bits
     nch, nkb, gpb = K // 32, K // 256, 256 // group
-    scb = 4 if affine else 2
+    scb = 4 if affine else 1 if mx else 2
     q = np.zeros((O_rows, K), np.int64)
     s = np.zeros((O_rows, K // group), np.uint16)
     b = np.zeros((O_rows, K // group), np.uint16)
@@ -161,10 +189,10 @@ def _read_matrix(buf, codes_off, scales_off, bits, group, affine, O_rows, K, row
                                           buf[blk + 1024 + lane * 16: blk + 1024 + lane * 16 + 16]])
                 else:
                     raw = buf[blk + lane * cb: blk + lane * cb + cb]
-                q[row, 32 * c: 32 * c + 32] = _read_chunk_codes(raw.view("<u4"), bits)
+                q[row, 32 * c: 32 * c + 32] = _read_chunk_codes(raw.view("<u4"), bits, mx)
             for kb in range(nkb):
                 sb = scales_off + ((t * nkb + kb) * 64 + lane) * gpb * scb
-                ent = buf[sb: sb + gpb * scb].view("<u4" if affine else "<u2")
+                ent = buf[sb: sb + gpb * scb].view("<u4" if affine else "<u1" if mx else "<u2")
                 for gi in range(gpb):
                     g = kb * gpb + gi
                     if affine:
@@ -175,13 +203,13 @@ def _read_matrix(buf, codes_off, scales_off, bits, group, affine, O_rows, K, row
     return q, s, b
 
 
-@pytest.mark.parametrize("base", [0, 2, 4, "q2", "q5", "q6"])
+@pytest.mark.parametrize("base", [0, 2, 4, "q2", "q5", "q6", "mx"])
 def test_packed_layout_decodes_to_canonical(base):
     _lib()
-    if base in ("q2", "q5", "q6"):     # routed and shared experts of that width
-        f = {"q2": Q2G64, "q5": Q5G64, "q6": Q6G64}[base]
+    if base in ("q2", "q5", "q6", "mx"):     # routed and shared experts of that format
+        f = {"q2": Q2G64, "q5": Q5G64, "q6": Q6G64, "mx": MX4G32}[base]
         src = replace(synth.CONFIGS[0], routed=f, shared=f)
-        cfg_id = 210 + f.bits
+        cfg_id = 210 + f.bits + (10 if base == "mx" else 0)
     else:
         src, cfg_id = synth.CONFIGS[base], 200 + base
     spec = synth.make_tiny_config(src, cfg_id=cfg_id, hidden=512,
@@ -190,11 +218,11 @@ def test_packed_layout_decodes_to_canonical(base):
     buf, lc = B.pack_layer_host(_desc(spec), to_abi.tensors(Lh))
     H, I = spec.hidden, spec.inter
     f = spec.routed
-    aff = f.mode == O.AFFINE
+    aff, mx = f.mode == O.AFFINE, f.mode == O.MXFP4
     for e in (0, 37, 63):
         blk = lc.experts_off + e * lc.expert_stride
         q, s, b = _read_matrix(buf, blk + lc.gu.codes, blk + lc.gu.scales, f.bits, f.group, aff,
-                               2 * I, H, lambda t, l: 64 * t + l)
+                               2 * I, H, lambda t, l: 64 * t + l, mx)
         # tile t, lane l < 32 -> gate row 32t+l ; lane >= 32 -> up row 32t+l-32
         perm = np.array([32 * (r // 64) + (r % 64) % 32 + (I if r % 64 >= 32 else 0)
                          for r in range(2 * I)])
@@ -206,7 +234,7 @@ def test_packed_layout_decodes_to_canonical(base):
         if aff:
             assert np.array_equal(b, np.concatenate([Lh.gate.biases[e], Lh.up.biases[e]])[perm])
         q, s, b = _read_matrix(buf, blk + lc.dn.codes, blk + lc.dn.scales, f.bits, f.group, aff,
-                               H, I, lambda t, l: 64 * t + l)
+                               H, I, lambda t, l: 64 * t + l, mx)
         assert np.array_equal(q, O.unpack_codes(Lh.down.codes[e], f.bits, I))
         assert np.array_equal(s, Lh.down.scales[e])
     fr = spec.router
