@@ -28,6 +28,7 @@ sleep so that the kernels run back to back (host launch gaps do not count).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -49,9 +50,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def scale_entry_bytes(fmt):
+    """Packed bytes per group: affine scale + bias 4, symmetric 2, MXFP4 1."""
+    return {0: 4, 1: 2, 3: 1}[fmt.mode]
+
+
 def expert_bytes(spec, fmt, inter):
     """Packed bytes of one expert: gate/up and down (codes + scale words)."""
-    scb = 4 if fmt.mode == 0 else 2
+    scb = scale_entry_bytes(fmt)
     gu = 2 * inter * spec.hidden * fmt.bits // 8 + 2 * inter * (spec.hidden // fmt.group) * scb
     dn = spec.hidden * inter * fmt.bits // 8 + spec.hidden * (inter // fmt.group) * scb
     return gu, dn
@@ -60,6 +66,8 @@ def expert_bytes(spec, fmt, inter):
 def fmt_name(f):
     """Short text name of a weight format, e.g. 'affine 4-bit g64 bf16 scale/bias'."""
     dt = "bf16" if f.scale_dtype == 0 else "fp16"
+    if f.mode == 3:
+        return f"mxfp4 e2m1 g{f.group} e8m0 scale"
     if f.mode == 2:
         return f"dense {dt}"
     if f.mode == 1:
@@ -69,7 +77,7 @@ def fmt_name(f):
 
 def router_bytes(spec):
     f, g = spec.router, spec.gate_row
-    scb = 4 if f.mode == 0 else 2
+    scb = scale_entry_bytes(f)
     r = spec.n_experts * spec.hidden * f.bits // 8 + spec.n_experts * (spec.hidden // f.group) * scb
     if g.mode == 2:
         gr = spec.hidden * 2
@@ -744,6 +752,16 @@ def main():
             workloads[f"c2_{r2}rows"] = bench_decode(spec2, layers2, r2, args.steps, args.warmup, B, synth,
                                                     torch, dev, stream, sleeper, graph=not args.no_graph)
         del layers2
+        torch.cuda.empty_cache()
+        # MXFP4 routed and shared experts, the headline shapes and router, over
+        # 10 distinct layers (4 GB of weights: not cache-resident)
+        spec_mx = dataclasses.replace(spec, cfg_id=340, name="decode-8rows-mxfp4-experts",
+                                      routed=synth.MX4G32, shared=synth.MX4G32)
+        layers_mx, _ = build_layers(spec_mx, args.layers or 10, B, to_abi, synth)
+        workloads["f4_mxfp4_8rows"] = bench_decode(spec_mx, layers_mx, R, args.steps, args.warmup, B, synth,
+                                                   torch, dev, stream, sleeper, graph=not args.no_graph,
+                                                   tag="decode-8rows-mxfp4-experts over 10 layers")
+        del layers_mx
         torch.cuda.empty_cache()
     for name, r in prefill.items():
         workloads[name] = r
