@@ -82,8 +82,9 @@ enum moe_dtype { MOE_BF16 = 0, MOE_FP16 = 1, MOE_E8M0 = 2 };
  *       NaN, no bias (the public OCP Microscaling v1.0 definition: the pages name an
  *       MXFP4-expert checkpoint, "Sage-1.5-W4A16" model card, Performance, decode speed
  *       table, and do not define it). Routed MXFP4 experts pair with an MXFP4 or 4-bit
- *       affine shared expert; read by moe_forward, moe_forward_windows and
- *       moe_forward_exact, refused by moe_experts_grouped (MOE_EUNSUPPORTED). */
+ *       affine shared expert; read by the decode path, moe_forward_windows and
+ *       moe_forward_exact, and by moe_experts_grouped when the layer carries
+ *       MOE_LAYER_MX_FP16 (block exponents 104..140 or 255; MOE_EUNSUPPORTED otherwise). */
 typedef struct moe_qformat {
   int32_t bits;
   int32_t group;
@@ -139,7 +140,14 @@ typedef struct moe_layer {
   moe_mat_off gu, dn;                      /* inside a routed expert block */
   uint64_t shared_off;
   moe_mat_off sh_gu, sh_dn;                /* inside the shared expert block */
+  uint32_t flags;                          /* MOE_LAYER_* bits, set by moe_pack_layer_host */
 } moe_layer;
+
+/* moe_layer.flags: MOE_LAYER_MX_FP16 = every E8M0 block exponent of the
+ * layer's MXFP4 experts (routed and shared) lies in 104..140 or is 255, so
+ * each element times its block scale is exact in fp16 (the grouped GEMMs'
+ * operand type); moe_experts_grouped reads MXFP4 experts only then. */
+enum moe_layer_flags { MOE_LAYER_MX_FP16 = 1 };
 
 /* Optional per-projection dumps (device memory, fp32), for tests and
  * accuracy reports; any member may be NULL. Layouts use slot index

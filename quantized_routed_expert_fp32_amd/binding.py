@@ -57,7 +57,7 @@ class LayerC(C.Structure):
                 ("gate_row_off", C.c_uint64), ("gate_row_scale_off", C.c_uint64),
                 ("experts_off", C.c_uint64), ("expert_stride", C.c_uint64),
                 ("gu", MatOffC), ("dn", MatOffC), ("shared_off", C.c_uint64),
-                ("sh_gu", MatOffC), ("sh_dn", MatOffC)]
+                ("sh_gu", MatOffC), ("sh_dn", MatOffC), ("flags", C.c_uint32)]
 
 
 class TapsC(C.Structure):

@@ -415,8 +415,15 @@ int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const i
       return MOE_EUNSUPPORTED;
     if (!grouped_pair_supported(fr.kid, fs.kid)) {
       set_error("moe_experts_grouped: routed " + fmt_name(layer->d.routed) + " with shared " +
-                fmt_name(layer->d.shared) + " is not read by the grouped GEMMs (a 2-, 5-, 6- or 8-bit routed "
-                "format needs a shared expert of the same width or 4-bit affine); moe_forward_windows reads it");
+                fmt_name(layer->d.shared) + " is not read by the grouped GEMMs (a 2-, 5-, 6-, 8-bit or MXFP4 "
+                "routed format needs a shared expert of the same format or 4-bit affine); moe_forward_windows "
+                "reads it");
+      return MOE_EUNSUPPORTED;
+    }
+    if ((fr.kid == KF_MX4 || fs.kid == KF_MX4) && !(layer->flags & MOE_LAYER_MX_FP16)) {
+      set_error("moe_experts_grouped: MXFP4 experts whose block exponents leave 104..140 (or a layer not "
+                "packed by moe_pack_layer_host) are not exact in the grouped GEMMs' fp16 operands; "
+                "moe_forward_windows and moe_forward_exact read them");
       return MOE_EUNSUPPORTED;
     }
   }

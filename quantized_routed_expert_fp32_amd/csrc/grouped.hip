@@ -253,6 +253,16 @@ __device__ __forceinline__ void deq_word<F_S4>(const uint32_t* wv, half2v s16, h
   for (int i = 0; i < 4; ++i) o[i] = as_u((as_h2(p[i]) - off) * s16);
 }
 
+// MXFP4: the word's 4 bytes are the pairs (consecutive k, low nibble first);
+// the FP4 converter scales each by the block scale 2^(e - 127) and rounds to
+// fp16, exactly for the exponents the grouped call accepts (104..140, 255).
+__device__ __forceinline__ void deq_word_mx(uint32_t v, float scale, uint32_t* o) {
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, 0));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, 1));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, 2));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, 3));
+}
+
 // Widths read through the generic B layout (the chunk block copied to LDS
 // as it is packed, every lane unpacking its row's whole chunk).
 template <int F> constexpr bool gen_fmt() { return F == F_Q2 || F == F_Q5 || F == F_Q6 || F == F_Q8; }
@@ -330,7 +340,7 @@ template <int FR, int FS> constexpr int stage_bytes() { return 2 * A_STAGE + 4 *
 // chunk, and the A fragments follow the same k. The 3-bit rows hold a
 // chunk's codes across all 3 words, so their lanes take the full row.
 template <int F> struct BFrag {
-  static constexpr bool HALF = F == F_Q4 || F == F_S4;
+  static constexpr bool HALF = F == F_Q4 || F == F_S4 || F == F_MX4;
   static constexpr int W = HALF ? 2 : Fmt<F>::WORDS;   // words per chunk per lane
 };
 
@@ -388,7 +398,12 @@ __device__ __forceinline__ void issue_b(uint8_t* bw, const uint8_t* blk, uint32_
     }
   }
   const uint8_t* sb = blk + scales + sblk_off<F>(T, kk0 / KBLK, nkb);
-  if constexpr (Fmt<F>::AFF) {
+  if constexpr (F == F_MX4) {
+    // the row's 8 exponent bytes of the block: the word of groups 4 h .. 4 h + 3
+    // that holds this step's two (h = the step's half of the block)
+    __builtin_amdgcn_global_load_lds(sb + lane * 8 + ((kk0 % KBLK) / 128) * 4,
+                                     (__attribute__((address_space(3))) void*)(bw + b_scale_off<F>()), 4, 0, 0);
+  } else if constexpr (Fmt<F>::AFF) {
     const int gi = (kk0 % KBLK) / Fmt<F>::G;
     __builtin_amdgcn_global_load_lds(sb + (lane * GPS + gi) * 4,
                                      (__attribute__((address_space(3))) void*)(bw + b_scale_off<F>()), 4, 0, 0);
@@ -465,7 +480,9 @@ __device__ __forceinline__ void read_b(BStage<F>& st, uint32_t bw, int col, int 
                    "s_waitcnt lgkmcnt(0)"
                    : "=&v"(c00), "=&v"(c10), "=&v"(c01), "=&v"(c11), "=&v"(s0), "=&v"(s1)
                    : "v"(ac), "v"(bw + 2048 + col * 4));
-      const int sh = 16 * ((step & 3) >> 1);
+      // symmetric: the fp16 scale of the step's group (half (step % 4) / 2);
+      // MXFP4: the exponent bytes of the step's two chunks in the low half
+      const int sh = F == F_MX4 ? 16 * (step & 1) : 16 * ((step & 3) >> 1);
       s0 >>= sh;
       s1 >>= sh;
     }
@@ -532,8 +549,14 @@ template <int F, int MT>
 __device__ __forceinline__ void step_mma(f16v_t (&acc)[MT][2], const BStage<F>& st, uint32_t abuf, int col,
                                          int hsel) {
   half2v s16[2], b2[2];
+  float mxs[2][2];   // MXFP4: block scale per n-tile and chunk
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
+    if constexpr (F == F_MX4) {
+      mxs[nt][0] = e8m0_to_f(st.sr[nt] & 0xFFu);
+      mxs[nt][1] = e8m0_to_f((st.sr[nt] >> 8) & 0xFFu);
+      continue;
+    }
     float sc, bi;
     if constexpr (Fmt<F>::AFF) {
       sc = bf16_to_f(st.sr[nt] & 0xFFFFu);
@@ -556,7 +579,8 @@ __device__ __forceinline__ void step_mma(f16v_t (&acc)[MT][2], const BStage<F>& 
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       uint32_t d[4];
-      if constexpr (BFrag<F>::HALF) deq_word<F>(&st.w[nt][c][j], s16[nt], b2[nt], d);
+      if constexpr (F == F_MX4) deq_word_mx(st.w[nt][c][j], mxs[nt][c], d);
+      else if constexpr (BFrag<F>::HALF) deq_word<F>(&st.w[nt][c][j], s16[nt], b2[nt], d);
       else deq_chunk_half<F>(st.w[nt][c], 2 * j + hsel, s16[nt], b2[nt], d);
       bf[nt] = __builtin_bit_cast(half8v_t, *reinterpret_cast<uint4*>(d));
     }
@@ -826,6 +850,7 @@ hipError_t launch_grouped(int fr, int fs, const GroupedArgs& a, hipStream_t s, h
     case F_Q5: return launch_grouped_s<F_Q5>(fs, a, s, ev);
     case F_Q6: return launch_grouped_s<F_Q6>(fs, a, s, ev);
     case F_Q8: return launch_grouped_s<F_Q8>(fs, a, s, ev);
+    case F_MX4: return launch_grouped_s<F_MX4>(fs, a, s, ev);
   }
   return hipErrorInvalidValue;
 }

@@ -27,8 +27,8 @@ enum TensorClass { TC_ROUTER = 0, TC_GATE_ROW, TC_ROUTED, TC_SHARED };
 // format is not read by the kernels for that tensor class.
 bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* out);
 // The routed / shared format pair (KF_ ids) the grouped GEMMs read: the 3-
-// and 4-bit formats in any pairing, the 2-, 5-, 6- and 8-bit ones with a
-// shared expert of the same width or 4-bit affine.
+// and 4-bit formats in any pairing, the 2-, 5-, 6-, 8-bit and MXFP4 ones with
+// a shared expert of the same format or 4-bit affine.
 bool grouped_pair_supported(int fr, int fs);
 
 // Validates a descriptor (shapes + formats). Sets the error on failure.

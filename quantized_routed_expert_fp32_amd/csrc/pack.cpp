@@ -74,7 +74,8 @@ bool format_info(const moe_qformat& f, TensorClass tc, FmtInfo* o) {
 bool grouped_pair_supported(int fr, int fs) {
   const auto low = [](int f) { return f == KF_Q4 || f == KF_Q3 || f == KF_S4; };
   if (low(fr)) return low(fs);
-  return (fr == KF_Q2 || fr == KF_Q5 || fr == KF_Q6 || fr == KF_Q8) && (fs == fr || fs == KF_Q4);
+  return (fr == KF_Q2 || fr == KF_Q5 || fr == KF_Q6 || fr == KF_Q8 || fr == KF_MX4) &&
+         (fs == fr || fs == KF_Q4);
 }
 
 int validate_desc(const moe_layer_desc* d) {
@@ -175,7 +176,18 @@ int compute_layout(const moe_layer_desc* d, moe_layer* L) {
   off += block(fs, Is, &L->sh_gu, &L->sh_dn);
   L->bytes = off;
   L->dev = nullptr;
+  L->flags = 0;
   return MOE_OK;
+}
+
+// True when every E8M0 byte of an MXFP4 tensor's scales (n entries) lies in
+// 104..140 or is 255: e2m1 * 2^(e - 127) is then a multiple of 2^(e - 128)
+// >= 2^-24 and at most 6 * 2^13 < 65504, exact in fp16 (NaN for 255).
+static bool mx_fp16_exact(const moe_qtensor& t, uint64_t n) {
+  const uint8_t* e = static_cast<const uint8_t*>(t.scales);
+  for (uint64_t i = 0; i < n; ++i)
+    if (e[i] != 255 && (e[i] < 104 || e[i] > 140)) return false;
+  return true;
 }
 
 // ------------------------------------------------------------------ repack
@@ -437,6 +449,18 @@ int pack_layer_host(const moe_layer_desc* d, const moe_layer_src* src, void* hos
   for (auto& t : th) t.join();
   pack_expert(fs, H, Is, src->sh_gate, src->sh_up, src->sh_down, 0, base + L.shared_off, L.sh_gu,
               L.sh_dn);
+  if (fe.kid == KF_MX4 || fs.kid == KF_MX4) {
+    bool ok = true;
+    if (fe.kid == KF_MX4) {
+      const uint64_t n = (uint64_t)E * I * (H / 32);
+      ok = mx_fp16_exact(src->gate, n) && mx_fp16_exact(src->up, n) && mx_fp16_exact(src->down, n);
+    }
+    if (ok && fs.kid == KF_MX4) {
+      const uint64_t n = (uint64_t)Is * (H / 32);
+      ok = mx_fp16_exact(src->sh_gate, n) && mx_fp16_exact(src->sh_up, n) && mx_fp16_exact(src->sh_down, n);
+    }
+    if (ok) L.flags |= MOE_LAYER_MX_FP16;
+  }
   *out = L;
   return MOE_OK;
 }

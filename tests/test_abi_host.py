@@ -262,3 +262,26 @@ def test_null_source_refused():
     t["down"] = (t["down"][0], None, t["down"][2])
     with pytest.raises(B.MoeError, match="down"):
         B.pack_layer_host(_desc(spec), t)
+
+
+@pytest.mark.parametrize("patch,flag", [(None, 1), (104, 1), (140, 1), (255, 1), (103, 0), (141, 0), (0, 0)])
+def test_mxfp4_fp16_flag(patch, flag):
+    """The packer marks an MXFP4 layer MOE_LAYER_MX_FP16 exactly when every
+    block exponent of its experts lies in 104..140 or is 255 (one exponent of
+    the shared down projection is patched)."""
+    _lib()
+    spec = synth.make_tiny_config(replace(synth.CONFIGS[0], routed=MX4G32, shared=MX4G32), cfg_id=230,
+                                  hidden=512, n_experts=64, top_k=4, inter=256, shared_inter=256)
+    Lh = synth.make_layer(spec, 0)
+    if patch is not None:
+        Lh.sh_down.scales[17, 2] = patch
+    _, lc = B.pack_layer_host(_desc(spec), to_abi.tensors(Lh))
+    assert lc.flags == flag
+
+
+def test_fp16_flag_clear_without_mxfp4():
+    _lib()
+    spec = synth.make_tiny_config(synth.CONFIGS[0], cfg_id=231, hidden=512, n_experts=64, top_k=4,
+                                  inter=256, shared_inter=256)
+    _, lc = B.pack_layer_host(_desc(spec), to_abi.tensors(synth.make_layer(spec, 0)))
+    assert lc.flags == 0
