@@ -318,6 +318,120 @@ __device__ __forceinline__ void gu_pass(const DecodeArgs& a, const GuItem& it, c
   rb ^= 1;   // the other buffer next: its readers passed this barrier
 }
 
+// gu_slice_mfma for NG groups of 4 rows at once (the exact chunk form):
+// each chunk is unpacked once for every group, and each group's
+// accumulators, chunk sums and folds are gu_slice_mfma's in its order, so
+// every row's result is the same bit for bit. Group g's rows are LDS rows
+// 4 g .. 4 g + 3 of the block (a row past m reads row 0; its results are
+// not used); lane l supplies row slot l % 4.
+template <int F, int ACT16, int W, int NG>
+__device__ __forceinline__ void gu_slice_mfma_n(const uint32_t (*w)[W], const uint32_t* sc, const uint32_t* xl,
+                                                const float* cs, int H, int m, int lane, int sl, f4v (&out)[NG]) {
+  constexpr int GPS = KBLK / Fmt<F>::G, CPG = Fmt<F>::G / 32;
+  constexpr bool NIB = F == F_Q8 && !ACT16;   // two nibble sets, two sums
+  const int nch = H / 32;
+  const PairMasks pk = pair_masks<F, ACT16>();
+#pragma unroll
+  for (int gi = 0; gi < GPS; ++gi) {
+    float ms, bm;
+    coef_reg<F>(sc, gi, ms, bm);
+    f4v acc[NG], acc2[NG];
+    float X[NG][4];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[g][i] = 0.f;
+        acc2[g][i] = 0.f;
+        X[g][i] = 0.f;
+      }
+#pragma unroll
+    for (int cc = 0; cc < CPG; ++cc) {
+      const int c = gi * CPG + cc;
+      uint32_t v[NIB ? 32 : 16], wc[Fmt<F>::WORDS];
+#pragma unroll
+      for (int q = 0; q < Fmt<F>::WORDS; ++q) {
+        wc[q] = w[c][q];
+        asm volatile("" : "+v"(wc[q]));
+      }
+      unpack_pairs<F, ACT16>(wc, pk, v);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int lr = 4 * g + (lane & 3);
+        const uint32_t* xr = xl + (uint64_t)(lr < m ? lr : 0) * (H / 2);
+        const uint4* q = reinterpret_cast<const uint4*>(xr + (sl * KBLK + 32 * c) / 2);
+        uint32_t av[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 tq = q[u];
+          av[4 * u] = tq.x; av[4 * u + 1] = tq.y; av[4 * u + 2] = tq.z; av[4 * u + 3] = tq.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          acc[g] = mfma4<ACT16>(av[2 * i], av[2 * i + 1], v[2 * i], v[2 * i + 1], acc[g]);
+        if constexpr (NIB) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            acc2[g] = mfma4<ACT16>(av[2 * i], av[2 * i + 1], v[16 + 2 * i], v[16 + 2 * i + 1], acc2[g]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          X[g][i] += cs[(r < m ? r : 0) * nch + sl * 8 + c];
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if constexpr (NIB) {
+        const float m16 = ms * (1.0f / 16.0f), b16 = bm - m16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          out[g][i] = fmaf(b16, X[g][i], fmaf(ms, acc2[g][i], fmaf(m16, acc[g][i], out[g][i])));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[g][i] = fmaf(bm, X[g][i], fmaf(ms, acc[g][i], out[g][i]));
+      }
+    }
+  }
+}
+
+// Rows per exact-form pass: 16 while the partial sums fit beside the block's
+// activations in LDS (hidden <= 3072), else 8.
+__host__ __device__ constexpr int exact_pass_rows(int H) { return H <= 3072 ? 16 : 8; }
+
+// One exact-form pass: the block's rows i0 .. i0 + m - 1 (m <= the pass
+// rows, NG = ceil(m / 4) groups) against the wave's K slices; the partials
+// of every wave to LDS, one barrier, then wave v finishes rows v, v + nw, ..
+// (gu_finish), and a second barrier before the partials are rewritten.
+template <int F, int ACT16, int NG, typename SB>
+__device__ __forceinline__ void exact_pass(const DecodeArgs& a, const GuItem& it, const SB& b, const uint32_t* xl,
+                                           const float* cs, float* red, int wv, int nw, int lane,
+                                           const int* sslot, int m) {
+  const int H = a.H, nch = H / 32, nsl = H / KBLK, k = a.k;
+  constexpr int W = sizeof(b.w[0]) / sizeof(uint32_t);
+  f4v out[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) out[g] = f4v{0.f, 0.f, 0.f, 0.f};
+  gu_slice_mfma_n<F, ACT16, W, NG>(b.w, b.sc, xl, cs, H, m, lane, wv, out);
+  for (int sl = wv + nw; sl < nsl; sl += nw) {     // hidden > 256 * waves: further slices in place
+    SB c2;
+    load_slice<F>(it.r, it.codes, it.scales, it.tl, sl, nch, nsl, lane, c2);
+    gu_slice_mfma_n<F, ACT16, W, NG>(c2.w, c2.sc, xl, cs, H, m, lane, sl, out);
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (4 * g + v < m) red[((4 * g + v) * nw + wv) * 64 + lane] = out[g][v];
+  __syncthreads();
+  for (int r = wv; r < m; r += nw) {
+    const int slot = sslot[r];
+    gu_finish(a, red + r * nw * 64, nw, slot / (k + 1), slot % (k + 1), it.t, lane);
+  }
+  __syncthreads();
+}
+
 // The rows of an item in passes of up to 4 (slot order = pick order); all
 // rows of the batch sit in LDS, so a slot's LDS row is its row.
 template <int F, int ACT16, typename SB>
@@ -485,27 +599,36 @@ __global__ __launch_bounds__(512) void k_dec_gateup(DecodeArgs a) {
 constexpr int GU_TG = 4;   // layout tiles per exact-form item
 constexpr int GX_RB = 16;  // rows per expert block
 
-// One tile of an exact-form item through gu_pass: the
-// block's mc slots in passes of 4; a slot's LDS row is its place in the block.
+// One tile of an exact-form item: the block's mc rows in passes of
+// exact_pass_rows(H) (one pass for a block of 16 at hidden <= 3072); a
+// row's LDS row is its place in the block. Layers with 5-, 6- or 8-bit
+// experts, whose wider unpack leaves no registers for more groups, take
+// passes of 4 (WIDE).
+template <int F, int ACT16, bool WIDE, typename SB>
+__device__ __forceinline__ void exact_tile_f(const DecodeArgs& a, const GuItem& it, const SB& b, const uint32_t* xl,
+                                             const float* cs, float* red, int wv, int nw, int lane,
+                                             const int* sslot, int mc) {
+  const int rp = WIDE ? 4 : exact_pass_rows(a.H);
+  for (int i = 0; i < mc; i += rp) {
+    const int m = min(rp, mc - i);
+    const uint32_t* xb = xl + (uint64_t)i * (a.H / 2);
+    const float* cb = cs + (uint64_t)i * (a.H / 32);
+    if constexpr (WIDE) {
+      exact_pass<F, ACT16, 1>(a, it, b, xb, cb, red, wv, nw, lane, sslot + i, m);
+    } else {
+      if (m > 8) exact_pass<F, ACT16, 4>(a, it, b, xb, cb, red, wv, nw, lane, sslot + i, m);
+      else if (m > 4) exact_pass<F, ACT16, 2>(a, it, b, xb, cb, red, wv, nw, lane, sslot + i, m);
+      else exact_pass<F, ACT16, 1>(a, it, b, xb, cb, red, wv, nw, lane, sslot + i, m);
+    }
+  }
+}
 template <int FR, int FS, int ACT16, typename SB>
 __device__ __forceinline__ void exact_tile(const DecodeArgs& a, const GuItem& it, const SB& b, const uint32_t* xl,
-                                           const float* cs, float* red, int& rb, int wv, int nw, int lane,
+                                           const float* cs, float* red, int wv, int nw, int lane,
                                            const int* sslot, int mc) {
-  const int k = a.k;
-  for (int i = 0; i < mc; i += 4) {
-    const int m = min(4, mc - i);
-    int lr[4], rr[4], jj[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int l = (v < m) ? i + v : i;
-      const int slot = sslot[l];
-      lr[v] = l;
-      rr[v] = slot / (k + 1);
-      jj[v] = slot % (k + 1);
-    }
-    if (it.shared) gu_pass<FS, ACT16>(a, it, b, xl, cs, red, rb, wv, nw, lane, lr, rr, jj, m);
-    else gu_pass<FR, ACT16>(a, it, b, xl, cs, red, rb, wv, nw, lane, lr, rr, jj, m);
-  }
+  constexpr bool WIDE = FR == F_Q5 || FR == F_Q6 || FR == F_Q8 || FS == F_Q5 || FS == F_Q6 || FS == F_Q8;
+  if (it.shared) exact_tile_f<FS, ACT16, WIDE>(a, it, b, xl, cs, red, wv, nw, lane, sslot, mc);
+  else exact_tile_f<FR, ACT16, WIDE>(a, it, b, xl, cs, red, wv, nw, lane, sslot, mc);
 }
 
 template <int FR, int FS, int ACT16>
@@ -518,7 +641,7 @@ __global__ __launch_bounds__(512) void k_exact_gateup(DecodeArgs a) {
   const int nch = H / 32, nsl = H / KBLK;
   uint32_t* xl = reinterpret_cast<uint32_t*>(smem);
   float* cs = reinterpret_cast<float*>(smem + (size_t)RB * H * 2);
-  float* red = cs + RB * nch;                  // [2][4][nw][64]
+  float* red = cs + RB * nch;                  // [pass rows][nw][64]
   __shared__ int sslot[GX_RB];                  // the block's slot indexes
 
   const int Tmax = 2 * a.Imax / 64, ngr = (Tmax + GU_TG - 1) / GU_TG;
@@ -526,7 +649,6 @@ __global__ __launch_bounds__(512) void k_exact_gateup(DecodeArgs a) {
   const GuCls rcl = gu_cls(a.rt), scl = gu_cls(a.sh);
   constexpr int SW = Fmt<FR>::WORDS > Fmt<FS>::WORDS ? Fmt<FR>::WORDS : Fmt<FS>::WORDS;
   SliceBuf<SW> A, B;
-  int rb = 0;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int* blk = a.blocks + 3 * (item / ngr);
     const int e = blk[0], p0 = blk[1], mc = blk[2];
@@ -579,12 +701,12 @@ __global__ __launch_bounds__(512) void k_exact_gateup(DecodeArgs a) {
       nx.t = nx.tl = t + 1;
       if (t + 1 < t1) gu_issue<FR, FS>(nx, wv, nch, nsl, lane, B);
       it.t = it.tl = t;
-      exact_tile<FR, FS, ACT16>(a, it, A, xl, cs, red, rb, wv, nw, lane, sslot, mc);
+      exact_tile<FR, FS, ACT16>(a, it, A, xl, cs, red, wv, nw, lane, sslot, mc);
       if (t + 1 >= t1) break;
       nx.t = nx.tl = t + 2;
       if (t + 2 < t1) gu_issue<FR, FS>(nx, wv, nch, nsl, lane, A);
       it.t = it.tl = t + 1;
-      exact_tile<FR, FS, ACT16>(a, it, B, xl, cs, red, rb, wv, nw, lane, sslot, mc);
+      exact_tile<FR, FS, ACT16>(a, it, B, xl, cs, red, wv, nw, lane, sslot, mc);
     }
   }
 }
@@ -1099,7 +1221,9 @@ static hipError_t launch_gateup(const DecodeArgs& a, hipStream_t s, hipEvent_t* 
 template <int FR, int FS>
 static hipError_t launch_exact_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   const int nw = std::min(8, a.H / KBLK);
-  const size_t gsm = decode_gu_smem(GX_RB, a.H), dsm = decode_dn_smem(a.k, a.Imax);
+  const size_t gsm = (size_t)GX_RB * a.H * 2 + (size_t)GX_RB * (a.H / 32) * 4 +
+                     (size_t)exact_pass_rows(a.H) * std::min(8, a.H / KBLK) * 64 * 4;
+  const size_t dsm = decode_dn_smem(a.k, a.Imax);
   hipError_t err;
   if (a.act_fp16) {
     if ((err = allow_smem(k_exact_gateup<FR, FS, 1>, gsm)) != hipSuccess) return err;
