@@ -237,14 +237,15 @@ def prefill_algorithmic(spec, ids):
                 flop_router=f_router)
 
 
-def bench_prefill(cfg_id, steps, warmup, B, to_abi, synth, torch, dev, stream, sleeper,
+def bench_prefill(cfg, steps, warmup, B, to_abi, synth, torch, dev, stream, sleeper,
                   n_sets=N_PREFILL_SETS, windows=False, keep_host=False):
     """One prompt chunk through one layer: route + grouped experts. The timed
     replays rotate through n_sets distinct weight sets (each with its own
     activations), so the touched experts come from HBM, not the MALL. Whole
     chunks are timed as HIP graph replays; per-phase times from events inside
-    the library's launches, queued behind a GPU sleep."""
-    spec = synth.CONFIGS[cfg_id]
+    the library's launches, queued behind a GPU sleep. cfg: a config id or a
+    ConfigSpec."""
+    spec = synth.CONFIGS[cfg] if isinstance(cfg, int) else cfg
     R, k, H, E = spec.rows[0], spec.top_k, spec.hidden, spec.n_experts
     desc = B.layer_desc(*to_abi.desc_args(spec))
     layers, biases, xs, host = [], [], [], None
@@ -724,6 +725,13 @@ def main():
                                  windows=args.windows, keep_host=not args.no_cpu_baseline)
             prefill[f"c{c}"] = r
             host_prefill[c] = h
+            torch.cuda.empty_cache()
+        if not args.no_extra:
+            # MXFP4 routed and shared experts at the 512-row chunk's shapes
+            spec_mx = dataclasses.replace(synth.CONFIGS[3], cfg_id=346, name="prefill-512rows-mxfp4-experts",
+                                          routed=synth.MX4G32, shared=synth.MX4G32)
+            prefill["f4_mxfp4_512rows"], _ = bench_prefill(spec_mx, args.steps, args.warmup, B, to_abi, synth,
+                                                           torch, dev, stream, sleeper)
             torch.cuda.empty_cache()
         if args.prefill_only:
             print(json.dumps({"prefill": prefill}), flush=True)
