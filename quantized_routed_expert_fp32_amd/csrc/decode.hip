@@ -205,7 +205,7 @@ __device__ __forceinline__ f4v gu_slice_mfma(const uint32_t (*w)[W], const uint3
 #pragma unroll
     for (int cc = 0; cc < CPG; ++cc) {
       const int c = gi * CPG + cc;
-      uint32_t v[NIB ? 32 : 16], av[16], wc[Fmt<F>::WORDS];
+      uint32_t v[16], av[16], wc[Fmt<F>::WORDS];
 #pragma unroll
       for (int q = 0; q < Fmt<F>::WORDS; ++q) {
         wc[q] = w[c][q];
@@ -213,7 +213,10 @@ __device__ __forceinline__ f4v gu_slice_mfma(const uint32_t (*w)[W], const uint3
         // instead of being hoisted out of the pass loop for every chunk
         asm volatile("" : "+v"(wc[q]));
       }
-      unpack_pairs<F, ACT16>(wc, pk, v);
+      // two nibble sets: the low set's dots, then the high set unpacked into
+      // the same registers (each accumulator keeps its order)
+      if constexpr (NIB) unpack_q8_nibbles<0>(wc, pk, v);
+      else unpack_pairs<F, ACT16>(wc, pk, v);
       const uint4* q = reinterpret_cast<const uint4*>(xr + (sl * KBLK + 32 * c) / 2);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -223,9 +226,10 @@ __device__ __forceinline__ f4v gu_slice_mfma(const uint32_t (*w)[W], const uint3
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc = mfma4<ACT16>(av[2 * i], av[2 * i + 1], v[2 * i], v[2 * i + 1], acc);
       if constexpr (NIB) {
+        unpack_q8_nibbles<1>(wc, pk, v);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          acc2 = mfma4<ACT16>(av[2 * i], av[2 * i + 1], v[16 + 2 * i], v[16 + 2 * i + 1], acc2);
+          acc2 = mfma4<ACT16>(av[2 * i], av[2 * i + 1], v[2 * i], v[2 * i + 1], acc2);
       }
       X0 += xs0[sl * 8 + c];
       X1 += xs1[sl * 8 + c];

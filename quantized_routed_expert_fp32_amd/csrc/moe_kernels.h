@@ -662,6 +662,19 @@ __device__ __forceinline__ PairMasks pair_masks() {
   asm volatile("" : "+s"(k.m), "+s"(k.q0), "+s"(k.q1), "+s"(k.q2), "+v"(k.c));
   return k;
 }
+// One nibble set of 8-bit codes for bf16 activations (HI = 0: the low
+// nibbles, 1: the high ones), 16 pairs 1 + n/16: unpack_pairs' o[0..15] or
+// o[16..31], for code that runs one set's dots before unpacking the other.
+template <int HI>
+__device__ __forceinline__ void unpack_q8_nibbles(const uint32_t* w, const PairMasks& k, uint32_t* o) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t v = w[i];
+    o[2 * i] = ((HI ? v >> 1 : v << 3) & k.m) | k.c;
+    o[2 * i + 1] = ((HI ? v >> 9 : v >> 5) & k.m) | k.c;
+  }
+}
+
 // 8-bit codes: with fp16 activations 16 pairs 1 + q/256; with bf16 ones
 // (7 mantissa bits) the low nibbles' 16 pairs in o[0..15] and the high
 // nibbles' in o[16..31], each 1 + n/16.
