@@ -369,7 +369,7 @@ def bench_prefill(cfg, steps, warmup, B, to_abi, synth, torch, dev, stream, slee
 
 
 def bench_decode(spec, layers, R, steps, warmup, B, synth, torch, dev, stream, sleeper,
-                 graph=True, tag=""):
+                 graph=True, tag="", sample_clock=False):
     """Decode: R rows through every layer of `layers` (route, then the decode
     experts), 4 activation sets rotating. Whole steps are timed as HIP graph
     replays; per-kernel times from events inside the library's launches."""
@@ -432,6 +432,21 @@ def bench_decode(spec, layers, R, steps, warmup, B, synth, torch, dev, stream, s
         torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
     mean_step_bytes = float(np.mean([step_bytes[s % NX] for s in range(steps)]))
+    # per-step spread, from a separate pass with an event between steps
+    with torch.cuda.stream(stream):
+        se = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        se[0].record(stream)
+        for s in range(steps):
+            run(s)
+            se[s + 1].record(stream)
+        torch.cuda.synchronize()
+    per_step = np.array([se[i].elapsed_time(se[i + 1]) for i in range(steps)])
+    spread = {q: float(np.percentile(per_step, v)) * 1e3 / L for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+    clock = None
+    if sample_clock:
+        # shader clock sampled from sysfs while ~0.2 s of steps replay
+        reps = max(1, int(200.0 / max(ms_step, 1e-3)))
+        clock = sampled_sclk(lambda: [run(s) for s in range(reps)], torch, stream)
 
     # per kernel: events around route, gate/up, down + combine of every layer
     nk = max(1, min(steps, 20))
@@ -451,7 +466,8 @@ def bench_decode(spec, layers, R, steps, warmup, B, synth, torch, dev, stream, s
     achieved = gu_bytes / (kus[1] * 1e-6) / 1e9
     res = {
         "workload": spec.name, "rows": R, "layers": L, "ms_per_step": ms_step,
-        "us_per_layer": ms_step * 1e3 / L, "tokens_per_s": R * L / (ms_step / 1e3),
+        "us_per_layer": ms_step * 1e3 / L, "us_per_layer_spread": spread,
+        "tokens_per_s": R * L / (ms_step / 1e3),
         "algorithmic_bytes_per_step": mean_step_bytes,
         "gbs": mean_step_bytes / ms_step / 1e6, "frac_hbm": mean_step_bytes / ms_step / 1e6 / HBM_PEAK_GBS,
         "kernel_us": {"route": kus[0], "decode_gateup": kus[1], "decode_down_combine": kus[2]},
@@ -459,6 +475,8 @@ def bench_decode(spec, layers, R, steps, warmup, B, synth, torch, dev, stream, s
         "mean_unique_experts": float(uniq.mean()),
         "timing": "hip graph replay" if graphs else "eager",
     }
+    if clock is not None:
+        res["sclk_mhz"] = clock
     log(f"[bench] decode {tag or spec.name} rows={R} layers={L}: {res['us_per_layer']:.2f} us/layer, "
         f"{res['tokens_per_s']:.0f} tokens/s, step HBM {res['gbs']:.0f} GB/s "
         f"({100 * res['frac_hbm']:.1f}%); route {kus[0]:.2f}, gate/up {kus[1]:.2f} ({achieved:.0f} GB/s), "
@@ -507,6 +525,68 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n}), flush=True)
 
 
+def read_sclk():
+    """Current shader clock in MHz from the amdgpu sysfs table (the level
+    marked '*'), or None where no table is readable."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if "*" in line:
+                    return float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def sampled_sclk(work, torch, stream):
+    """Samples read_sclk() every ~2 ms on a host thread while `work` enqueues
+    and the GPU runs it; min / median / max MHz, or the reason there is none."""
+    import threading
+    vals, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = read_sclk()
+            if v is None:
+                return
+            vals.append(v)
+            time.sleep(0.002)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    with torch.cuda.stream(stream):
+        work()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not vals:
+        return {"note": "no readable pp_dpm_sclk on this host"}
+    return {"min": min(vals), "median": float(np.median(vals)), "max": max(vals), "samples": len(vals)}
+
+
+def mfma_ceiling(torch, dev, stream):
+    """Dense fp16 MFMA rate measured with back-to-back 32x32x16 MFMAs on every
+    SIMD (libmoe_ceilings.so, built beside libmoe.so), TFLOP/s."""
+    import ctypes as C
+    path = os.path.join(ROOT, "quantized_routed_expert_fp32_amd", "libmoe_ceilings.so")
+    if not os.path.exists(path):
+        return None
+    lib = C.CDLL(path)
+    lib.moe_ceiling_mfma_f16.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                         C.POINTER(C.c_double)]
+    lib.moe_ceiling_mfma_f16.restype = C.c_int
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 8 * n_cu                    # 8 waves per CU: two per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    tf = C.c_double(0.0)
+    st = lib.moe_ceiling_mfma_f16(blocks, 2000, 10, C.c_void_p(out.data_ptr()),
+                                  C.c_void_p(stream.cuda_stream), C.byref(tf))
+    if st != 0:
+        raise RuntimeError(f"moe_ceiling_mfma_f16 failed: hipError {st}")
+    return tf.value
+
+
 def measured_ceilings(torch, dev, stream):
     """A practical HBM ceiling beside the published peak: a plain 1 GiB device
     copy (read + write bytes over its time), timed with events on the bench
@@ -529,6 +609,7 @@ def measured_ceilings(torch, dev, stream):
         out["copy_1GiB_gbs"] = 2 * n * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
     del a, b
     torch.cuda.empty_cache()
+    out["mfma_f16_32x32x16_tflops"] = mfma_ceiling(torch, dev, stream)
     return out
 
 
@@ -743,7 +824,7 @@ def main():
     default_workload = L == spec.layers
     layers, host = build_layers(spec, L, B, to_abi, synth, keep_host=1)
     head = bench_decode(spec, layers, R, args.steps, args.warmup, B, synth, torch, dev, stream, sleeper,
-                        graph=not args.no_graph)
+                        graph=not args.no_graph, sample_clock=True)
     workloads = {}
     if not args.no_extra:
         # one row through the same 40 layers (the one-row workload's shapes
@@ -775,7 +856,9 @@ def main():
         workloads[name] = r
 
     ceilings = measured_ceilings(torch, dev, stream)
-    log(f"[bench] measured ceiling: copy {ceilings['copy_1GiB_gbs']:.0f} GB/s")
+    mf = ceilings.get("mfma_f16_32x32x16_tflops")
+    log(f"[bench] measured ceilings: copy {ceilings['copy_1GiB_gbs']:.0f} GB/s, 32x32x16 f16 MFMA loop "
+        + (f"{mf:.0f} TFLOP/s" if mf else "not built") + f"; sclk during the headline steps {head.get('sclk_mhz')}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -819,6 +902,8 @@ def main():
                      "traffic": stored_traffic("k_dec_gateup") if default_workload else None,
                      "mean_us": head["kernel_us"]["decode_gateup"],
                      "bytes_per_launch": head["gateup_bytes_per_launch"]},
+        "us_per_layer_spread": head["us_per_layer_spread"],
+        "sclk_mhz": head.get("sclk_mhz"),
         "step_hbm": {"algorithmic_bytes": head["algorithmic_bytes_per_step"], "gbs": head["gbs"],
                      "frac": head["frac_hbm"], "us_per_layer": head["us_per_layer"],
                      "kernel_us": head["kernel_us"],
