@@ -338,13 +338,19 @@ int moe_forward_exact(const moe_layer* layer, const void* x, int rows, const flo
                       void* stream);
 
 /* The same layer for prompt chunks (the prefill form): rows are sorted by
- * expert (histogram, prefix scan, stable scatter), then grouped GEMMs on
- * 16-bit MFMA compute gate/up + SwiGLU and down, then a fixed-order combine.
- * Equal to the decode form within rounding, not bit for bit ("Sage-A1.5 ...
- * #1329", Limits to agree on: the grouped MoE has a different sum order).
+ * expert (histogram, prefix scan, scatter; a slot's place inside its
+ * expert's run is not fixed and no result depends on it), then grouped GEMMs
+ * on 16-bit MFMA compute gate/up + SwiGLU and down, then a fixed-order
+ * combine. Equal to the decode form within rounding, not bit for bit
+ * ("Sage-A1.5 ... #1329", Limits to agree on: the grouped MoE has a
+ * different sum order); deterministic from call to call.
  *   rows >= 1 (<= 65536); other arguments as moe_experts_decode, with the
  *   workspace from moe_workspace_size(grouped=1).
- * Preconditions: |x| < 65504 and |h| < 65504 (fp16 MFMA operands). */
+ * Preconditions: |x| < 65504 and |h| < 65504 (fp16 MFMA operands).
+ * Errors: as moe_experts_decode; MOE_EUNSUPPORTED (nothing enqueued, the
+ * message names the reason) for a routed / shared format pair the grouped
+ * GEMMs do not read (see moe_qformat) and for MXFP4 experts of a layer
+ * without MOE_LAYER_MX_FP16. */
 int moe_experts_grouped(const moe_layer* layer, const void* x, int rows, const int32_t* ids,
                         const float* p, const float* shared_gate, float* y, void* ws,
                         uint64_t ws_bytes, const moe_taps* taps, void* stream);
