@@ -3,16 +3,19 @@ nothing: its workspace is a fixed device array inside the library).
 
 Through the C ABI it must give the same bits as moe_forward_windows with a
 caller's workspace, on two calls in a row (the second with fewer rows, so it
-runs on the array as the first call left it), and refuse a layer whose
+runs on the array as the first call left it; a 4-bit affine and an MXFP4
+layer), and refuse a layer whose
 windows need more than the array holds, before anything is enqueued.
 """
 import ctypes as C
+from dataclasses import replace
 
 import numpy as np
 import pytest
 
 import synth
 from synth import to_abi
+from synth.gen import MX4G32
 
 from gpu_common import binding, log, to_dev_x, torch_mod
 
@@ -24,10 +27,14 @@ def _bits(t):
     return a.view(np.uint32) if a.dtype == np.float32 else a
 
 
-def test_noalloc_equals_workspace_form_on_two_calls():
+SPECS = [synth.CONFIGS[1],
+         replace(synth.CONFIGS[1], cfg_id=380, name="decode-mxfp4-experts", routed=MX4G32, shared=MX4G32)]
+
+
+@pytest.mark.parametrize("spec", SPECS, ids=["q4g64", "mxfp4"])
+def test_noalloc_equals_workspace_form_on_two_calls(spec):
     B = binding()
     torch = torch_mod()
-    spec = synth.CONFIGS[1]
     Lh = synth.make_layer(spec, 2)
     dev = B.pack_layer(B.layer_desc(*to_abi.desc_args(spec)), to_abi.tensors(Lh))
     for n, rows in enumerate((27, 5)):
