@@ -701,6 +701,34 @@ def counter_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel
     return "\n".join(lines) + "\n"
 
 
+def counter_table(csvs, title, commands, fetch_scale=2.0):
+    """Markdown table of the mean of every counter per kernel over the given
+    rocprofv3 --pmc CSVs (one pass each); FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch) also as MB, FETCH_SIZE scaled by the plain copy's factor."""
+    import collections
+    import csv
+    d = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            d[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for v in d.values() for c in v})
+    out = [f"# {title}", "", "Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first):", ""]
+    out += [f"    {c}" for c in commands]
+    out += ["", f"Mean per dispatch; FETCH_SIZE and WRITE_SIZE in KiB as counted, `fetch MB` = FETCH_SIZE x "
+            f"{fetch_scale} (the factor a plain 1 GiB copy reads for the counter) / 1e6.", "",
+            "| kernel | dispatches | " + " | ".join(names) + (" | fetch MB |" if "FETCH_SIZE" in names else " |"),
+            "|---" * (2 + len(names) + ("FETCH_SIZE" in names)) + "|"]
+    for k in sorted(d):
+        v = d[k]
+        n = max(len(x) for x in v.values())
+        cells = [f"{np.mean(v[c]):.4g}" if c in v else "-" for c in names]
+        row = f"| `{k}` | {n} | " + " | ".join(cells)
+        if "FETCH_SIZE" in names:
+            row += f" | {np.mean(v['FETCH_SIZE']) * 1024 * fetch_scale / 1e6:.1f}" if "FETCH_SIZE" in v else " | -"
+        out.append(row + " |")
+    return "\n".join(out) + "\n"
+
+
 def trace_summary(stats_csv, title, command, render, top=16):
     """Markdown table of a rocprofv3 kernel-stats CSV: per kernel the calls
     and the average, min and max duration in microseconds, and its share."""
@@ -738,6 +766,9 @@ def main():
     ap.add_argument("--trace-summary", nargs=3, metavar=("CSV", "PROGRAM", "TITLE"),
                     help="print a markdown table of a kernel-stats CSV written by rocprofv3 "
                          "--kernel-trace --stats around PROGRAM")
+    ap.add_argument("--counter-table", nargs="+", metavar="ARG",
+                    help="TITLE PROGRAM CSV...: a markdown table of per-kernel counter means from "
+                         "rocprofv3 --pmc CSVs taken around PROGRAM (one pass per CSV)")
     ap.add_argument("--mfma-summary", nargs=2, metavar="CSV",
                     help="print the MFMA counter summary of the grouped GEMMs from a counter CSV "
                          "and a kernel-trace CSV of `bench.py --prefill-only`")
@@ -770,6 +801,18 @@ def main():
         sys.stdout.write(trace_summary(path, title, f"rocprofv3 --kernel-trace --stats --output-format csv "
                                                     f"-d {folder} -o {prefix} -- {prog}",
                                        f'python3 bench.py --trace-summary {path} "{prog}" "{title}"'))
+        return
+    if args.counter_table:
+        import csv
+        title, prog, *paths = args.counter_table
+        cmds = []
+        for path in paths:
+            folder, prefix = run_of(path)
+            counters = sorted({r["Counter_Name"] for r in csv.DictReader(open(path))})
+            cmds.append(f"rocprofv3 --pmc {' '.join(counters)} --output-format csv -d {folder} -o {prefix} -- {prog}")
+        cmds.append("python3 bench.py --counter-table " + " ".join(f'"{a_}"' if " " in a_ else a_
+                                                                 for a_ in args.counter_table))
+        sys.stdout.write(counter_table(paths, title, cmds))
         return
     if args.mfma_summary:
         import csv
