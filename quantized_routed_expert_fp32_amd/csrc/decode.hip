@@ -1063,6 +1063,7 @@ __device__ __forceinline__ void exact_down_item(const DecodeArgs& a, uint32_t (*
   const float* hca = reinterpret_cast<const float*>(hw[0] + 256);
   const float* hcb = reinterpret_cast<const float*>(hw[1] + 256);
   const bool one_kb = nkb <= DN_KS;
+  int held = kb0;   // the K block whose weights wr holds (several per wave: reloaded per pass)
   HBlk ha, hb;
   if (one_kb && kp < nkb) {
     ha = dn_load_block(a, (uint64_t)sslot[0], kp, lane);
@@ -1081,11 +1082,12 @@ __device__ __forceinline__ void exact_down_item(const DecodeArgs& a, uint32_t (*
           hb = dn_load_block(a, (uint64_t)sslot[min(i + 3, mc - 1)], kb, lane);
         }
       } else {
-        if (kb != kb0) {
+        if (kb != held) {
           load_scales_rs<F>(rs, scale_voff<F>(lane), scales + (uint32_t)sblk_off<F>(t, kb, nkb), sc);
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc)
             load_chunk_rs<F>(rs, chunk_voff<F>(lane), codes + (uint32_t)chunk_off<F>(t, kb * 8 + cc, nch), wr[cc]);
+          held = kb;
         }
         dn_store_block(dn_load_block(a, (uint64_t)sa, kb, lane), hw[0], lane);
         dn_store_block(dn_load_block(a, (uint64_t)sb, kb, lane), hw[1], lane);

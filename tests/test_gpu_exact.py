@@ -35,6 +35,10 @@ SMALL_ZIPF = replace(synth.make_tiny_config(synth.CONFIGS[4], cfg_id=351, hidden
                                             inter=256, shared_inter=256), bias="zipf")
 MIXED3 = replace(synth.CONFIGS[2], cfg_id=352, name="exact-mixed-3bit", rows=(64,))
 Q8 = replace(synth.CONFIGS[3], cfg_id=353, name="exact-512rows-q8g64-experts", routed=Q8G64, shared=Q8G64)
+# intermediate 1024: four 256-wide K blocks per down matrix, two per wave of
+# a wave pair, so each pass of two slots reloads its weights
+WIDE_I = synth.make_tiny_config(synth.CONFIGS[3], cfg_id=354, hidden=512, n_experts=64, top_k=8, inter=1024,
+                                shared_inter=1024)
 
 _cache = {}
 
@@ -129,6 +133,16 @@ def test_exact_8bit_experts_equal_windows():
     Lh, dev = layer_of(Q8)
     xb = synth.make_x(Q8, 0, 96, rep=2)
     assert_bits_equal(exact(Lh, dev, xb, (50,)), windows(Lh, dev, xb), "8-bit exact (cut at 50) vs windows")
+
+
+def test_exact_wide_intermediate_equals_windows():
+    """Down matrices of more K blocks than a wave pair holds at once: every
+    pass of two slots of an expert block uses its own weights, so a block of
+    many slots (40 rows, top-8 of 64 experts) equals the windows bit for bit
+    (not only its first two slots)."""
+    Lh, dev = layer_of(WIDE_I)
+    xb = synth.make_x(WIDE_I, 0, 40, rep=23)
+    assert_bits_equal(exact(Lh, dev, xb), windows(Lh, dev, xb), "inter-1024 exact vs windows")
 
 
 def test_exact_refuses_a_short_workspace():
