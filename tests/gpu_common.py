@@ -79,6 +79,16 @@ def run_gpu(dev, Lh, xb, grouped=False, taps=True, stream=None):
     return out
 
 
+def assert_rows_bits_equal(a, b, what, keys=("ids", "p", "sg", "y")):
+    """Asserts that two forms' outputs are bit-identical row by row."""
+    for key in keys:
+        u, v = a[key], b[key]
+        if u.dtype == np.float32:
+            u, v = u.view(np.uint32), v.view(np.uint32)
+        bad = np.where(~np.all(u.reshape(len(u), -1) == v.reshape(len(v), -1), axis=1))[0]
+        assert bad.size == 0, f"{what}: {key} differs on rows {bad[:8]}"
+
+
 def near_tie_rows(routing, k):
     """Rows whose oracle k-th and (k+1)-th logits are within NEAR_TIE: the
     only rows whose pick set may differ from the oracle's."""

@@ -20,15 +20,15 @@ The oracle (fp64, 200 MB per dequantised expert, held only while the
 decode and grouped tests use it) runs on three sampled rows: every row's
 outputs are independent of the other rows of its batch (checked bit for
 bit at this shape below), so a sampled row's reference is the oracle on
-that row alone. The 16 rows of every form are
-also compared with each other bit for bit where the forms promise it."""
-import numpy as np
+that row alone. The 16 rows of every form are also compared with each
+other bit for bit where the forms promise it."""
 import pytest
 
 import oracle.moe_oracle as O
 import synth
 
-from gpu_common import binding, build_layer, check_parity, log, run_gpu, to_dev_x, torch_mod
+from gpu_common import (assert_rows_bits_equal, binding, build_layer, check_parity, log, run_gpu,
+                        to_dev_x, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,22 +67,13 @@ def _rows(g, sel):
     return {k_: v[sel] for k_, v in g.items()}
 
 
-def _bits_equal(a, b, what, keys=("ids", "p", "sg", "y")):
-    for key in keys:
-        u, v = a[key], b[key]
-        if u.dtype == np.float32:
-            u, v = u.view(np.uint32), v.view(np.uint32)
-        bad = np.where(~np.all(u.reshape(len(u), -1) == v.reshape(len(v), -1), axis=1))[0]
-        assert bad.size == 0, f"{what}: {key} differs on rows {bad[:8]}"
-
-
 def test_max_shape_decode_parity_and_batch_invariance():
     Lh, dev, xb = _layer()
     log(f"case max-shape decode rows={ROWS}")
     g = run_gpu(dev, Lh, xb)
     for r in SAMPLE:
         solo = run_gpu(dev, Lh, xb[r:r + 1], taps=False)
-        _bits_equal(_rows(g, [r]), solo, f"max-shape row {r} batch vs solo")
+        assert_rows_bits_equal(_rows(g, [r]), solo, f"max-shape row {r} batch vs solo")
     log(f"[max-shape] oracle on rows {SAMPLE}")
     check_parity(Lh, xb[SAMPLE], _rows(g, SAMPLE), _oracle_dense(), name="decode-max-shape-r16",
                  form="expert_major")
@@ -115,7 +106,7 @@ def test_max_shape_exact_equals_windows_and_decode():
     torch.cuda.synchronize()
     keys = ("ids", "p", "sg", "y")
     ed, wd = dict(zip(keys, e)), dict(zip(keys, w))
-    _bits_equal(ed, wd, "max-shape exact vs windows")
+    assert_rows_bits_equal(ed, wd, "max-shape exact vs windows")
     d = run_gpu(dev, Lh, xb[:ROWS], taps=False)
-    _bits_equal(_rows(ed, slice(0, ROWS)), d, "max-shape exact vs decode")
+    assert_rows_bits_equal(_rows(ed, slice(0, ROWS)), d, "max-shape exact vs decode")
     _state.clear()
