@@ -23,7 +23,7 @@ import pytest
 
 import oracle.moe_oracle as O
 import synth
-from synth.gen import Q8G64
+from synth.gen import MX4G32, Q2G64, Q3G64, Q5G64, Q6G64, Q8G64, S4G128
 
 from gpu_common import binding, build_layer, check_parity, log, run_gpu, to_dev_x, torch_mod
 
@@ -143,6 +143,19 @@ def test_exact_wide_intermediate_equals_windows():
     Lh, dev = layer_of(WIDE_I)
     xb = synth.make_x(WIDE_I, 0, 40, rep=23)
     assert_bits_equal(exact(Lh, dev, xb), windows(Lh, dev, xb), "inter-1024 exact vs windows")
+
+
+@pytest.mark.parametrize("fmt,cid", [(Q3G64, 370), (Q8G64, 371), (Q2G64, 372), (Q5G64, 373), (Q6G64, 374),
+                                     (S4G128, 375), (MX4G32, 376)],
+                         ids=["q3", "q8", "q2", "q5", "q6", "s4g128", "mxfp4"])
+def test_exact_wide_intermediate_formats_equal_windows(fmt, cid):
+    """The same at intermediate 1024 for every other expert format (routed
+    and shared of one format), each with its own exact-form kernels."""
+    spec = replace(WIDE_I, cfg_id=cid, name=f"exact-inter1024-{cid}", routed=fmt, shared=fmt)
+    log(f"case exact inter-1024 {spec.name}")
+    Lh, dev = layer_of(spec)
+    xb = synth.make_x(spec, 0, 40, rep=24)
+    assert_bits_equal(exact(Lh, dev, xb), windows(Lh, dev, xb), f"{spec.name} exact vs windows")
 
 
 def test_exact_refuses_a_short_workspace():
