@@ -15,7 +15,7 @@ What it reaches that the other tests do not:
   * 6 picks per row (slot counts not a power of two).
 Every form is checked against the oracle (decode, grouped) or bit for bit
 against the form it promises to equal (batch = solo, exact = windows =
-decode)."""
+decode). The same checks run at top-1 and top-3."""
 import pytest
 
 import synth
@@ -82,3 +82,34 @@ def test_odd_shape_exact_equals_windows_and_decode():
     d = run_gpu(dev, Lh, xb[:16], taps=False)
     assert_rows_bits_equal({k_: v[:16] for k_, v in e.items()}, d, "odd-shape exact vs decode")
     _state.clear()
+
+
+# top-1 and top-3 on 128 experts (two router tiles, so picks are handed from
+# tile to tile): one or three slots per row, a down workgroup of two or six
+# waves, a shared intermediate wider than the routed one
+SMALL_K = {k: synth.make_tiny_config(synth.CONFIGS[1], cfg_id=396 + k, hidden=768, n_experts=128, top_k=k,
+                                     inter=256, shared_inter=512) for k in (1, 3)}
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_small_top_k_every_form(k):
+    spec = SMALL_K[k]
+    log(f"case top-{k} {spec.name}")
+    Lh, dev = build_layer(spec, 0)
+    B = binding()
+    torch = torch_mod()
+    xd = synth.make_x(spec, 0, 16, rep=141 + k)
+    g = run_gpu(dev, Lh, xd)
+    check_parity(Lh, xd, g, name=f"decode-top{k}-r16")
+    solo = run_gpu(dev, Lh, xd[5:6], taps=False)
+    assert_rows_bits_equal({k_: v[5:6] for k_, v in g.items()}, solo, f"top-{k} row 5 batch vs solo")
+    xg = synth.make_x(spec, 0, 150, rep=151 + k)
+    check_parity(Lh, xg, run_gpu(dev, Lh, xg, grouped=True), name=f"grouped-top{k}-r150",
+                 form="expert_major")
+    xe = synth.make_x(spec, 0, 37, rep=161 + k)
+    x = to_dev_x(xe)
+    keys = ("ids", "p", "sg", "y")
+    e = dict(zip(keys, [t.cpu().numpy() for t in B.forward_exact(dev, x, _bias(Lh))]))
+    w = dict(zip(keys, [t.cpu().numpy() for t in B.forward_windows(dev, x, _bias(Lh))]))
+    torch.cuda.synchronize()
+    assert_rows_bits_equal(e, w, f"top-{k} exact vs windows")
