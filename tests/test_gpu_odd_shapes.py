@@ -15,7 +15,8 @@ What it reaches that the other tests do not:
   * 6 picks per row (slot counts not a power of two).
 Every form is checked against the oracle (decode, grouped) or bit for bit
 against the form it promises to equal (batch = solo, exact = windows =
-decode). The same checks run at top-1 and top-3."""
+decode). The same checks run at top-1 and top-3, and at the smallest
+accepted shape (hidden and intermediates 256)."""
 import pytest
 
 import synth
@@ -113,3 +114,31 @@ def test_small_top_k_every_form(k):
     w = dict(zip(keys, [t.cpu().numpy() for t in B.forward_windows(dev, x, _bias(Lh))]))
     torch.cuda.synchronize()
     assert_rows_bits_equal(e, w, f"top-{k} exact vs windows")
+
+
+# the smallest shape accepted: one K slice (a decode gate/up workgroup of one
+# wave, a one-slice router), 4 down tiles per row, one column block in the
+# grouped down GEMM
+MIN = synth.make_tiny_config(synth.CONFIGS[1], cfg_id=390, hidden=256, n_experts=64, top_k=8,
+                             inter=256, shared_inter=256)
+
+
+@pytest.mark.parametrize("rows", [1, 16])
+def test_smallest_shape_every_form(rows):
+    log(f"case smallest shape rows={rows}")
+    Lh, dev = build_layer(MIN, 0)
+    B = binding()
+    torch = torch_mod()
+    xd = synth.make_x(MIN, 0, rows, rep=171 + rows)
+    g = run_gpu(dev, Lh, xd)
+    check_parity(Lh, xd, g, name=f"decode-smallest-r{rows}")
+    xg = synth.make_x(MIN, 0, 10 * rows, rep=181 + rows)
+    check_parity(Lh, xg, run_gpu(dev, Lh, xg, grouped=True), name=f"grouped-smallest-r{10 * rows}",
+                 form="expert_major")
+    xe = synth.make_x(MIN, 0, 2 * rows + 3, rep=191 + rows)
+    x = to_dev_x(xe)
+    keys = ("ids", "p", "sg", "y")
+    e = dict(zip(keys, [t.cpu().numpy() for t in B.forward_exact(dev, x, _bias(Lh))]))
+    w = dict(zip(keys, [t.cpu().numpy() for t in B.forward_windows(dev, x, _bias(Lh))]))
+    torch.cuda.synchronize()
+    assert_rows_bits_equal(e, w, "smallest exact vs windows")
